@@ -1,0 +1,13 @@
+"""MI355X (gfx950) library for exact state forking of decision-request trees:
+ForkAttention and forked Gated DeltaNet behind a C ABI (include/forkgdn.h).
+
+The HIP library ``libforkgdn.so`` is the only implementation; this package
+marshals torch tensors into its calls (``api``) and plans page tables for
+rounds (``rounds``).
+"""
+from . import _lib  # noqa: F401
+from .api import (TreeMeta, alloc_workspace, fk_read_status, fk_strerror,  # noqa: F401
+                  fk_token_positions, fk_tree_build, fk_tree_validate_host, fk_workspace_bytes,
+                  fork_attn_forward, gdn_checkpoint_resume, gdn_checkpoint_save, gdn_fork_forward,
+                  kv_append, make_tree_meta)
+from .rounds import RoundPlan, capacities, plan_round  # noqa: F401,E402

@@ -1,0 +1,223 @@
+// attn_bf16.hip -- ForkAttention prefill on bf16 MFMA for gfx950
+// (Flide section 3.2.1, Eq. 3; section 3.3.1: fully visible key blocks are
+// read without a mask and only the partially visible ones are masked).
+//
+// Work item: one 16-token tile of one segment x one kv head.  The tile's
+// 16 tokens x 8 q heads of the GQA group form 128 query rows; each of the 4
+// waves owns 32 rows (4 tokens x 8 heads), so a key/value block staged once in
+// LDS feeds the whole group.  Keys are visited range by range along the
+// tile's ancestor chain (each ancestor's first `fork` tokens, then the own
+// segment causally), in 64-key blocks anchored at every range start; a row's
+// reduction order therefore depends only on its own chain (Flide 3.5).
+//
+// Per block and wave, with v_mfma_f32_32x32x16_bf16 (fp32 accumulate):
+//   S^T[64 keys x 32 rows] = K_blk[64 x 128] . Q^T[128 x 32]      16 MFMAs
+//   online softmax on S^T in registers (row = lane % 32; the two halves of
+//   the wave hold disjoint keys of the same row; max via one lane swap)
+//   O^T[128 x 32] += V^T[128 x 64] . P^T[64 x 32]                 16 MFMAs
+// The accumulator layout of S^T is reused directly as the P^T operand: the
+// K rows are loaded under a fixed permutation (bits 2 and 3 of the row index
+// swapped) so that each lane's accumulator registers hold 8 consecutive keys
+// of the V^T operand.  Values sit transposed in their pages ([d][slot]), so
+// V^T rows are contiguous in LDS.
+#include <hip/hip_runtime.h>
+
+#include "fk_common.h"
+
+namespace fk {
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int D = 128;           // head dim
+constexpr int G = 8;             // q heads per kv head
+constexpr int BN = 64;           // keys per block
+constexpr int WAVES = 4;
+constexpr int THREADS = WAVES * 64;
+constexpr int K_STRIDE = D + 8;  // LDS row stride (bf16) of the key tile, padded
+constexpr int V_STRIDE = BN + 8; // LDS row stride (bf16) of the transposed value tile
+constexpr int K_LDS = BN * K_STRIDE;
+constexpr int V_LDS = D * V_STRIDE;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ uint4 pack8(const float *x)
+{
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[e];
+    return __builtin_bit_cast(uint4, v);
+}
+
+// Stage keys [BN][D] and transposed values [D][BN] of one 64-key block of a
+// range into LDS.  Pages past the range's valid keys are zero-filled, so no
+// page-list entry beyond the range is ever read.
+__device__ __forceinline__ void stage_block(uint16_t *__restrict__ ks, uint16_t *__restrict__ vs,
+                                            const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
+                                            const int32_t *__restrict__ plist, int key0, int count, int g, int Hkv)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < BN / FK_TILE_TOKENS; ++p) {
+        const int kbase = key0 + p * FK_TILE_TOKENS;
+        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+        if (kbase < count) {
+            const size_t pb = ((size_t)plist[kbase / FK_TILE_TOKENS] * Hkv + g) * (FK_TILE_TOKENS * D);
+            kv = *reinterpret_cast<const uint4 *>(kp + pb + tid * 8);   // slot tid/16, dims (tid%16)*8
+            vv = *reinterpret_cast<const uint4 *>(vp + pb + tid * 8);   // dim tid/2, slots (tid%2)*8
+        }
+        *reinterpret_cast<uint4 *>(ks + (p * FK_TILE_TOKENS + tid / 16) * K_STRIDE + (tid % 16) * 8) = kv;
+        *reinterpret_cast<uint4 *>(vs + (tid / 2) * V_STRIDE + p * FK_TILE_TOKENS + (tid % 2) * 8) = vv;
+    }
+}
+
+__global__ void __launch_bounds__(THREADS, 2)
+k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, const uint16_t *__restrict__ kp,
+            const uint16_t *__restrict__ vp, uint16_t *__restrict__ out, const int32_t *__restrict__ header,
+            const int32_t *__restrict__ tile_seg, const int32_t *__restrict__ tile_row0,
+            const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_len,
+            const int32_t *__restrict__ seg_depth, const int32_t *__restrict__ seg_anc,
+            const int32_t *__restrict__ seg_fork, const int32_t *__restrict__ page_off,
+            const int32_t *__restrict__ pages)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[K_LDS];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[V_LDS];
+    if (header[H_STATUS] != FK_OK) return;
+    const int tile = blockIdx.x, g = blockIdx.y;
+    if (tile >= header[H_NTILES]) return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int half = lane >> 5, n = lane & 31;
+    const int s = tile_seg[tile], row0 = tile_row0[tile];
+    const int len = seg_len[s];
+    const int tok = row0 + w * 4 + n / 8;          // local token of this lane's row
+    const int h = g * G + (n % 8);
+    const bool row_valid = tok < len;
+    const size_t t_glob = (size_t)seg_start[s] + tok;
+
+    // Q^T as the B operand: lane holds its row's dims 16*ks + 8*half + [0, 8)
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (row_valid) u = *reinterpret_cast<const uint4 *>(q + (t_glob * Hq + h) * D + ks * 16 + half * 8);
+        qf[ks] = as_bf16x8(u);
+    }
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+    float m = -INFINITY, l = 0.f;
+
+    const int depth = seg_depth[s];
+    const int *anc = seg_anc + s * FK_MAX_DEPTH;
+    // MFMA row m of a 32-key tile holds key perm(m): bits 2 and 3 swapped
+    const int prow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+
+    for (int lvl = 0; lvl <= depth; ++lvl) {
+        const int a = anc[lvl];
+        const bool own = lvl == depth;
+        const int count = own ? min(row0 + FK_TILE_TOKENS, len) : seg_fork[anc[lvl + 1]];
+        const int32_t *plist = pages + page_off[a];
+        for (int key0 = 0; key0 < count; key0 += BN) {
+            __syncthreads();   // previous block fully consumed
+            stage_block(k_lds, v_lds, kp, vp, plist, key0, count, g, Hkv);
+            __syncthreads();
+            // S^T = K . Q^T
+            f32x16 sacc[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                sacc[mt] = f32x16{};
+                const uint16_t *krow = k_lds + (mt * 32 + prow) * K_STRIDE + half * 8;
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + ks * 16));
+                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
+                }
+            }
+            // mask: register r of tile mt holds key 32*mt + 16*(r/8) + 8*half + r%8
+            const bool full = own ? (key0 + BN - 1 <= row0) : (key0 + BN <= count);
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float x = sacc[mt][r] * scale_log2e;
+                    if (!full) {
+                        const int key = key0 + mt * 32 + (r / 8) * 16 + half * 8 + (r % 8);
+                        const bool vis = own ? key <= tok : key < count;
+                        if (!vis) x = -INFINITY;
+                    }
+                    sacc[mt][r] = x;
+                    mloc = fmaxf(mloc, x);
+                }
+            const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+            const float mnew = fmaxf(m, mrow);
+            const float corr = exp2f(m - mnew);
+            m = mnew;
+            float psum = 0.f;
+            bf16x8 pf[4];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    float pv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        pv[e] = exp2f(sacc[mt][hh * 8 + e] - mnew);
+                        psum += pv[e];
+                    }
+                    pf[mt * 2 + hh] = as_bf16x8(pack8(pv));
+                }
+            l = l * corr + psum;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) o[i] *= corr;
+            // O^T += V^T . P^T ; k-step kk covers keys 16*kk + [0, 16)
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) {
+                const uint16_t *vrow = v_lds + (i * 32 + n) * V_STRIDE + half * 8;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + kk * 16));
+                    o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[i], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // epilogue: the row's sum is split over the two halves of the wave
+    const float lsum = l + __shfl_xor(l, 32, 64);
+    if (!row_valid) return;
+    const float inv = 1.f / lsum;
+    uint16_t *orow = out + (t_glob * Hq + h) * D;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            // registers 4*rq .. 4*rq+3 hold dims 32*i + 8*rq + 4*half + [0, 4)
+            uint2 packed;
+            __bf16 b4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b4[e] = (__bf16)(o[i][rq * 4 + e] * inv);
+            packed.x = (uint32_t)__builtin_bit_cast(uint16_t, b4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, b4[1]) << 16);
+            packed.y = (uint32_t)__builtin_bit_cast(uint16_t, b4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, b4[3]) << 16);
+            *reinterpret_cast<uint2 *>(orow + i * 32 + rq * 8 + half * 4) = packed;
+        }
+}
+
+}  // namespace attn
+}  // namespace fk
+
+using namespace fk;
+
+int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv, float scale, const void *k_pool,
+                        const void *v_pool, void *out, const void *ws, hipStream_t st)
+{
+    const WsLayout L = ws_layout(*meta, 0);
+    dim3 grid((unsigned)L.tile_cap, (unsigned)Hkv);
+    attn::k_attn_bf16<<<grid, attn::THREADS, 0, st>>>(
+        (const uint16_t *)q, Hq, Hkv, scale * 1.4426950408889634f, (const uint16_t *)k_pool,
+        (const uint16_t *)v_pool, (uint16_t *)out, ws_at<int32_t>(ws, L.header), ws_at<int32_t>(ws, L.tile_seg),
+        ws_at<int32_t>(ws, L.tile_row0), ws_at<int32_t>(ws, L.seg_start), ws_at<int32_t>(ws, L.seg_len),
+        ws_at<int32_t>(ws, L.seg_depth), ws_at<int32_t>(ws, L.seg_anc), meta->seg_fork, meta->seg_page_off,
+        meta->seg_pages);
+    return launch_status();
+}

@@ -1,0 +1,94 @@
+// kv_append.hip -- write the stream's keys and values into the paged pool.
+// ForkServe item 1: a write allocates the writer's own pages only, and a
+// child reads its ancestors' pages through their page lists (an alias), never
+// through a copy.  Flide section 3.4: cached keys/values precede the new ones
+// in each state's history buffer -- here, the cached segment's pages.
+//
+// One block per (16-token tile = one page, kv head).  Keys keep their row
+// layout [slot][d]; values are stored transposed inside the page, [d][slot],
+// so the attention kernel's value operand reads keys contiguously.  Slots
+// after a segment's last token are zero-filled.
+#include <hip/hip_runtime.h>
+
+#include "fk_common.h"
+
+namespace fk {
+
+template <typename E>
+__global__ void __launch_bounds__(256) k_kv_append(const E *__restrict__ k, const E *__restrict__ v, int Hkv,
+                                                   int d, const int32_t *__restrict__ header,
+                                                   const int32_t *__restrict__ tile_seg,
+                                                   const int32_t *__restrict__ tile_row0,
+                                                   const int32_t *__restrict__ seg_start,
+                                                   const int32_t *__restrict__ seg_len,
+                                                   const int32_t *__restrict__ page_off,
+                                                   const int32_t *__restrict__ pages, E *__restrict__ kp,
+                                                   E *__restrict__ vp)
+{
+    if (header[H_STATUS] != FK_OK) return;
+    const int tile = blockIdx.x, h = blockIdx.y;
+    if (tile >= header[H_NTILES]) return;
+    const int s = tile_seg[tile], row0 = tile_row0[tile];
+    const int count = min(FK_TILE_TOKENS, seg_len[s] - row0);
+    const int page = pages[page_off[s] + row0 / FK_TILE_TOKENS];
+    const int t0 = seg_start[s] + row0;
+    const size_t page_base = ((size_t)page * Hkv + h) * (size_t)FK_TILE_TOKENS * d;
+    const int n = FK_TILE_TOKENS * d;
+    for (int e = threadIdx.x; e < n; e += blockDim.x) {
+        // keys: e -> (slot, dim), coalesced on both sides
+        const int r = e / d, x = e % d;
+        E kv = E(0);
+        if (r < count) kv = k[((size_t)(t0 + r) * Hkv + h) * d + x];
+        kp[page_base + e] = kv;
+        // values: e -> (dim, slot), coalesced on the page side
+        const int xv = e / FK_TILE_TOKENS, rv = e % FK_TILE_TOKENS;
+        E vv = E(0);
+        if (rv < count) vv = v[((size_t)(t0 + rv) * Hkv + h) * d + xv];
+        vp[page_base + e] = vv;
+    }
+}
+
+}  // namespace fk
+
+using namespace fk;
+
+// shared with fork_attn_forward
+int fk_launch_kv_append(const fk_tree_meta *meta, const void *k, const void *v, int dtype, int Hkv, int d,
+                        void *k_pool, void *v_pool, const void *ws, hipStream_t st)
+{
+    const WsLayout L = ws_layout(*meta, 0);
+    dim3 grid((unsigned)L.tile_cap, (unsigned)Hkv);
+    const int32_t *hdr = ws_at<int32_t>(ws, L.header);
+    const int32_t *ts = ws_at<int32_t>(ws, L.tile_seg), *tr = ws_at<int32_t>(ws, L.tile_row0);
+    const int32_t *ss = ws_at<int32_t>(ws, L.seg_start), *sl = ws_at<int32_t>(ws, L.seg_len);
+    if (dtype == FK_BF16)
+        k_kv_append<uint16_t><<<grid, 256, 0, st>>>((const uint16_t *)k, (const uint16_t *)v, Hkv, d, hdr, ts, tr,
+                                                   ss, sl, meta->seg_page_off, meta->seg_pages,
+                                                   (uint16_t *)k_pool, (uint16_t *)v_pool);
+    else
+        k_kv_append<float><<<grid, 256, 0, st>>>((const float *)k, (const float *)v, Hkv, d, hdr, ts, tr, ss, sl,
+                                                meta->seg_page_off, meta->seg_pages, (float *)k_pool,
+                                                (float *)v_pool);
+    return launch_status();
+}
+
+int fk_check_kv_args(const fk_tree_meta *meta, const void *k, const void *v, int dtype, int Hkv, int d,
+                     void *k_pool, void *v_pool, const void *ws)
+{
+    int rc = check_meta_scalars(meta);
+    if (rc) return rc;
+    if (!ws || !k_pool || !v_pool || (meta->T > 0 && (!k || !v))) return FK_E_INVALID_ARG;
+    if (!meta->seg_page_off || meta->n_pages < 1) return FK_E_INVALID_ARG;
+    if (dtype != FK_F32 && dtype != FK_BF16) return FK_E_UNSUPPORTED;
+    if (Hkv < 1 || d < 1 || d > 128) return FK_E_UNSUPPORTED;
+    return FK_OK;
+}
+
+extern "C" int kv_append(const fk_tree_meta *meta, const void *k, const void *v, int dtype, int Hkv, int d,
+                         void *k_pool, void *v_pool, const void *ws, fk_stream_t stream)
+{
+    int rc = fk_check_kv_args(meta, k, v, dtype, Hkv, d, k_pool, v_pool, ws);
+    if (rc) return rc;
+    if (meta->T == 0) return FK_OK;
+    return fk_launch_kv_append(meta, k, v, dtype, Hkv, d, k_pool, v_pool, ws, (hipStream_t)stream);
+}

@@ -1,0 +1,416 @@
+// tree_build.hip -- the tree-metadata builder (Flide section 3.3.1: every
+// variable set by the round composition -- segment lengths, positions, key
+// ranges, state indices -- lives in device buffers, and the attention tile
+// table is built on the GPU; section 3.3.2: launch sizes come from host-known
+// capacities, so the host never reads the tree).
+//
+// Kernels:
+//   k_tokens   grid over T   token runs of every segment (start, end, run count)
+//   k_build    one block     validation, lengths, first positions, ancestor
+//                            chains, attention tiles, level lists, fork points
+//   k_positions grid over T  per-token positions
+// No dense T x T mask is ever formed: a tile's key ranges follow from its
+// segment's ancestor chain and the forks along it.
+#include <hip/hip_runtime.h>
+
+#include <vector>
+
+#include "fk_common.h"
+#include "tree_rules.h"
+
+namespace fk {
+
+constexpr int BUILD_THREADS = 1024;
+
+__global__ void k_init(int32_t *header, int32_t *seg_nrun, int32_t *kid_cnt, int32_t *kid_fill,
+                       int S)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < H_WORDS) header[i] = 0;
+    for (int s = i; s < S; s += gridDim.x * blockDim.x) {
+        seg_nrun[s] = 0;
+        kid_cnt[s] = 0;
+        kid_fill[s] = 0;
+    }
+}
+
+// Phase 0: each token checks its segment id; the first token of every run
+// records the run start, the last its end, and counts the run.
+__global__ void k_tokens(const int32_t *__restrict__ tok_seg, int T, int S, int32_t *header,
+                         int32_t *seg_start, int32_t *seg_end, int32_t *seg_nrun)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    const int s = tok_seg[t];
+    if (s < 0 || s >= S) {
+        set_error(header, FK_E_SEG_RANGE);
+        return;
+    }
+    if (t == 0 || tok_seg[t - 1] != s) {
+        atomicAdd(seg_nrun + s, 1);   // an integer count: order-independent
+        seg_start[s] = t;             // meaningful only when the run count is 1
+    }
+    if (t == T - 1 || tok_seg[t + 1] != s) seg_end[s] = t + 1;
+}
+
+// Exclusive prefix sum over the block (BUILD_THREADS threads, wave64).
+__device__ int block_scan(int x, int *lds, int *total)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int v = x;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(v, o, 64);
+        if (lane >= o) v += y;
+    }
+    if (lane == 63) lds[wid] = v;
+    __syncthreads();
+    if (wid == 0) {
+        int w = lane < nw ? lds[lane] : 0;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(w, o, 64);
+            if (lane >= o) w += y;
+        }
+        if (lane < nw) lds[lane] = w;
+    }
+    __syncthreads();
+    const int before = wid ? lds[wid - 1] : 0;
+    *total = lds[nw - 1];
+    __syncthreads();
+    return before + v - x;
+}
+
+struct BuildArgs {
+    fk_tree_meta m;
+    int32_t *header, *seg_start, *seg_end, *seg_nrun, *seg_len, *seg_pos0, *seg_depth, *seg_anc;
+    int32_t *seg_src, *seg_owner, *kid_cnt, *kid_off, *kid_fill, *kids, *emit_off, *emit_pos;
+    int32_t *tile_seg, *tile_row0, *lvl_seg;
+};
+
+__device__ bool block_failed(int32_t *header, int *flag)
+{
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) *flag = __hip_atomic_load(header + H_STATUS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    return *flag != FK_OK;
+}
+
+__global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
+{
+    __shared__ int lds[32];
+    __shared__ int lvl_lds[FK_MAX_DEPTH];
+    __shared__ int flag;
+    const fk_tree_meta &m = A.m;
+    const int S = m.S;
+    if (block_failed(A.header, &flag)) return;   // phase 0 failed
+
+    // phase 1: lengths
+    for (int s = threadIdx.x; s < S; s += blockDim.x) {
+        const int nrun = A.seg_nrun[s];
+        int len = 0;
+        const int code = rule_length(m.seg_cached_len[s], nrun,
+                                     nrun == 1 ? A.seg_end[s] - A.seg_start[s] : 0, &len);
+        if (code) set_error(A.header, code);
+        A.seg_len[s] = len;
+        if (m.seg_cached_len[s] > 0) A.seg_start[s] = -1;
+    }
+    if (block_failed(A.header, &flag)) return;
+
+    // phase 2: links, chains, slots, pages; GDN sources of children of cached
+    // or fresh roots; child counts of live parents
+    for (int s = threadIdx.x; s < S; s += blockDim.x) {
+        SegDerived d;
+        const int code = rule_links(s, S, m.max_depth, m.seg_parent, m.seg_fork, m.seg_cached_len,
+                                    A.seg_len, m.seg_state_in, m.n_state_in, m.seg_state_out,
+                                    m.n_state_out, m.seg_page_off, m.seg_pages, m.page_size,
+                                    m.n_pages, &d);
+        if (code) set_error(A.header, code);
+        A.seg_depth[s] = d.depth;
+        A.seg_pos0[s] = d.pos0;
+        for (int j = 0; j < FK_MAX_DEPTH; ++j) A.seg_anc[s * FK_MAX_DEPTH + j] = j <= d.depth ? d.anc[j] : -1;
+        const int p = m.seg_parent[s];
+        const bool live = m.seg_cached_len[s] == 0;
+        int src = -1;
+        if (live && p >= 0 && p < S) {
+            if (m.seg_cached_len[p] > 0) src = -2 - (m.seg_state_in ? m.seg_state_in[p] : 0);
+            else atomicAdd(A.kid_cnt + p, 1);
+        }
+        A.seg_src[s] = src;
+    }
+    if (block_failed(A.header, &flag)) return;
+
+    // phase 3a: scans -- attention tiles, children CSR, level lists
+    if (threadIdx.x < FK_MAX_DEPTH) lvl_lds[threadIdx.x] = 0;
+    __syncthreads();
+    int tile_base = 0, kid_base = 0;
+    for (int base = 0; base < S; base += blockDim.x) {
+        const int s = base + threadIdx.x;
+        const bool in = s < S;
+        const bool live = in && m.seg_cached_len[s] == 0;
+        const int len = in ? A.seg_len[s] : 0;
+        const int ntile = live ? (len + FK_TILE_TOKENS - 1) / FK_TILE_TOKENS : 0;
+        int tot;
+        const int toff = tile_base + block_scan(ntile, lds, &tot);
+        tile_base += tot;
+        for (int r = 0; r < ntile; ++r) {
+            A.tile_seg[toff + r] = s;
+            A.tile_row0[toff + r] = r * FK_TILE_TOKENS;
+        }
+        const int kc = in ? A.kid_cnt[s] : 0;
+        const int koff = kid_base + block_scan(kc, lds, &tot);
+        kid_base += tot;
+        if (in) A.kid_off[s] = koff;
+        const int depth = in ? A.seg_depth[s] : -1;
+        for (int dd = 0; dd < m.max_depth; ++dd) {
+            const int pos = block_scan(live && depth == dd, lds, &tot);
+            if (live && depth == dd) {
+                const int rank = lvl_lds[dd] + pos;
+                if (rank < m.level_cap) A.lvl_seg[dd * m.level_cap + rank] = s;
+                else set_error(A.header, FK_E_CAPACITY);
+            }
+            __syncthreads();
+            if (threadIdx.x == 0) lvl_lds[dd] += tot;
+            __syncthreads();
+        }
+    }
+    if (threadIdx.x == 0) {
+        A.kid_off[S] = kid_base;
+        A.header[H_NTILES] = tile_base;
+        for (int dd = 0; dd < FK_MAX_DEPTH; ++dd) A.header[H_LEVEL0 + dd] = dd < m.max_depth ? lvl_lds[dd] : 0;
+    }
+    __syncthreads();
+    // children lists (filled in arbitrary order; every later rule compares
+    // (fork, index) so the order does not matter)
+    for (int s = threadIdx.x; s < S; s += blockDim.x) {
+        const int p = m.seg_parent[s];
+        if (m.seg_cached_len[s] == 0 && p >= 0 && m.seg_cached_len[p] == 0) {
+            const int at = atomicAdd(A.kid_fill + p, 1);
+            A.kids[A.kid_off[p] + at] = s;
+        }
+    }
+    if (block_failed(A.header, &flag)) return;
+
+    // phase 3b: fork points -- one slot per distinct (parent, fork offset);
+    // the lowest-index child at an offset owns it
+    for (int c = threadIdx.x; c < S; c += blockDim.x) {
+        const int p = m.seg_parent[c];
+        int owner = 0;
+        if (m.seg_cached_len[c] == 0 && p >= 0 && m.seg_cached_len[p] == 0) {
+            owner = 1;
+            for (int j = A.kid_off[p]; j < A.kid_off[p + 1]; ++j) {
+                const int o = A.kids[j];
+                if (o < c && m.seg_fork[o] == m.seg_fork[c]) owner = 0;
+            }
+        }
+        A.seg_owner[c] = owner;
+    }
+    __syncthreads();
+    __threadfence_block();
+    int emit_base = 0;
+    for (int base = 0; base < S; base += blockDim.x) {
+        const int s = base + threadIdx.x;
+        int n = 0;
+        if (s < S)
+            for (int j = A.kid_off[s]; j < A.kid_off[s + 1]; ++j) n += A.seg_owner[A.kids[j]];
+        int tot;
+        const int off = emit_base + block_scan(n, lds, &tot);
+        emit_base += tot;
+        if (s < S) A.emit_off[s] = off;
+    }
+    if (threadIdx.x == 0) {
+        A.emit_off[S] = emit_base;
+        A.header[H_NFORKS] = emit_base;
+        if (emit_base > m.fork_cap) set_error(A.header, FK_E_CAPACITY);
+    }
+    if (block_failed(A.header, &flag)) return;
+    for (int c = threadIdx.x; c < S; c += blockDim.x) {
+        const int p = m.seg_parent[c];
+        if (m.seg_cached_len[c] == 0 && p >= 0 && m.seg_cached_len[p] == 0) {
+            int rank = 0;
+            for (int j = A.kid_off[p]; j < A.kid_off[p + 1]; ++j) {
+                const int o = A.kids[j];
+                if (A.seg_owner[o] && m.seg_fork[o] < m.seg_fork[c]) ++rank;
+            }
+            const int slot = A.emit_off[p] + rank;
+            A.seg_src[c] = slot;
+            if (A.seg_owner[c]) A.emit_pos[slot] = m.seg_fork[c];
+        }
+    }
+}
+
+__global__ void k_positions(const int32_t *__restrict__ tok_seg, int T, const int32_t *header,
+                            const int32_t *seg_start, const int32_t *seg_pos0, int32_t *tok_pos)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T || header[H_STATUS] != FK_OK) return;
+    const int s = tok_seg[t];
+    tok_pos[t] = seg_pos0[s] + (t - seg_start[s]);
+}
+
+int check_meta_scalars(const fk_tree_meta *m)
+{
+    if (!m) return FK_E_INVALID_ARG;
+    if (m->T < 0 || m->S < 1 || m->max_depth < 1 || m->max_depth > FK_MAX_DEPTH ||
+        m->level_cap < 1 || m->fork_cap < 0 || m->n_state_in < 0 || m->n_state_out < 0 ||
+        m->n_pages < 0)
+        return FK_E_INVALID_ARG;
+    if (m->seg_page_off && m->page_size != FK_TILE_TOKENS) return FK_E_UNSUPPORTED;
+    if ((m->T > 0 && !m->tok_seg) || !m->seg_parent || !m->seg_fork || !m->seg_cached_len)
+        return FK_E_INVALID_ARG;
+    if (m->seg_page_off && !m->seg_pages) return FK_E_INVALID_ARG;
+    return FK_OK;
+}
+
+}  // namespace fk
+
+using namespace fk;
+
+extern "C" size_t fk_workspace_bytes(const fk_tree_meta *meta, int64_t gdn_state_elems)
+{
+    if (!meta) return 0;
+    return ws_layout(*meta, gdn_state_elems).total;
+}
+
+extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes, fk_stream_t stream)
+{
+    int rc = check_meta_scalars(meta);
+    if (rc) return rc;
+    if (!ws) return FK_E_INVALID_ARG;
+    const WsLayout L = ws_layout(*meta, 0);
+    if (ws_bytes < L.total) return FK_E_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    BuildArgs A;
+    A.m = *meta;
+    A.header = ws_at<int32_t>(ws, L.header);
+    A.seg_start = ws_at<int32_t>(ws, L.seg_start);
+    A.seg_end = ws_at<int32_t>(ws, L.seg_end);
+    A.seg_nrun = ws_at<int32_t>(ws, L.seg_nrun);
+    A.seg_len = ws_at<int32_t>(ws, L.seg_len);
+    A.seg_pos0 = ws_at<int32_t>(ws, L.seg_pos0);
+    A.seg_depth = ws_at<int32_t>(ws, L.seg_depth);
+    A.seg_anc = ws_at<int32_t>(ws, L.seg_anc);
+    A.seg_src = ws_at<int32_t>(ws, L.seg_src);
+    A.seg_owner = ws_at<int32_t>(ws, L.seg_owner);
+    A.kid_cnt = ws_at<int32_t>(ws, L.kid_cnt);
+    A.kid_off = ws_at<int32_t>(ws, L.kid_off);
+    A.kid_fill = ws_at<int32_t>(ws, L.kid_fill);
+    A.kids = ws_at<int32_t>(ws, L.kids);
+    A.emit_off = ws_at<int32_t>(ws, L.emit_off);
+    A.emit_pos = ws_at<int32_t>(ws, L.emit_pos);
+    A.tile_seg = ws_at<int32_t>(ws, L.tile_seg);
+    A.tile_row0 = ws_at<int32_t>(ws, L.tile_row0);
+    A.lvl_seg = ws_at<int32_t>(ws, L.lvl_seg);
+    const int S = meta->S, T = meta->T;
+    k_init<<<(S + 255) / 256 > 0 ? (S + 255) / 256 : 1, 256, 0, st>>>(A.header, A.seg_nrun, A.kid_cnt,
+                                                                   A.kid_fill, S);
+    if ((rc = launch_status())) return rc;
+    if (T > 0) {
+        k_tokens<<<(T + 255) / 256, 256, 0, st>>>(meta->tok_seg, T, S, A.header, A.seg_start, A.seg_end,
+                                                 A.seg_nrun);
+        if ((rc = launch_status())) return rc;
+    }
+    k_build<<<1, BUILD_THREADS, 0, st>>>(A);
+    if ((rc = launch_status())) return rc;
+    if (T > 0) {
+        k_positions<<<(T + 255) / 256, 256, 0, st>>>(meta->tok_seg, T, A.header, A.seg_start, A.seg_pos0,
+                                                    ws_at<int32_t>(ws, L.tok_pos));
+        if ((rc = launch_status())) return rc;
+    }
+    return FK_OK;
+}
+
+extern "C" int fk_tree_validate_host(const fk_tree_meta *m)
+{
+    int rc = check_meta_scalars(m);
+    if (rc) return rc;
+    const int S = m->S, T = m->T;
+    std::vector<int32_t> nrun(S, 0), start(S, 0), end(S, 0), len(S, 0);
+    int code = FK_OK;
+    for (int t = 0; t < T; ++t) {
+        const int s = m->tok_seg[t];
+        if (s < 0 || s >= S) { code = imin(code, FK_E_SEG_RANGE); continue; }
+        if (t == 0 || m->tok_seg[t - 1] != s) { nrun[s]++; start[s] = t; }
+        if (t == T - 1 || m->tok_seg[t + 1] != s) end[s] = t + 1;
+    }
+    if (code) return code;
+    for (int s = 0; s < S; ++s)
+        code = imin(code, rule_length(m->seg_cached_len[s], nrun[s], nrun[s] == 1 ? end[s] - start[s] : 0,
+                                      &len[s]));
+    if (code) return code;
+    for (int s = 0; s < S; ++s) {
+        SegDerived d;
+        code = imin(code, rule_links(s, S, m->max_depth, m->seg_parent, m->seg_fork, m->seg_cached_len,
+                                     len.data(), m->seg_state_in, m->n_state_in, m->seg_state_out,
+                                     m->n_state_out, m->seg_page_off, m->seg_pages, m->page_size,
+                                     m->n_pages, &d));
+    }
+    if (code) return code;
+    // phase 3: capacities
+    std::vector<int> per_level(FK_MAX_DEPTH, 0);
+    for (int s = 0; s < S; ++s) {
+        if (m->seg_cached_len[s] > 0) continue;
+        int depth = 0;
+        for (int i = s; m->seg_parent[i] >= 0; i = m->seg_parent[i]) ++depth;
+        per_level[depth]++;
+    }
+    for (int dd = 0; dd < FK_MAX_DEPTH; ++dd)
+        if (per_level[dd] > m->level_cap) code = imin(code, FK_E_CAPACITY);
+    long long forks = 0;
+    for (int c = 0; c < S; ++c) {
+        const int p = m->seg_parent[c];
+        if (m->seg_cached_len[c] > 0 || p < 0 || m->seg_cached_len[p] > 0) continue;
+        bool owner = true;
+        for (int o = 0; o < c; ++o)
+            if (m->seg_parent[o] == p && m->seg_cached_len[o] == 0 && m->seg_fork[o] == m->seg_fork[c])
+                owner = false;
+        forks += owner;
+    }
+    if (forks > m->fork_cap) code = imin(code, FK_E_CAPACITY);
+    return code;
+}
+
+extern "C" int fk_token_positions(const fk_tree_meta *meta, const void *ws, int32_t *pos, fk_stream_t stream)
+{
+    int rc = check_meta_scalars(meta);
+    if (rc) return rc;
+    if (!ws || (meta->T > 0 && !pos)) return FK_E_INVALID_ARG;
+    if (meta->T == 0) return FK_OK;
+    const WsLayout L = ws_layout(*meta, 0);
+    FK_HIP(hipMemcpyAsync(pos, ws_at<int32_t>(ws, L.tok_pos), (size_t)meta->T * 4, hipMemcpyDeviceToDevice,
+                          (hipStream_t)stream));
+    return FK_OK;
+}
+
+extern "C" int fk_read_status(const void *ws, fk_stream_t stream, int32_t *status_out)
+{
+    if (!ws || !status_out) return FK_E_INVALID_ARG;
+    int32_t v = 0;
+    FK_HIP(hipMemcpyAsync(&v, ws, sizeof(int32_t), hipMemcpyDeviceToHost, (hipStream_t)stream));
+    FK_HIP(hipStreamSynchronize((hipStream_t)stream));
+    *status_out = v;
+    return FK_OK;
+}
+
+extern "C" const char *fk_strerror(int code)
+{
+    switch (code) {
+    case FK_OK: return "ok";
+    case FK_E_INVALID_ARG: return "invalid argument";
+    case FK_E_UNSUPPORTED: return "unsupported shape or dtype";
+    case FK_E_WORKSPACE: return "workspace too small";
+    case FK_E_HIP: return "HIP runtime error";
+    case FK_E_SEG_RANGE: return "token names a segment outside [0, S)";
+    case FK_E_NONCONTIG: return "segment tokens are not contiguous in the stream";
+    case FK_E_PARENT: return "parent index out of range";
+    case FK_E_CYCLE: return "parent chain loops or exceeds max_depth";
+    case FK_E_FORK: return "fork offset outside the parent";
+    case FK_E_EMPTY: return "live segment without tokens, or cached segment with tokens";
+    case FK_E_CACHED: return "cached segment misplaced, or child forks inside a cached history";
+    case FK_E_PAGES: return "page list too short or page id out of range";
+    case FK_E_CAPACITY: return "level or fork-point capacity exceeded";
+    case FK_E_STATE_SLOT: return "state slot missing or out of range";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int fk_abi_version(void) { return 1; }

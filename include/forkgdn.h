@@ -1,0 +1,242 @@
+/*
+ * forkgdn.h -- C ABI of the MI355X (gfx950) library for exact state forking.
+ *
+ * A round of decision requests is one flat token stream (Flide, section 3.2,
+ * Eq. 2).  Every request is a tree of segments: a trunk (the shared state),
+ * question branches forked from it, possibly deeper forks, and optionally a
+ * cached history saved by an earlier pass (Flide, section 3.4).  Each branch
+ * token must see exactly its own root-to-leaf ancestry, so that every branch
+ * equals an isolated forward pass of its path (Flide, Proposition 3.1):
+ *   - causal GQA softmax attention under the visibility rule of Flide
+ *     section 3.2.1, Eq. 3, generalised to deeper trees as a sequence of
+ *     aliases (ForkServe, item 1);
+ *   - the gated delta rule of Flide section 3.2.2, Eq. 4,
+ *       S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  o_t = S_t q_t,
+ *     where a child continues from its parent's state at the fork point by
+ *     index, without copying it.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns and
+ *     allocates every buffer (activations, K/V page pool, states, checkpoints,
+ *     workspace); the library never allocates device memory.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the default
+ *     stream) and return without synchronising, except fk_read_status.
+ *   - Return value: FK_OK (0), or a negative FK_E_* code detected on the host
+ *     (nothing is enqueued then).  Errors in the tree that only the device can
+ *     see (the tree arrays are device-resident and never read by the host) are
+ *     recorded in a status word inside the workspace; every later kernel of
+ *     the round then exits early and outputs are unspecified.  Read it with
+ *     fk_read_status.
+ *   - Tensors are dense, row-major, in stream order.  dtype FK_F32 (float) or
+ *     FK_BF16 (bfloat16, round-to-nearest-even on output).  a, b and all
+ *     recurrent states are always float32 (Flide section 3.4 stores the
+ *     recurrent state in float32).
+ *   - Results are batch invariant: a branch's output bits depend only on its
+ *     own path and segment boundaries, never on the other requests of the
+ *     round (Flide, section 3.5).  No reduction uses atomics.
+ */
+#ifndef FORKGDN_H
+#define FORKGDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *fk_stream_t; /* hipStream_t */
+
+enum fk_dtype { FK_F32 = 0, FK_BF16 = 1 };
+
+enum fk_status {
+    FK_OK = 0,
+    FK_E_INVALID_ARG = -1,   /* null pointer, bad size, slot out of range        */
+    FK_E_UNSUPPORTED = -2,   /* shape/dtype combination without a kernel        */
+    FK_E_WORKSPACE = -3,     /* workspace smaller than fk_workspace_bytes        */
+    FK_E_HIP = -4,           /* a HIP runtime call failed                        */
+    /* tree errors: host validator and device status word */
+    FK_E_SEG_RANGE = -10,    /* a token names a segment outside [0, S)           */
+    FK_E_NONCONTIG = -11,    /* a segment's tokens are not contiguous            */
+    FK_E_PARENT = -12,       /* parent index out of range, or a segment's own    */
+    FK_E_CYCLE = -13,        /* parent chain loops or is deeper than max_depth   */
+    FK_E_FORK = -14,         /* fork outside [0, parent length]; root fork != 0  */
+    FK_E_EMPTY = -15,        /* live segment without tokens, cached with tokens  */
+    FK_E_CACHED = -16,       /* cached segment below a live one; live child of a
+                                cached segment not forked at its end             */
+    FK_E_PAGES = -17,        /* page list too short or a page id out of range    */
+    FK_E_CAPACITY = -18,     /* more segments on one level than level_cap, or
+                                more distinct fork points than fork_cap          */
+    FK_E_STATE_SLOT = -19    /* state slot missing or out of range               */
+};
+
+/* Deepest supported tree (levels 0 .. FK_MAX_DEPTH-1). */
+#define FK_MAX_DEPTH 8
+/* Query rows of one attention tile (tokens per tile, anchored at the start of
+   every segment, so tiles never straddle segments). */
+#define FK_TILE_TOKENS 16
+
+/*
+ * Round description (Flide section 3.3.1: all variables set by the round
+ * composition live in device buffers; section 3.3.2: launches are sized by
+ * host-known capacities, so the host never reads the tree).
+ *
+ * A segment is LIVE (its tokens are in the stream, contiguous and in position
+ * order) or CACHED (seg_cached_len > 0: no stream tokens; its K/V are already
+ * in the page pool and its final recurrent state is state_in[seg_state_in]).
+ * seg_fork[c] is how many of the parent's tokens child c sees (0..len(parent);
+ * a root has 0).  A segment's first position is its parent's first position
+ * plus its fork, so question positions continue from the state (Flide 3.2).
+ * Cached segments must be roots or children of cached segments, and a live
+ * child of a cached segment must fork at the cached segment's end.
+ *
+ * K/V pages: segment s owns pages seg_pages[seg_page_off[s] ..
+ * seg_page_off[s+1]); its token i lives in page seg_pages[off + i/page_size],
+ * slot i % page_size.  Every segment starts on a fresh page; a child aliases
+ * its ancestors' pages by reading them, never by copying (ForkServe item 1:
+ * fork copies the parent page table and an alias length).
+ */
+typedef struct fk_tree_meta {
+    int32_t T;           /* live stream tokens (>= 0)                            */
+    int32_t S;           /* segments, live + cached (>= 1)                       */
+    int32_t max_depth;   /* capacity: tree levels, 1..FK_MAX_DEPTH               */
+    int32_t level_cap;   /* capacity: live segments on any one level (>= 1)      */
+    int32_t fork_cap;    /* capacity: distinct (parent, fork offset) fork points */
+    int32_t page_size;   /* tokens per K/V page; must be 16                      */
+    int32_t n_pages;     /* pages in the K/V pool                                */
+    int32_t n_state_in;  /* slots in state_in (may be 0)                         */
+    int32_t n_state_out; /* slots in state_out (may be 0)                        */
+    const int32_t *tok_seg;        /* [T]   segment of every stream token         */
+    const int32_t *seg_parent;     /* [S]   parent segment, -1 for a root         */
+    const int32_t *seg_fork;       /* [S]   parent tokens this segment sees       */
+    const int32_t *seg_cached_len; /* [S]   history length if cached, else 0      */
+    const int32_t *seg_page_off;   /* [S+1] CSR offsets into seg_pages            */
+    const int32_t *seg_pages;      /* [seg_page_off[S]] page ids                  */
+    const int32_t *seg_state_in;   /* [S]   state_in slot of a cached segment, -1 */
+    const int32_t *seg_state_out;  /* [S]   state_out slot to receive the final
+                                            state of a live segment, or -1        */
+} fk_tree_meta;
+
+/*
+ * Workspace bytes for a round: derived metadata (segment starts, positions,
+ * ancestor chains, attention tiles, level lists, fork-point routing, status)
+ * plus the fork-point states of one Gated DeltaNet layer, fork_cap *
+ * gdn_state_elems floats (gdn_state_elems = Hv * dv * dk of the largest GDN
+ * layer, 0 if none).  `meta` is (host); only its scalar fields are read.
+ */
+size_t fk_workspace_bytes(const fk_tree_meta *meta, int64_t gdn_state_elems);
+
+/*
+ * fk_tree_build -- the tree-metadata builder (Flide section 3.3.1: the
+ * attention tile table and the GDN chunk work are built on the GPU).  Turns
+ * (tok_seg, seg_parent, seg_fork, ...) into per-segment starts, lengths,
+ * first positions, depths and ancestor chains; per-token positions; the
+ * attention tile list (FK_TILE_TOKENS rows per tile, each with its ancestor
+ * KV ranges implied by the chain -- no dense mask); per-level GDN segment
+ * lists; and the fork-point routing (one state slot per distinct fork point,
+ * shared by all children forked there).  Validates the tree on the device
+ * and records the first error class in the status word.  Must run before
+ * kv_append / fork_attn_forward / gdn_fork_forward of the same round; the
+ * workspace then holds the round's metadata for every layer.
+ * meta: (host) struct of device arrays.  ws: >= fk_workspace_bytes.
+ */
+int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes, fk_stream_t stream);
+
+/*
+ * fk_tree_validate_host -- the same checks as fk_tree_build, on HOST arrays
+ * (meta's pointers are host pointers here).  Returns FK_OK or the error
+ * class.  For callers holding host copies of the tree, and for tests.
+ */
+int fk_tree_validate_host(const fk_tree_meta *meta_host);
+
+/*
+ * fk_token_positions -- copy the builder's per-token positions (int32 [T],
+ * device) to `pos` (device): position = segment first position + local index
+ * (Flide section 3.2: positions of a question continue from the state).
+ */
+int fk_token_positions(const fk_tree_meta *meta, const void *ws, int32_t *pos, fk_stream_t stream);
+
+/*
+ * kv_append -- write the stream's keys and values into the paged pool
+ * (ForkServe item 1: a write allocates the writer's own pages only; children
+ * alias the parent's).  k, v: [T, Hkv, d] in `dtype`.  k_pool: [n_pages, Hkv,
+ * page_size, d]; v_pool: [n_pages, Hkv, d, page_size] (values are stored
+ * transposed inside a page so that the attention kernel reads them with keys
+ * contiguous).  Cached segments' pages are left untouched.  Slots past a
+ * segment's last token in its last page are left untouched (readers mask them).
+ */
+int kv_append(const fk_tree_meta *meta, const void *k, const void *v, int dtype, int Hkv, int d,
+              void *k_pool, void *v_pool, const void *ws, fk_stream_t stream);
+
+/*
+ * fork_attn_forward -- ForkAttention prefill over the whole round (Flide
+ * section 3.2.1, Eq. 3; section 3.3.1: fully visible key blocks load without
+ * a mask, only partially visible ones are masked; other requests' keys are
+ * never read).  Appends k, v of the live tokens into the page pool (as
+ * kv_append), then for every stream token x and q head h computes
+ *   out[x,h] = sum_{y in vis(x)} softmax_y(scale * q[x,h] . k_y) v_y
+ * where vis(x) is the cached history of x's root, each ancestor's first
+ * `fork` tokens, and x's own segment up to and including x; q head h reads
+ * kv head h / (Hq / Hkv).
+ * q, out: [T, Hq, d]; k, v: [T, Hkv, d]; pools as in kv_append.
+ * Supported: FK_F32 with d <= 128; FK_BF16 with d == 128 and Hq/Hkv == 8.
+ */
+int fork_attn_forward(const fk_tree_meta *meta, const void *q, const void *k, const void *v,
+                      int dtype, int Hq, int Hkv, int d, float scale, void *k_pool, void *v_pool,
+                      void *out, void *ws, size_t ws_bytes, fk_stream_t stream);
+
+/*
+ * gdn_fork_forward -- forked Gated DeltaNet (Flide section 3.2.2, Eq. 4, and
+ * its two-call scheme generalised to one launch per tree level).  A fresh
+ * root starts from the zero state; a child of a cached segment from
+ * state_in[seg_state_in[parent]]; any other child from its parent's state
+ * after `fork` tokens, which the parent's launch writes once per distinct
+ * fork point into the workspace and every child reads by index (no copy per
+ * child).  Each live segment with seg_state_out >= 0 writes its final state
+ * to state_out[slot] (a checkpoint, Flide section 3.4).
+ * q, k: [T, Hk, dk]; v, out: [T, Hv, dv] in `dtype`; a, b: [T, Hv] float
+ * (decay and write strength, after the sigmoid); v-head h reads q/k head
+ * h / (Hv / Hk).  state_in: [n_state_in, Hv, dv, dk] float, state_out:
+ * [n_state_out, Hv, dv, dk] float (S is dv x dk, row-major).
+ * Supported: FK_F32 with dk, dv in {16, 32, 64, 128}; FK_BF16 with
+ * dk == dv == 128 (chunked form on MFMA, fp32 state).
+ */
+int gdn_fork_forward(const fk_tree_meta *meta, const void *q, const void *k, const void *v,
+                     const float *a, const float *b, int dtype, int Hk, int Hv, int dk, int dv,
+                     const float *state_in, float *state_out, void *out, void *ws, size_t ws_bytes,
+                     fk_stream_t stream);
+
+/*
+ * gdn_checkpoint_save -- copy the float32 recurrent state in
+ * state_out[slot] ([Hv, dv, dk]) into caller storage `ckpt` (Flide section
+ * 3.4: a checkpoint keeps the float32 state; the K/V before the checkpoint
+ * stay in their pages, which the caller retains by id).
+ */
+int gdn_checkpoint_save(const float *state_out, int32_t slot, int32_t n_slots, int32_t Hv,
+                        int32_t dk, int32_t dv, float *ckpt, fk_stream_t stream);
+
+/*
+ * gdn_checkpoint_resume -- copy a saved state `ckpt` ([Hv, dv, dk] float)
+ * into state_in[slot], so that a cached segment of a later round continues
+ * exactly where the saved pass stopped (Flide section 3.4).
+ */
+int gdn_checkpoint_resume(const float *ckpt, float *state_in, int32_t slot, int32_t n_slots,
+                          int32_t Hv, int32_t dk, int32_t dv, fk_stream_t stream);
+
+/*
+ * fk_read_status -- synchronise `stream` and read the device status word
+ * written by fk_tree_build into *status_out (host): FK_OK or a tree error.
+ */
+int fk_read_status(const void *ws, fk_stream_t stream, int32_t *status_out);
+
+/* Static description of a status code (host). */
+const char *fk_strerror(int code);
+
+/* ABI version of this header (host). */
+int fk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FORKGDN_H */
