@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(HERE, "libforkgdn.so")
 FK_F32, FK_BF16 = 0, 1
 FK_MAX_DEPTH = 8
 FK_TILE_TOKENS = 16
+FK_GDN_CHUNK = 64
 
 STATUS = {0: "FK_OK", -1: "FK_E_INVALID_ARG", -2: "FK_E_UNSUPPORTED", -3: "FK_E_WORKSPACE",
           -4: "FK_E_HIP", -10: "FK_E_SEG_RANGE", -11: "FK_E_NONCONTIG", -12: "FK_E_PARENT",
@@ -57,7 +58,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L = ctypes.CDLL(path)
     vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
     mp = ctypes.POINTER(TreeMetaC)
-    L.fk_workspace_bytes.argtypes = [mp, ctypes.c_int64]
+    L.fk_workspace_bytes.argtypes = [mp, i32, i32, i32]
     L.fk_workspace_bytes.restype = sz
     L.fk_tree_build.argtypes = [mp, vp, sz, vp]
     L.fk_tree_validate_host.argtypes = [mp]

@@ -89,13 +89,15 @@ def make_tree_meta(tok_seg, seg_parent, seg_fork, seg_cached_len, seg_page_off, 
                     seg_state_out=dev(seg_state_out, S))
 
 
-def fk_workspace_bytes(meta: TreeMeta, gdn_state_elems: int = 0) -> int:
+def fk_workspace_bytes(meta: TreeMeta, gdn_Hv: int = 0, gdn_dk: int = 0, gdn_dv: int = 0) -> int:
     m = meta.c()
-    return int(_lib.load().fk_workspace_bytes(ctypes.byref(m), int(gdn_state_elems)))
+    return int(_lib.load().fk_workspace_bytes(ctypes.byref(m), int(gdn_Hv), int(gdn_dk), int(gdn_dv)))
 
 
-def alloc_workspace(meta: TreeMeta, gdn_state_elems: int = 0, device="cuda") -> torch.Tensor:
-    n = fk_workspace_bytes(meta, gdn_state_elems)
+def alloc_workspace(meta: TreeMeta, gdn_Hv: int = 0, gdn_dk: int = 0, gdn_dv: int = 0,
+                    device="cuda") -> torch.Tensor:
+    """Workspace for a round and the largest GDN layer (Hv, dk, dv) it runs."""
+    n = fk_workspace_bytes(meta, gdn_Hv, gdn_dk, gdn_dv)
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 

@@ -118,7 +118,7 @@ extern "C" int fork_attn_forward(const fk_tree_meta *meta, const void *q, const 
     if (Hq < 1 || Hq % Hkv) return FK_E_UNSUPPORTED;
     if (meta->T > 0 && (!q || !out)) return FK_E_INVALID_ARG;
     if (!(scale > 0.f) || !isfinite(scale)) return FK_E_INVALID_ARG;
-    const WsLayout L = ws_layout(*meta, 0);
+    const WsLayout L = ws_layout(*meta, 0, 0, 0);
     if (ws_bytes < L.total) return FK_E_WORKSPACE;
     if (dtype == FK_BF16 && (d != 128 || Hq / Hkv != 8)) return FK_E_UNSUPPORTED;
     if (meta->T == 0) return FK_OK;

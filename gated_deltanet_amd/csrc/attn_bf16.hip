@@ -211,7 +211,7 @@ using namespace fk;
 int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv, float scale, const void *k_pool,
                         const void *v_pool, void *out, const void *ws, hipStream_t st)
 {
-    const WsLayout L = ws_layout(*meta, 0);
+    const WsLayout L = ws_layout(*meta, 0, 0, 0);
     dim3 grid((unsigned)L.tile_cap, (unsigned)Hkv);
     attn::k_attn_bf16<<<grid, attn::THREADS, 0, st>>>(
         (const uint16_t *)q, Hq, Hkv, scale * 1.4426950408889634f, (const uint16_t *)k_pool,

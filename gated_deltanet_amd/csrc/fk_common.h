@@ -19,6 +19,7 @@ enum HeaderSlot {
     H_STATUS = 0,       // FK_OK or the first (most negative) tree error
     H_NTILES = 1,       // attention tiles in tile_seg / tile_row0
     H_NFORKS = 2,       // distinct fork points (GDN fork-state slots used)
+    H_NCHUNKS = 3,      // GDN chunks in chunk_seg / chunk_row0
     H_LEVEL0 = 4,       // live segments per level: H_LEVEL0 + d, d < FK_MAX_DEPTH
     H_WORDS = 64
 };
@@ -45,9 +46,14 @@ struct WsLayout {
     size_t tile_seg;      // int32[tile_cap]
     size_t tile_row0;     // int32[tile_cap]
     size_t lvl_seg;       // int32[FK_MAX_DEPTH*level_cap]
-    size_t fork_states;   // float[fork_cap * state_elems]
+    size_t chunk_seg;     // int32[chunk_cap] segment of each GDN chunk
+    size_t chunk_row0;    // int32[chunk_cap] first local token of each chunk
+    size_t seg_chunk0;    // int32[S] index of a live segment's first chunk
+    size_t fork_states;   // float[fork_cap * Hv * dv * dk]
+    size_t tmat;          // bf16[chunk_cap * Hv * FK_GDN_CHUNK^2] per-chunk (I + A)^-1
     size_t total;
     int64_t tile_cap;
+    int64_t chunk_cap;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -57,8 +63,16 @@ inline int64_t tile_capacity(int64_t T, int64_t S)
     return (T + FK_TILE_TOKENS - 1) / FK_TILE_TOKENS + S;
 }
 
-inline WsLayout ws_layout(const fk_tree_meta &m, int64_t state_elems)
+inline int64_t chunk_capacity(int64_t T, int64_t S)
 {
+    return (T + FK_GDN_CHUNK - 1) / FK_GDN_CHUNK + S;
+}
+
+// Hv, dk, dv: the largest Gated DeltaNet layer that will use the workspace
+// (0 if none).
+inline WsLayout ws_layout(const fk_tree_meta &m, int64_t Hv, int64_t dk, int64_t dv)
+{
+    const int64_t state_elems = Hv * dk * dv;
     WsLayout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -69,6 +83,7 @@ inline WsLayout ws_layout(const fk_tree_meta &m, int64_t state_elems)
     const size_t S = (size_t)(m.S > 0 ? m.S : 0), T = (size_t)(m.T > 0 ? m.T : 0);
     const size_t fc = (size_t)(m.fork_cap > 0 ? m.fork_cap : 0);
     L.tile_cap = tile_capacity((int64_t)T, (int64_t)S);
+    L.chunk_cap = chunk_capacity((int64_t)T, (int64_t)S);
     L.header = take(H_WORDS * 4);
     L.seg_start = take(S * 4);
     L.seg_end = take(S * 4);
@@ -89,7 +104,11 @@ inline WsLayout ws_layout(const fk_tree_meta &m, int64_t state_elems)
     L.tile_seg = take((size_t)L.tile_cap * 4);
     L.tile_row0 = take((size_t)L.tile_cap * 4);
     L.lvl_seg = take((size_t)FK_MAX_DEPTH * (size_t)(m.level_cap > 0 ? m.level_cap : 1) * 4);
+    L.chunk_seg = take((size_t)L.chunk_cap * 4);
+    L.chunk_row0 = take((size_t)L.chunk_cap * 4);
+    L.seg_chunk0 = take(S * 4);
     L.fork_states = take(fc * (size_t)(state_elems > 0 ? state_elems : 0) * 4);
+    L.tmat = take((size_t)L.chunk_cap * (size_t)(Hv > 0 ? Hv : 0) * FK_GDN_CHUNK * FK_GDN_CHUNK * 2);
     L.total = off;
     return L;
 }

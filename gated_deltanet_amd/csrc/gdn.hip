@@ -141,8 +141,7 @@ extern "C" int gdn_fork_forward(const fk_tree_meta *meta, const void *q, const v
     } else {
         return FK_E_UNSUPPORTED;
     }
-    const int64_t elems = (int64_t)Hv * dk * dv;
-    const WsLayout L = ws_layout(*meta, elems);
+    const WsLayout L = ws_layout(*meta, Hv, dk, dv);
     if (ws_bytes < L.total) return FK_E_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     float *fork_states = ws_at<float>(ws, L.fork_states);

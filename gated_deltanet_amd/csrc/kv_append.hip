@@ -56,7 +56,7 @@ using namespace fk;
 int fk_launch_kv_append(const fk_tree_meta *meta, const void *k, const void *v, int dtype, int Hkv, int d,
                         void *k_pool, void *v_pool, const void *ws, hipStream_t st)
 {
-    const WsLayout L = ws_layout(*meta, 0);
+    const WsLayout L = ws_layout(*meta, 0, 0, 0);
     dim3 grid((unsigned)L.tile_cap, (unsigned)Hkv);
     const int32_t *hdr = ws_at<int32_t>(ws, L.header);
     const int32_t *ts = ws_at<int32_t>(ws, L.tile_seg), *tr = ws_at<int32_t>(ws, L.tile_row0);

@@ -83,7 +83,7 @@ struct BuildArgs {
     fk_tree_meta m;
     int32_t *header, *seg_start, *seg_end, *seg_nrun, *seg_len, *seg_pos0, *seg_depth, *seg_anc;
     int32_t *seg_src, *seg_owner, *kid_cnt, *kid_off, *kid_fill, *kids, *emit_off, *emit_pos;
-    int32_t *tile_seg, *tile_row0, *lvl_seg;
+    int32_t *tile_seg, *tile_row0, *lvl_seg, *chunk_seg, *chunk_row0, *seg_chunk0;
 };
 
 __device__ bool block_failed(int32_t *header, int *flag)
@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
     // phase 3a: scans -- attention tiles, children CSR, level lists
     if (threadIdx.x < FK_MAX_DEPTH) lvl_lds[threadIdx.x] = 0;
     __syncthreads();
-    int tile_base = 0, kid_base = 0;
+    int tile_base = 0, kid_base = 0, chunk_base = 0;
     for (int base = 0; base < S; base += blockDim.x) {
         const int s = base + threadIdx.x;
         const bool in = s < S;
@@ -155,6 +155,14 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
         for (int r = 0; r < ntile; ++r) {
             A.tile_seg[toff + r] = s;
             A.tile_row0[toff + r] = r * FK_TILE_TOKENS;
+        }
+        const int nchunk = live ? (len + FK_GDN_CHUNK - 1) / FK_GDN_CHUNK : 0;
+        const int coff = chunk_base + block_scan(nchunk, lds, &tot);
+        chunk_base += tot;
+        if (in) A.seg_chunk0[s] = live ? coff : -1;
+        for (int r = 0; r < nchunk; ++r) {
+            A.chunk_seg[coff + r] = s;
+            A.chunk_row0[coff + r] = r * FK_GDN_CHUNK;
         }
         const int kc = in ? A.kid_cnt[s] : 0;
         const int koff = kid_base + block_scan(kc, lds, &tot);
@@ -176,6 +184,7 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
     if (threadIdx.x == 0) {
         A.kid_off[S] = kid_base;
         A.header[H_NTILES] = tile_base;
+        A.header[H_NCHUNKS] = chunk_base;
         for (int dd = 0; dd < FK_MAX_DEPTH; ++dd) A.header[H_LEVEL0 + dd] = dd < m.max_depth ? lvl_lds[dd] : 0;
     }
     __syncthreads();
@@ -265,10 +274,10 @@ int check_meta_scalars(const fk_tree_meta *m)
 
 using namespace fk;
 
-extern "C" size_t fk_workspace_bytes(const fk_tree_meta *meta, int64_t gdn_state_elems)
+extern "C" size_t fk_workspace_bytes(const fk_tree_meta *meta, int32_t gdn_Hv, int32_t gdn_dk, int32_t gdn_dv)
 {
-    if (!meta) return 0;
-    return ws_layout(*meta, gdn_state_elems).total;
+    if (!meta || gdn_Hv < 0 || gdn_dk < 0 || gdn_dv < 0) return 0;
+    return ws_layout(*meta, gdn_Hv, gdn_dk, gdn_dv).total;
 }
 
 extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes, fk_stream_t stream)
@@ -276,7 +285,7 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
     int rc = check_meta_scalars(meta);
     if (rc) return rc;
     if (!ws) return FK_E_INVALID_ARG;
-    const WsLayout L = ws_layout(*meta, 0);
+    const WsLayout L = ws_layout(*meta, 0, 0, 0);
     if (ws_bytes < L.total) return FK_E_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     BuildArgs A;
@@ -300,6 +309,9 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
     A.tile_seg = ws_at<int32_t>(ws, L.tile_seg);
     A.tile_row0 = ws_at<int32_t>(ws, L.tile_row0);
     A.lvl_seg = ws_at<int32_t>(ws, L.lvl_seg);
+    A.chunk_seg = ws_at<int32_t>(ws, L.chunk_seg);
+    A.chunk_row0 = ws_at<int32_t>(ws, L.chunk_row0);
+    A.seg_chunk0 = ws_at<int32_t>(ws, L.seg_chunk0);
     const int S = meta->S, T = meta->T;
     k_init<<<(S + 255) / 256 > 0 ? (S + 255) / 256 : 1, 256, 0, st>>>(A.header, A.seg_nrun, A.kid_cnt,
                                                                    A.kid_fill, S);
@@ -375,7 +387,7 @@ extern "C" int fk_token_positions(const fk_tree_meta *meta, const void *ws, int3
     if (rc) return rc;
     if (!ws || (meta->T > 0 && !pos)) return FK_E_INVALID_ARG;
     if (meta->T == 0) return FK_OK;
-    const WsLayout L = ws_layout(*meta, 0);
+    const WsLayout L = ws_layout(*meta, 0, 0, 0);
     FK_HIP(hipMemcpyAsync(pos, ws_at<int32_t>(ws, L.tok_pos), (size_t)meta->T * 4, hipMemcpyDeviceToDevice,
                           (hipStream_t)stream));
     return FK_OK;

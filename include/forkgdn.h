@@ -75,6 +75,9 @@ enum fk_status {
 /* Query rows of one attention tile (tokens per tile, anchored at the start of
    every segment, so tiles never straddle segments). */
 #define FK_TILE_TOKENS 16
+/* Tokens per Gated DeltaNet chunk of the bf16 path (anchored at the start of
+   every segment, so a trunk's chunking never depends on its branches). */
+#define FK_GDN_CHUNK 64
 
 /*
  * Round description (Flide section 3.3.1: all variables set by the round
@@ -119,12 +122,14 @@ typedef struct fk_tree_meta {
 
 /*
  * Workspace bytes for a round: derived metadata (segment starts, positions,
- * ancestor chains, attention tiles, level lists, fork-point routing, status)
- * plus the fork-point states of one Gated DeltaNet layer, fork_cap *
- * gdn_state_elems floats (gdn_state_elems = Hv * dv * dk of the largest GDN
- * layer, 0 if none).  `meta` is (host); only its scalar fields are read.
+ * ancestor chains, attention tiles, GDN chunks, level lists, fork-point
+ * routing, status) plus the scratch of one Gated DeltaNet layer: fork_cap
+ * fork-point states (Hv * dv * dk floats each) and one bf16 64 x 64 matrix
+ * per chunk and v-head.  gdn_Hv, gdn_dk, gdn_dv describe the largest GDN
+ * layer that will use the workspace (all 0 if none).  `meta` is (host); only
+ * its scalar fields are read.
  */
-size_t fk_workspace_bytes(const fk_tree_meta *meta, int64_t gdn_state_elems);
+size_t fk_workspace_bytes(const fk_tree_meta *meta, int32_t gdn_Hv, int32_t gdn_dk, int32_t gdn_dv);
 
 /*
  * fk_tree_build -- the tree-metadata builder (Flide section 3.3.1: the
@@ -132,8 +137,9 @@ size_t fk_workspace_bytes(const fk_tree_meta *meta, int64_t gdn_state_elems);
  * (tok_seg, seg_parent, seg_fork, ...) into per-segment starts, lengths,
  * first positions, depths and ancestor chains; per-token positions; the
  * attention tile list (FK_TILE_TOKENS rows per tile, each with its ancestor
- * KV ranges implied by the chain -- no dense mask); per-level GDN segment
- * lists; and the fork-point routing (one state slot per distinct fork point,
+ * KV ranges implied by the chain -- no dense mask); the GDN chunk list
+ * (FK_GDN_CHUNK tokens per chunk); per-level GDN segment lists; and the
+ * fork-point routing (one state slot per distinct fork point,
  * shared by all children forked there).  Validates the tree on the device
  * and records the first error class in the status word.  Must run before
  * kv_append / fork_attn_forward / gdn_fork_forward of the same round; the

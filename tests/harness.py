@@ -75,7 +75,7 @@ class GpuRound:
             hplan = fk.plan_round(hts, np.full(len(cached), -1), np.zeros(len(cached)),
                                   np.zeros(len(cached)), first_page=0, n_pages=self.n_pages,
                                   device=device)
-            hws = fk.alloc_workspace(hplan.meta, 0, device)
+            hws = fk.alloc_workspace(hplan.meta, device=device)
             fk.fk_tree_build(hplan.meta, hws)
             fk.kv_append(hplan.meta, dev_tensor(inp, "ak", True), dev_tensor(inp, "av", True),
                          self.k_pool, self.v_pool, hws)
@@ -84,7 +84,7 @@ class GpuRound:
                                   n_pages=self.n_pages, seg_state_in=ssi, seg_state_out=sso,
                                   n_state_in=n_in, n_state_out=n_out, device=device)
         self.meta = self.plan.meta
-        self.ws = fk.alloc_workspace(self.meta, sh.Hv * sh.dk * sh.dv, device)
+        self.ws = fk.alloc_workspace(self.meta, sh.Hv, sh.dk, sh.dv, device=device)
         self.state_in = None
         if n_in:
             st = state_in_np if state_in_np is not None else np.zeros((n_in, sh.Hv, sh.dv, sh.dk))

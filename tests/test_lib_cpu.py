@@ -85,9 +85,10 @@ def test_workspace_bytes_grow_with_round():
     m = _lib.TreeMetaC()
     m.T, m.S, m.max_depth, m.level_cap, m.fork_cap, m.page_size = 100, 4, 2, 3, 1, 16
     L = _lib.load()
-    a = L.fk_workspace_bytes(ctypes.byref(m), 0)
-    b = L.fk_workspace_bytes(ctypes.byref(m), 2 * 32 * 32)
-    assert b - a >= 2 * 32 * 32 * 4 and a > 0
+    a = L.fk_workspace_bytes(ctypes.byref(m), 0, 0, 0)
+    b = L.fk_workspace_bytes(ctypes.byref(m), 2, 32, 32)
+    # one fork-point state plus one 64 x 64 bf16 matrix per chunk and v-head
+    assert b - a >= 2 * 32 * 32 * 4 + (2 + 4) * 2 * 64 * 64 * 2 and a > 0
 
 
 def test_bad_arguments_rejected_on_host():
