@@ -150,8 +150,9 @@ def kv_append(meta: TreeMeta, k, v, k_pool, v_pool, ws, stream=None):
 
 def fork_attn_forward(meta: TreeMeta, q, k, v, k_pool, v_pool, ws, scale=None, out=None,
                       stream=None) -> torch.Tensor:
+    """k = v = None: the round's keys/values are already in the pool."""
     T, Hq, d = q.shape
-    Hkv = k.shape[1]
+    Hkv = k_pool.shape[1]
     if out is None:
         out = torch.empty_like(q)
     scale = float(scale if scale is not None else d ** -0.5)

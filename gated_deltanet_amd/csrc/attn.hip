@@ -113,7 +113,9 @@ extern "C" int fork_attn_forward(const fk_tree_meta *meta, const void *q, const 
                                  int Hq, int Hkv, int d, float scale, void *k_pool, void *v_pool, void *out,
                                  void *ws, size_t ws_bytes, fk_stream_t stream)
 {
-    int rc = fk_check_kv_args(meta, k, v, dtype, Hkv, d, k_pool, v_pool, ws);
+    // k == v == NULL: this round's keys/values are already in the pool
+    const bool append = k || v;
+    int rc = fk_check_kv_args(meta, append ? k : q, append ? v : q, dtype, Hkv, d, k_pool, v_pool, ws);
     if (rc) return rc;
     if (Hq < 1 || Hq % Hkv) return FK_E_UNSUPPORTED;
     if (meta->T > 0 && (!q || !out)) return FK_E_INVALID_ARG;
@@ -123,8 +125,10 @@ extern "C" int fork_attn_forward(const fk_tree_meta *meta, const void *q, const 
     if (dtype == FK_BF16 && (d != 128 || Hq / Hkv != 8)) return FK_E_UNSUPPORTED;
     if (meta->T == 0) return FK_OK;
     hipStream_t st = (hipStream_t)stream;
-    rc = fk_launch_kv_append(meta, k, v, dtype, Hkv, d, k_pool, v_pool, ws, st);
-    if (rc) return rc;
+    if (append) {
+        rc = fk_launch_kv_append(meta, k, v, dtype, Hkv, d, k_pool, v_pool, ws, st);
+        if (rc) return rc;
+    }
     if (dtype == FK_BF16) return fk_launch_attn_bf16(meta, q, Hq, Hkv, scale, k_pool, v_pool, out, ws, st);
     dim3 grid((unsigned)L.tile_cap, (unsigned)Hq);
     k_attn_f32<<<grid, 64, 0, st>>>((const float *)q, Hq, Hkv, d, scale, (const float *)k_pool,

@@ -1,10 +1,431 @@
-// gdn_bf16.hip -- placeholder until the chunked MFMA kernel lands.
+// gdn_bf16.hip -- forked Gated DeltaNet, chunked form on bf16 MFMA (gfx950).
+//
+// Eq. 4 of Flide section 3.2.2, S_t = a_t S_{t-1} (I - b_t k_t k_t^T) +
+// b_t v_t k_t^T and o_t = S_t q_t (S is dv x dk), rewritten exactly over a
+// chunk of c <= 64 tokens.  With l_i = sum_{j<=i} ln a_j (log space), S0 the
+// state entering the chunk and rows = tokens:
+//   A_ij = b_i e^{l_i - l_j} (k_i . k_j) for j < i,   T = (I + A)^-1
+//   U    = T diag(b) (V - diag(e^l) K S0^T)          (the corrected writes)
+//   O    = diag(e^l) Q S0^T + (Gamma o Q K^T) U,  Gamma_ij = e^{l_i - l_j}, j <= i
+//   S^T after r tokens = e^{l_{r-1}} S0^T + K_{<r}^T diag(e^{l_{r-1} - l_j}) U_{<r}
+// (unrolling Eq. 4 inside the chunk: S_i = g_i S0 + sum_{j<=i} (g_i/g_j) u_j k_j^T
+// with u_i = b_i (v_i - a_i S_{i-1} k_i); every ratio g_i/g_j <= 1 is taken as
+// e^{l_i - l_j}).  Chunks are anchored at the start of every segment, so a
+// trunk's arithmetic never depends on its branches (Flide section 3.5).
+//
+// k_gdn_prep  (all chunks of the round at once, before the level launches):
+//             T of every (chunk, v-head) in fp32 by forward substitution,
+//             stored as bf16.  It depends only on k, a, b -- never on a state.
+// k_gdn_chunk (one launch per tree level): one work-group per (segment,
+//             v-head, 64-wide dv slice) walks the segment's chunks in order.
+//             Each wave keeps its 128 x 16 slice of S^T in fp32 MFMA
+//             accumulator registers for the whole segment and feeds it
+//             straight back as an MFMA operand (a fixed permutation of the
+//             reduction index makes the accumulator layout the operand
+//             layout), so the state never leaves registers between chunks.
+//             It starts from the zero state, state_in, or the parent's
+//             fork-point state (by index), and writes the states at the
+//             segment's fork points once each.
 #include <hip/hip_runtime.h>
 
 #include "fk_common.h"
 
-int fk_launch_gdn_bf16(const fk_tree_meta *, int, const void *, const void *, const void *, const float *,
-                       const float *, int, int, const float *, float *, void *, const void *, float *, hipStream_t)
+namespace fk {
+namespace gdnk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int C = FK_GDN_CHUNK;   // 64 tokens
+constexpr int DK = 128, DV = 128;
+constexpr int DVS = 64;           // dv columns of one work-group (4 waves x 16)
+constexpr int KS = DK + 8;        // LDS stride (bf16) of key/query rows
+constexpr int TS = C + 8;         // LDS stride (bf16) of 64-wide rows (T, P, K^T)
+constexpr int AS = C + 4;         // LDS stride (fp32) of the prep matrix
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
 {
-    return FK_E_UNSUPPORTED;
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack(f32x4 lo, f32x4 hi)
+{
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[e] = (__bf16)lo[e];
+        v[e + 4] = (__bf16)hi[e];
+    }
+    return v;
+}
+
+// Operand with a permuted reduction index: for a k-step over 32 positions,
+// lane group G = lane/16 supplies positions 4G..4G+3 and 16+4G..16+4G+3 --
+// exactly the rows a 16x16 accumulator pair holds in that lane group.
+__device__ __forceinline__ bf16x8 load_perm(const uint16_t *row, int ks, int G)
+{
+    const uint2 lo = *reinterpret_cast<const uint2 *>(row + ks * 32 + 4 * G);
+    const uint2 hi = *reinterpret_cast<const uint2 *>(row + ks * 32 + 16 + 4 * G);
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ bf16x8 load_row8(const uint16_t *row, int ks, int G)
+{
+    return as_bf16x8(*reinterpret_cast<const uint4 *>(row + ks * 32 + 8 * G));
+}
+
+// ---------------------------------------------------------------------------
+// T = (I + A)^-1 per (chunk, v-head).  One wave; lane = column of T.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(64)
+k_gdn_prep(const uint16_t *__restrict__ k, const float *__restrict__ a, const float *__restrict__ b, int Hk, int Hv,
+           const int32_t *__restrict__ header, const int32_t *__restrict__ chunk_seg,
+           const int32_t *__restrict__ chunk_row0, const int32_t *__restrict__ seg_start,
+           const int32_t *__restrict__ seg_len, uint16_t *__restrict__ tmat)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t ks[C * KS];
+    __shared__ __attribute__((aligned(16))) float am[C * AS];
+    __shared__ float lsh[C], esh[C];
+    if (header[H_STATUS] != FK_OK) return;
+    const int c = blockIdx.x, h = blockIdx.y;
+    if (c >= header[H_NCHUNKS]) return;
+    const int lane = threadIdx.x, G = lane >> 4, c16 = lane & 15;
+    const int s = chunk_seg[c], r0 = chunk_row0[c];
+    const int n = min(C, seg_len[s] - r0);
+    const size_t t0 = (size_t)seg_start[s] + r0;
+    const int g = h / (Hv / Hk);
+#pragma unroll 4
+    for (int j = 0; j < 16; ++j) {
+        const int idx = j * 64 + lane, row = idx >> 4, c8 = idx & 15;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < n) v = *reinterpret_cast<const uint4 *>(k + ((t0 + row) * Hk + g) * DK + c8 * 8);
+        *reinterpret_cast<uint4 *>(ks + row * KS + c8 * 8) = v;
+    }
+    float la = 0.f, eta = 0.f;
+    if (lane < n) {
+        la = logf(a[(t0 + lane) * Hv + h]);
+        eta = b[(t0 + lane) * Hv + h];
+    }
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(la, o, 64);
+        if (lane >= o) la += y;
+    }
+    lsh[lane] = la;
+    esh[lane] = eta;
+    __syncthreads();
+    // A = strictly lower part of diag(b) (Gamma o K K^T)
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+        for (int tj = 0; tj <= ti; ++tj) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk)
+                acc = mfma(load_row8(ks + (ti * 16 + c16) * KS, kk, G), load_row8(ks + (tj * 16 + c16) * KS, kk, G),
+                           acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + G * 4 + r, j = tj * 16 + c16;
+                am[i * AS + j] = j < i ? esh[i] * __expf(lsh[i] - lsh[j]) * acc[r] : 0.f;
+            }
+        }
+    __syncthreads();
+    // forward substitution: T[i][col] = delta(i, col) - sum_{j<i} A[i][j] T[j][col]
+    float x[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        float acc0 = i == lane ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < i; j += 2) {
+            acc0 -= am[i * AS + j] * x[j];
+            if (j + 1 < i) acc1 -= am[i * AS + j + 1] * x[j + 1];
+        }
+        x[i] = acc0 + acc1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C; ++i) am[i * AS + lane] = x[i];
+    __syncthreads();
+    uint16_t *dst = tmat + (((size_t)c * Hv + h) * C + lane) * C;
+#pragma unroll
+    for (int j8 = 0; j8 < C / 8; ++j8) {
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)am[lane * AS + j8 * 8 + e];
+        *reinterpret_cast<uint4 *>(dst + j8 * 8) = __builtin_bit_cast(uint4, v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Sequential chunk walk of one (segment, v-head, dv slice).
+// ---------------------------------------------------------------------------
+struct ChunkArgs {
+    const uint16_t *q, *k, *v;
+    const float *a, *b;
+    uint16_t *out;
+    int Hk, Hv, level, level_cap;
+    const int32_t *header, *lvl_seg, *seg_start, *seg_len, *seg_src, *seg_chunk0, *emit_off, *emit_pos,
+        *seg_state_out;
+    const uint16_t *tmat;
+    const float *state_in;
+    float *state_out, *fork_states;
+};
+
+// 16 dk x 4-row fp32 state fragment <-> global [dv][dk] row (4 consecutive dk)
+__device__ __forceinline__ void store_state(float *base, int dvc, int G, const f32x4 *st)
+{
+#pragma unroll
+    for (int i = 0; i < DK / 16; ++i)
+        *reinterpret_cast<f32x4 *>(base + (size_t)dvc * DK + i * 16 + G * 4) = st[i];
+}
+
+__global__ void __launch_bounds__(256) k_gdn_chunk(ChunkArgs A)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t kr[C * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t qr[C * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t kt[DK * TS];
+    __shared__ __attribute__((aligned(16))) uint16_t tm[C * TS];
+    __shared__ __attribute__((aligned(16))) uint16_t pm[C * TS];
+    __shared__ float lsh[C], esh[C], gsh[C];
+    if (A.header[H_STATUS] != FK_OK) return;
+    if ((int)blockIdx.x >= A.header[H_LEVEL0 + A.level]) return;
+    const int s = A.lvl_seg[A.level * A.level_cap + blockIdx.x];
+    const int h = blockIdx.y, g = h / (A.Hv / A.Hk);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int G = lane >> 4, c16 = lane & 15;
+    const int dvc = blockIdx.z * DVS + w * 16 + c16;   // this lane's state column (dv index)
+    const size_t SZ = (size_t)DV * DK;
+
+    // P's strictly-upper 16x16 tiles stay zero for the whole walk
+    for (int e = tid; e < C * C; e += 256) {
+        const int i = e / C, j = e % C;
+        if (j / 16 > i / 16) pm[i * TS + j] = 0;
+    }
+    f32x4 st[DK / 16];
+    {
+        const int src = A.seg_src[s];
+        const float *S0 = src == -1 ? nullptr
+                                    : (src >= 0 ? A.fork_states + ((size_t)src * A.Hv + h) * SZ
+                                                : A.state_in + ((size_t)(-2 - src) * A.Hv + h) * SZ);
+#pragma unroll
+        for (int i = 0; i < DK / 16; ++i)
+            st[i] = S0 ? *reinterpret_cast<const f32x4 *>(S0 + (size_t)dvc * DK + i * 16 + G * 4)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    int e = A.emit_off[s];
+    const int e_end = A.emit_off[s + 1];
+    while (e < e_end && A.emit_pos[e] == 0) {
+        store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, st);
+        ++e;
+    }
+    const int len = A.seg_len[s], chunk0 = A.seg_chunk0[s];
+    const int nch = (len + C - 1) / C;
+    for (int c = 0; c < nch; ++c) {
+        const int n = min(C, len - c * C);
+        const size_t t0 = (size_t)A.seg_start[s] + (size_t)c * C;
+        __syncthreads();   // the previous chunk is done with every LDS buffer
+        // stage keys (rows and transposed), queries, T
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = j * 256 + tid, row = idx >> 4, c8 = idx & 15;
+            uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
+            if (row < n) {
+                kv = *reinterpret_cast<const uint4 *>(A.k + ((t0 + row) * A.Hk + g) * DK + c8 * 8);
+                qv = *reinterpret_cast<const uint4 *>(A.q + ((t0 + row) * A.Hk + g) * DK + c8 * 8);
+            }
+            *reinterpret_cast<uint4 *>(kr + row * KS + c8 * 8) = kv;
+            *reinterpret_cast<uint4 *>(qr + row * KS + c8 * 8) = qv;
+            const uint16_t *k8 = reinterpret_cast<const uint16_t *>(&kv);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) kt[(c8 * 8 + x) * TS + row] = k8[x];
+        }
+        {
+            const uint16_t *tsrc = A.tmat + ((size_t)(chunk0 + c) * A.Hv + h) * C * C;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int idx = j * 256 + tid, row = idx >> 3, c8 = idx & 7;
+                *reinterpret_cast<uint4 *>(tm + row * TS + c8 * 8) =
+                    *reinterpret_cast<const uint4 *>(tsrc + row * C + c8 * 8);
+            }
+        }
+        if (w == 0) {
+            float la = 0.f, eta = 0.f;
+            if (lane < n) {
+                la = logf(A.a[(t0 + lane) * A.Hv + h]);
+                eta = A.b[(t0 + lane) * A.Hv + h];
+            }
+            for (int o = 1; o < 64; o <<= 1) {
+                const float y = __shfl_up(la, o, 64);
+                if (lane >= o) la += y;
+            }
+            lsh[lane] = la;
+            esh[lane] = eta;
+            gsh[lane] = __expf(la);
+        }
+        __syncthreads();
+
+        // (1) P = Gamma o Q K^T, lower tiles (10) shared among the waves
+        for (int pi = w; pi < 10; pi += 4) {
+            const int ti = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
+            const int tj = pi - ti * (ti + 1) / 2;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk)
+                acc = mfma(load_row8(qr + (ti * 16 + c16) * KS, kk, G), load_row8(kr + (tj * 16 + c16) * KS, kk, G),
+                           acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + G * 4 + r, j = tj * 16 + c16;
+                const float v = j <= i ? __expf(lsh[i] - lsh[j]) * acc[r] : 0.f;
+                pm[i * TS + j] = __builtin_bit_cast(uint16_t, (__bf16)v);
+            }
+        }
+        // (2) X = K S0^T and Y = Q S0^T for this wave's 16 dv columns
+        bf16x8 sb[DK / 32];
+#pragma unroll
+        for (int ks2 = 0; ks2 < DK / 32; ++ks2) sb[ks2] = pack(st[2 * ks2], st[2 * ks2 + 1]);
+        f32x4 xa[C / 16], ya[C / 16];
+#pragma unroll
+        for (int mt = 0; mt < C / 16; ++mt) {
+            xa[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            ya[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks2 = 0; ks2 < DK / 32; ++ks2) {
+                xa[mt] = mfma(load_perm(kr + (mt * 16 + c16) * KS, ks2, G), sb[ks2], xa[mt]);
+                ya[mt] = mfma(load_perm(qr + (mt * 16 + c16) * KS, ks2, G), sb[ks2], ya[mt]);
+            }
+        }
+        // (3) R = diag(b) (V - diag(e^l) X);  U = T R
+#pragma unroll
+        for (int mt = 0; mt < C / 16; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = mt * 16 + G * 4 + r;
+                float vv = 0.f;
+                if (i < n) vv = bf16_to_f32(A.v[((t0 + i) * A.Hv + h) * DV + dvc]);
+                xa[mt][r] = esh[i] * (vv - gsh[i] * xa[mt][r]);
+            }
+        bf16x8 rb[2] = {pack(xa[0], xa[1]), pack(xa[2], xa[3])};
+        f32x4 ua[C / 16];
+#pragma unroll
+        for (int mt = 0; mt < C / 16; ++mt) {
+            ua[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2) ua[mt] = mfma(load_perm(tm + (mt * 16 + c16) * TS, ks2, G), rb[ks2], ua[mt]);
+        }
+        __syncthreads();   // P complete
+        // (4) O = diag(e^l) Y + P U
+        bf16x8 ub[2] = {pack(ua[0], ua[1]), pack(ua[2], ua[3])};
+#pragma unroll
+        for (int mt = 0; mt < C / 16; ++mt) {
+            f32x4 oa;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oa[r] = gsh[mt * 16 + G * 4 + r] * ya[mt][r];
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2) oa = mfma(load_perm(pm + (mt * 16 + c16) * TS, ks2, G), ub[ks2], oa);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = mt * 16 + G * 4 + r;
+                if (i < n) A.out[((t0 + i) * A.Hv + h) * DV + dvc] = __builtin_bit_cast(uint16_t, (__bf16)oa[r]);
+            }
+        }
+        // (5) fork points strictly inside this chunk: state after `off` tokens
+        while (e < e_end && A.emit_pos[e] < c * C + n) {
+            const int off = A.emit_pos[e] - c * C;   // 1 .. n-1
+            const float lr = lsh[off - 1];
+            f32x4 u0[C / 16];
+#pragma unroll
+            for (int mt = 0; mt < C / 16; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = mt * 16 + G * 4 + r;
+                    u0[mt][r] = j < off ? __expf(lr - lsh[j]) * ua[mt][r] : 0.f;
+                }
+            const bf16x8 eb[2] = {pack(u0[0], u0[1]), pack(u0[2], u0[3])};
+            const float gr = __expf(lr);
+            f32x4 tmp[DK / 16];
+#pragma unroll
+            for (int i = 0; i < DK / 16; ++i) {
+                tmp[i] = st[i] * gr;
+#pragma unroll
+                for (int ks2 = 0; ks2 < 2; ++ks2) tmp[i] = mfma(load_perm(kt + (i * 16 + c16) * TS, ks2, G), eb[ks2], tmp[i]);
+            }
+            store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, tmp);
+            ++e;
+        }
+        // (6) S^T <- e^{l_last} S^T + K^T diag(e^{l_last - l}) U
+        const float ll = lsh[C - 1];
+#pragma unroll
+        for (int mt = 0; mt < C / 16; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ua[mt][r] *= __expf(ll - lsh[mt * 16 + G * 4 + r]);
+        const bf16x8 wb[2] = {pack(ua[0], ua[1]), pack(ua[2], ua[3])};
+        const float gl = __expf(ll);
+#pragma unroll
+        for (int i = 0; i < DK / 16; ++i) {
+            st[i] *= gl;
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2) st[i] = mfma(load_perm(kt + (i * 16 + c16) * TS, ks2, G), wb[ks2], st[i]);
+        }
+        // (7) a fork point at the end of this chunk
+        while (e < e_end && A.emit_pos[e] == c * C + n) {
+            store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, st);
+            ++e;
+        }
+    }
+    const int so = A.seg_state_out[s];
+    if (so >= 0) store_state(A.state_out + ((size_t)so * A.Hv + h) * SZ, dvc, G, st);
+}
+
+}  // namespace gdnk
+}  // namespace fk
+
+using namespace fk;
+
+int fk_launch_gdn_bf16_prep(const fk_tree_meta *meta, const void *k, const float *a, const float *b, int Hk, int Hv,
+                            const void *ws, hipStream_t st)
+{
+    const WsLayout L = ws_layout(*meta, Hv, gdnk::DK, gdnk::DV);
+    dim3 grid((unsigned)L.chunk_cap, (unsigned)Hv);
+    gdnk::k_gdn_prep<<<grid, 64, 0, st>>>((const uint16_t *)k, a, b, Hk, Hv, ws_at<int32_t>(ws, L.header),
+                                          ws_at<int32_t>(ws, L.chunk_seg), ws_at<int32_t>(ws, L.chunk_row0),
+                                          ws_at<int32_t>(ws, L.seg_start), ws_at<int32_t>(ws, L.seg_len),
+                                          const_cast<uint16_t *>(ws_at<uint16_t>(ws, L.tmat)));
+    return launch_status();
+}
+
+int fk_launch_gdn_bf16(const fk_tree_meta *meta, int level, const void *q, const void *k, const void *v,
+                       const float *a, const float *b, int Hk, int Hv, const float *state_in, float *state_out,
+                       void *out, const void *ws, float *fork_states, hipStream_t st)
+{
+    const WsLayout L = ws_layout(*meta, Hv, gdnk::DK, gdnk::DV);
+    gdnk::ChunkArgs A;
+    A.q = (const uint16_t *)q;
+    A.k = (const uint16_t *)k;
+    A.v = (const uint16_t *)v;
+    A.a = a;
+    A.b = b;
+    A.out = (uint16_t *)out;
+    A.Hk = Hk;
+    A.Hv = Hv;
+    A.level = level;
+    A.level_cap = meta->level_cap;
+    A.header = ws_at<int32_t>(ws, L.header);
+    A.lvl_seg = ws_at<int32_t>(ws, L.lvl_seg);
+    A.seg_start = ws_at<int32_t>(ws, L.seg_start);
+    A.seg_len = ws_at<int32_t>(ws, L.seg_len);
+    A.seg_src = ws_at<int32_t>(ws, L.seg_src);
+    A.seg_chunk0 = ws_at<int32_t>(ws, L.seg_chunk0);
+    A.emit_off = ws_at<int32_t>(ws, L.emit_off);
+    A.emit_pos = ws_at<int32_t>(ws, L.emit_pos);
+    A.seg_state_out = meta->seg_state_out;
+    A.tmat = ws_at<uint16_t>(ws, L.tmat);
+    A.state_in = state_in;
+    A.state_out = state_out;
+    A.fork_states = fork_states;
+    dim3 grid((unsigned)meta->level_cap, (unsigned)Hv, (unsigned)(gdnk::DV / gdnk::DVS));
+    gdnk::k_gdn_chunk<<<grid, 256, 0, st>>>(A);
+    return launch_status();
 }

@@ -88,7 +88,7 @@ struct BuildArgs {
 
 __device__ bool block_failed(int32_t *header, int *flag)
 {
-    __threadfence();
+    __threadfence_block();
     __syncthreads();
     if (threadIdx.x == 0) *flag = __hip_atomic_load(header + H_STATUS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
@@ -247,6 +247,19 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
     }
 }
 
+// Phase 3 (pages): one block per segment checks the page ids the segment
+// uses, in parallel.  Runs only when the tree passed every other check.
+__global__ void k_check_pages(int S, const int32_t *__restrict__ seg_len, const int32_t *__restrict__ page_off,
+                              const int32_t *__restrict__ pages, int page_size, int n_pages, int32_t *header)
+{
+    if (header[H_STATUS] != FK_OK) return;
+    const int s = blockIdx.x;
+    if (s >= S) return;
+    const int need = (seg_len[s] + page_size - 1) / page_size, a = page_off[s];
+    for (int j = threadIdx.x; j < need; j += blockDim.x)
+        if (!rule_page_id(pages[a + j], n_pages)) set_error(header, FK_E_PAGES);
+}
+
 __global__ void k_positions(const int32_t *__restrict__ tok_seg, int T, const int32_t *header,
                             const int32_t *seg_start, const int32_t *seg_pos0, int32_t *tok_pos)
 {
@@ -323,6 +336,11 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
     }
     k_build<<<1, BUILD_THREADS, 0, st>>>(A);
     if ((rc = launch_status())) return rc;
+    if (meta->seg_page_off) {
+        k_check_pages<<<S, 256, 0, st>>>(S, A.seg_len, meta->seg_page_off, meta->seg_pages, meta->page_size,
+                                         meta->n_pages, A.header);
+        if ((rc = launch_status())) return rc;
+    }
     if (T > 0) {
         k_positions<<<(T + 255) / 256, 256, 0, st>>>(meta->tok_seg, T, A.header, A.seg_start, A.seg_pos0,
                                                     ws_at<int32_t>(ws, L.tok_pos));
@@ -378,6 +396,12 @@ extern "C" int fk_tree_validate_host(const fk_tree_meta *m)
         forks += owner;
     }
     if (forks > m->fork_cap) code = imin(code, FK_E_CAPACITY);
+    if (code || !m->seg_page_off || !m->seg_pages) return code;
+    for (int s = 0; s < S; ++s) {
+        const int need = (len[s] + m->page_size - 1) / m->page_size;
+        for (int j = 0; j < need; ++j)
+            if (!rule_page_id(m->seg_pages[m->seg_page_off[s] + j], m->n_pages)) return FK_E_PAGES;
+    }
     return code;
 }
 

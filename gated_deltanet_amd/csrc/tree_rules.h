@@ -14,8 +14,9 @@
 //            a live child of a cached segment forks at its end;     FK_E_CACHED,
 //            chain reaches a root within max_depth levels;          FK_E_CYCLE,
 //            state slots in range, a cached parent brings a state;  FK_E_STATE_SLOT,
-//            page lists cover the segment with ids in range         FK_E_PAGES
-//   phase 3  capacities: live segments per level, fork points       FK_E_CAPACITY
+//            page lists are long enough for the segment             FK_E_PAGES
+//   phase 3  capacities: live segments per level, fork points;      FK_E_CAPACITY,
+//            every page id a segment uses lies in [0, n_pages)      FK_E_PAGES
 // A phase runs only when the previous ones found nothing; the reported code
 // is the most negative one of the first failing phase.
 #pragma once
@@ -109,16 +110,12 @@ FK_HD int rule_links(int s, int S, int max_depth, const int32_t *parent, const i
     if (page_off) {
         const int a = page_off[s], b = page_off[s + 1];
         const int need = (len[s] + page_size - 1) / page_size;
-        if (a < 0 || b < a || b - a < need) {
-            code = imin(code, FK_E_PAGES);
-        } else if (pages) {
-            for (int j = 0; j < need; ++j) {
-                const int pg = pages[a + j];
-                if (pg < 0 || pg >= n_pages) { code = imin(code, FK_E_PAGES); break; }
-            }
-        }
+        if (a < 0 || b < a || b - a < need) code = imin(code, FK_E_PAGES);
     }
     return code;
 }
+
+// phase 3: page ids of segment s (its first ceil(len/page_size) entries)
+FK_HD bool rule_page_id(int page, int n_pages) { return page >= 0 && page < n_pages; }
 
 }  // namespace fk

@@ -184,7 +184,9 @@ int kv_append(const fk_tree_meta *meta, const void *k, const void *v, int dtype,
  * where vis(x) is the cached history of x's root, each ancestor's first
  * `fork` tokens, and x's own segment up to and including x; q head h reads
  * kv head h / (Hq / Hkv).
- * q, out: [T, Hq, d]; k, v: [T, Hkv, d]; pools as in kv_append.
+ * q, out: [T, Hq, d]; k, v: [T, Hkv, d]; pools as in kv_append.  With k and
+ * v both NULL the append is skipped (the round's keys/values are already in
+ * the pool, e.g. written by kv_append).
  * Supported: FK_F32 with d <= 128; FK_BF16 with d == 128 and Hq/Hkv == 8.
  */
 int fork_attn_forward(const fk_tree_meta *meta, const void *q, const void *k, const void *v,
