@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index (0-4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=3,
+    ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests of the workload in the CPU oracle sample")
     return ap.parse_args()
 

@@ -77,31 +77,50 @@ __device__ __forceinline__ bf16x8 load_row8(const uint16_t *row, int ks, int G)
 }
 
 // ---------------------------------------------------------------------------
-// T = (I + A)^-1 per (chunk, v-head).  One wave; lane = column of T.
+// T = (I + A)^-1 per (chunk, v-head).  Four items per work-group, one wave
+// each; lane = column of T.  A wave's key rows and its A matrix share LDS.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(64)
+constexpr int PREP_WAVES = 4;
+constexpr int PREP_LDS = C * KS * 2;   // bytes: key rows, later the fp32 A / T matrix
+static_assert(C * AS * 4 <= PREP_LDS, "A overlays the key rows");
+
+__global__ void __launch_bounds__(64 * PREP_WAVES)
 k_gdn_prep(const uint16_t *__restrict__ k, const float *__restrict__ a, const float *__restrict__ b, int Hk, int Hv,
            const int32_t *__restrict__ header, const int32_t *__restrict__ chunk_seg,
            const int32_t *__restrict__ chunk_row0, const int32_t *__restrict__ seg_start,
            const int32_t *__restrict__ seg_len, uint16_t *__restrict__ tmat)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t ks[C * KS];
-    __shared__ __attribute__((aligned(16))) float am[C * AS];
-    __shared__ float lsh[C], esh[C];
+    __shared__ __attribute__((aligned(16))) char lds[PREP_WAVES * PREP_LDS];
+    __shared__ float lsh_all[PREP_WAVES][C], esh_all[PREP_WAVES][C];
     if (header[H_STATUS] != FK_OK) return;
-    const int c = blockIdx.x, h = blockIdx.y;
-    if (c >= header[H_NCHUNKS]) return;
-    const int lane = threadIdx.x, G = lane >> 4, c16 = lane & 15;
+    const int nitems = header[H_NCHUNKS] * Hv;
+    if ((int)blockIdx.x * PREP_WAVES >= nitems) return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, G = lane >> 4, c16 = lane & 15;
+    const int item = blockIdx.x * PREP_WAVES + w;
+    const bool valid = item < nitems;   // every wave reaches every barrier
+    const int c = valid ? item / Hv : 0, h = valid ? item % Hv : 0;
+    uint16_t *ks = reinterpret_cast<uint16_t *>(lds + w * PREP_LDS);
+    float *am = reinterpret_cast<float *>(lds + w * PREP_LDS);
+    float *lsh = lsh_all[w], *esh = esh_all[w];
     const int s = chunk_seg[c], r0 = chunk_row0[c];
-    const int n = min(C, seg_len[s] - r0);
+    const int n = valid ? min(C, seg_len[s] - r0) : 0;
     const size_t t0 = (size_t)seg_start[s] + r0;
     const int g = h / (Hv / Hk);
-#pragma unroll 4
-    for (int j = 0; j < 16; ++j) {
-        const int idx = j * 64 + lane, row = idx >> 4, c8 = idx & 15;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < n) v = *reinterpret_cast<const uint4 *>(k + ((t0 + row) * Hk + g) * DK + c8 * 8);
-        *reinterpret_cast<uint4 *>(ks + row * KS + c8 * 8) = v;
+    {
+        uint4 kv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int idx = j * 64 + lane, row = idx >> 4, c8 = idx & 15;
+            const int rr = row < n ? row : 0;
+            kv[j] = make_uint4(0, 0, 0, 0);
+            if (n > 0) kv[j] = *reinterpret_cast<const uint4 *>(k + ((t0 + rr) * Hk + g) * DK + c8 * 8);
+            if (row >= n) kv[j] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int idx = j * 64 + lane, row = idx >> 4, c8 = idx & 15;
+            *reinterpret_cast<uint4 *>(ks + row * KS + c8 * 8) = kv[j];
+        }
     }
     float la = 0.f, eta = 0.f;
     if (lane < n) {
@@ -115,22 +134,29 @@ k_gdn_prep(const uint16_t *__restrict__ k, const float *__restrict__ a, const fl
     lsh[lane] = la;
     esh[lane] = eta;
     __syncthreads();
-    // A = strictly lower part of diag(b) (Gamma o K K^T)
+    // K K^T, lower 16x16 tiles, into registers (the key rows are overwritten next)
+    f32x4 gt[10];
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
+    for (int ti = 0, p = 0; ti < 4; ++ti)
 #pragma unroll
-        for (int tj = 0; tj <= ti; ++tj) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int tj = 0; tj <= ti; ++tj, ++p) {
+            gt[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk)
-                acc = mfma(load_row8(ks + (ti * 16 + c16) * KS, kk, G), load_row8(ks + (tj * 16 + c16) * KS, kk, G),
-                           acc);
+                gt[p] = mfma(load_row8(ks + (ti * 16 + c16) * KS, kk, G), load_row8(ks + (tj * 16 + c16) * KS, kk, G),
+                             gt[p]);
+        }
+    __syncthreads();
+    // A = strictly lower part of diag(b) (Gamma o K K^T); upper part never read
+#pragma unroll
+    for (int ti = 0, p = 0; ti < 4; ++ti)
+#pragma unroll
+        for (int tj = 0; tj <= ti; ++tj, ++p)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = ti * 16 + G * 4 + r, j = tj * 16 + c16;
-                am[i * AS + j] = j < i ? esh[i] * __expf(lsh[i] - lsh[j]) * acc[r] : 0.f;
+                am[i * AS + j] = j < i ? esh[i] * __expf(lsh[i] - lsh[j]) * gt[p][r] : 0.f;
             }
-        }
     __syncthreads();
     // forward substitution: T[i][col] = delta(i, col) - sum_{j<i} A[i][j] T[j][col]
     float x[C];
@@ -148,6 +174,7 @@ k_gdn_prep(const uint16_t *__restrict__ k, const float *__restrict__ a, const fl
 #pragma unroll
     for (int i = 0; i < C; ++i) am[i * AS + lane] = x[i];
     __syncthreads();
+    if (!valid) return;
     uint16_t *dst = tmat + (((size_t)c * Hv + h) * C + lane) * C;
 #pragma unroll
     for (int j8 = 0; j8 < C / 8; ++j8) {
@@ -160,6 +187,11 @@ k_gdn_prep(const uint16_t *__restrict__ k, const float *__restrict__ a, const fl
 
 // ---------------------------------------------------------------------------
 // Sequential chunk walk of one (segment, v-head, dv slice).
+// Waves 0-3 (consumers) own the state and run the products of chunk c;
+// waves 4-5 (producers) meanwhile stage chunk c+1 into the other LDS buffer
+// -- key rows and their transpose, query rows, T, the dv slice of the
+// values, the decays -- half of the rows each, with every global load of
+// their half in flight at once.
 // ---------------------------------------------------------------------------
 struct ChunkArgs {
     const uint16_t *q, *k, *v;
@@ -173,6 +205,20 @@ struct ChunkArgs {
     float *state_out, *fork_states;
 };
 
+constexpr int CONSUMERS = DVS / 16;           // 4 waves, 16 dv columns each
+constexpr int PRODUCERS = 2;
+constexpr int CHUNK_THREADS = (CONSUMERS + PRODUCERS) * 64;
+constexpr int VS = DVS + 8;                   // LDS stride (bf16) of the value slice
+
+struct ChunkBuf {
+    uint16_t kr[C * KS];     // key rows
+    uint16_t qr[C * KS];     // query rows
+    uint16_t kt[DK * TS];    // keys transposed
+    uint16_t tm[C * TS];     // T = (I + A)^-1
+    uint16_t vs[C * VS];     // values of this dv slice
+    float lsh[C], esh[C], gsh[C];   // log-decay prefix, write strength, e^l
+};
+
 // 16 dk x 4-row fp32 state fragment <-> global [dv][dk] row (4 consecutive dk)
 __device__ __forceinline__ void store_state(float *base, int dvc, int G, const f32x4 *st)
 {
@@ -181,30 +227,92 @@ __device__ __forceinline__ void store_state(float *base, int dvc, int G, const f
         *reinterpret_cast<f32x4 *>(base + (size_t)dvc * DK + i * 16 + G * 4) = st[i];
 }
 
-__global__ void __launch_bounds__(256) k_gdn_chunk(ChunkArgs A)
+// producer `part` stages rows [32 part, 32 part + 32) of chunk `c` into `B`
+__device__ __forceinline__ void stage_chunk(ChunkBuf &B, const ChunkArgs &A, int s, int c, int h, int g, int lane,
+                                            int part, int dv0, int chunk0)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t kr[C * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t qr[C * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t kt[DK * TS];
-    __shared__ __attribute__((aligned(16))) uint16_t tm[C * TS];
-    __shared__ __attribute__((aligned(16))) uint16_t pm[C * TS];
-    __shared__ float lsh[C], esh[C], gsh[C];
-    if (A.header[H_STATUS] != FK_OK) return;
-    if ((int)blockIdx.x >= A.header[H_LEVEL0 + A.level]) return;
-    const int s = A.lvl_seg[A.level * A.level_cap + blockIdx.x];
-    const int h = blockIdx.y, g = h / (A.Hv / A.Hk);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int G = lane >> 4, c16 = lane & 15;
-    const int dvc = blockIdx.z * DVS + w * 16 + c16;   // this lane's state column (dv index)
-    const size_t SZ = (size_t)DV * DK;
-
-    // P's strictly-upper 16x16 tiles stay zero for the whole walk
-    for (int e = tid; e < C * C; e += 256) {
-        const int i = e / C, j = e % C;
-        if (j / 16 > i / 16) pm[i * TS + j] = 0;
+    const int len = A.seg_len[s];
+    const int n = min(C, len - c * C);
+    const size_t t0 = (size_t)A.seg_start[s] + (size_t)c * C;
+    const uint16_t *tsrc = A.tmat + ((size_t)(chunk0 + c) * A.Hv + h) * C * C;
+    const int rbase = part * (C / PRODUCERS);
+    uint4 kv[8], qv[8], tv[4], vv[4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int idx = j * 64 + lane, row = rbase + (idx >> 4), c8 = idx & 15;
+        const int rr = row < n ? row : n - 1;
+        kv[j] = *reinterpret_cast<const uint4 *>(A.k + ((t0 + rr) * A.Hk + g) * DK + c8 * 8);
+        qv[j] = *reinterpret_cast<const uint4 *>(A.q + ((t0 + rr) * A.Hk + g) * DK + c8 * 8);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int idx = j * 64 + lane, row = rbase + (idx >> 3), c8 = idx & 7;
+        const int rr = row < n ? row : n - 1;
+        tv[j] = *reinterpret_cast<const uint4 *>(tsrc + row * C + c8 * 8);
+        vv[j] = *reinterpret_cast<const uint4 *>(A.v + ((t0 + rr) * A.Hv + h) * DV + dv0 + c8 * 8);
+    }
+    float a_raw = 1.f, b_raw = 0.f;
+    if (part == 0) {
+        const int lr = lane < n ? lane : n - 1;
+        a_raw = A.a[(t0 + lr) * A.Hv + h];
+        b_raw = A.b[(t0 + lr) * A.Hv + h];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int idx = j * 64 + lane, row = rbase + (idx >> 4), c8 = idx & 15;
+        if (row >= n) kv[j] = qv[j] = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(B.kr + row * KS + c8 * 8) = kv[j];
+        *reinterpret_cast<uint4 *>(B.qr + row * KS + c8 * 8) = qv[j];
+        const uint16_t *k8 = reinterpret_cast<const uint16_t *>(&kv[j]);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) B.kt[(c8 * 8 + x) * TS + row] = k8[x];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int idx = j * 64 + lane, row = rbase + (idx >> 3), c8 = idx & 7;
+        if (row >= n) vv[j] = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(B.tm + row * TS + c8 * 8) = tv[j];
+        *reinterpret_cast<uint4 *>(B.vs + row * VS + c8 * 8) = vv[j];
+    }
+    if (part == 0) {
+        float la = lane < n ? logf(a_raw) : 0.f;
+        const float eta = lane < n ? b_raw : 0.f;
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(la, o, 64);
+            if (lane >= o) la += y;
+        }
+        B.lsh[lane] = la;
+        B.esh[lane] = eta;
+        B.gsh[lane] = __expf(la);
+    }
+}
+
+__global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
+{
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    ChunkBuf *buf = reinterpret_cast<ChunkBuf *>(smem);
+    if (A.header[H_STATUS] != FK_OK) return;
+    // 1-D grid, work item = (segment rank, v-head, dv slice) with the slice
+    // fastest: the live items are the lowest ids, so they spread over all XCDs
+    constexpr int NSL = DV / DVS;
+    const int rank = blockIdx.x / (A.Hv * NSL);
+    if (rank >= A.header[H_LEVEL0 + A.level]) return;
+    const int s = A.lvl_seg[A.level * A.level_cap + rank];
+    const int h = (blockIdx.x / NSL) % A.Hv, g = h / (A.Hv / A.Hk);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const bool producer = w >= CONSUMERS;
+    const int part = w - CONSUMERS;
+    const int G = lane >> 4, c16 = lane & 15;
+    const int dv0 = (blockIdx.x % NSL) * DVS;
+    const int dvc = dv0 + w * 16 + c16;   // a consumer lane's state column (dv index)
+    const size_t SZ = (size_t)DV * DK;
+    const int len = A.seg_len[s], chunk0 = A.seg_chunk0[s];
+    const int nch = (len + C - 1) / C;
+
     f32x4 st[DK / 16];
-    {
+    int e = A.emit_off[s];
+    const int e_end = A.emit_off[s + 1];
+    if (!producer) {
         const int src = A.seg_src[s];
         const float *S0 = src == -1 ? nullptr
                                     : (src >= 0 ? A.fork_states + ((size_t)src * A.Hv + h) * SZ
@@ -213,170 +321,131 @@ __global__ void __launch_bounds__(256) k_gdn_chunk(ChunkArgs A)
         for (int i = 0; i < DK / 16; ++i)
             st[i] = S0 ? *reinterpret_cast<const f32x4 *>(S0 + (size_t)dvc * DK + i * 16 + G * 4)
                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        while (e < e_end && A.emit_pos[e] == 0) {
+            store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, st);
+            ++e;
+        }
+    } else {
+        stage_chunk(buf[0], A, s, 0, h, g, lane, part, dv0, chunk0);
     }
-    int e = A.emit_off[s];
-    const int e_end = A.emit_off[s + 1];
-    while (e < e_end && A.emit_pos[e] == 0) {
-        store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, st);
-        ++e;
-    }
-    const int len = A.seg_len[s], chunk0 = A.seg_chunk0[s];
-    const int nch = (len + C - 1) / C;
+    __syncthreads();
     for (int c = 0; c < nch; ++c) {
-        const int n = min(C, len - c * C);
-        const size_t t0 = (size_t)A.seg_start[s] + (size_t)c * C;
-        __syncthreads();   // the previous chunk is done with every LDS buffer
-        // stage keys (rows and transposed), queries, T
+        ChunkBuf &B = buf[c & 1];
+        if (producer) {
+            if (c + 1 < nch) stage_chunk(buf[(c + 1) & 1], A, s, c + 1, h, g, lane, part, dv0, chunk0);
+        } else {
+            const int n = min(C, len - c * C);
+            const size_t t0 = (size_t)A.seg_start[s] + (size_t)c * C;
+            // X = K S0^T, Y = Q S0^T for this wave's 16 dv columns
+            f32x4 xa[C / 16], ya[C / 16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int idx = j * 256 + tid, row = idx >> 4, c8 = idx & 15;
-            uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-            if (row < n) {
-                kv = *reinterpret_cast<const uint4 *>(A.k + ((t0 + row) * A.Hk + g) * DK + c8 * 8);
-                qv = *reinterpret_cast<const uint4 *>(A.q + ((t0 + row) * A.Hk + g) * DK + c8 * 8);
-            }
-            *reinterpret_cast<uint4 *>(kr + row * KS + c8 * 8) = kv;
-            *reinterpret_cast<uint4 *>(qr + row * KS + c8 * 8) = qv;
-            const uint16_t *k8 = reinterpret_cast<const uint16_t *>(&kv);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) kt[(c8 * 8 + x) * TS + row] = k8[x];
-        }
-        {
-            const uint16_t *tsrc = A.tmat + ((size_t)(chunk0 + c) * A.Hv + h) * C * C;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int idx = j * 256 + tid, row = idx >> 3, c8 = idx & 7;
-                *reinterpret_cast<uint4 *>(tm + row * TS + c8 * 8) =
-                    *reinterpret_cast<const uint4 *>(tsrc + row * C + c8 * 8);
-            }
-        }
-        if (w == 0) {
-            float la = 0.f, eta = 0.f;
-            if (lane < n) {
-                la = logf(A.a[(t0 + lane) * A.Hv + h]);
-                eta = A.b[(t0 + lane) * A.Hv + h];
-            }
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(la, o, 64);
-                if (lane >= o) la += y;
-            }
-            lsh[lane] = la;
-            esh[lane] = eta;
-            gsh[lane] = __expf(la);
-        }
-        __syncthreads();
-
-        // (1) P = Gamma o Q K^T, lower tiles (10) shared among the waves
-        for (int pi = w; pi < 10; pi += 4) {
-            const int ti = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
-            const int tj = pi - ti * (ti + 1) / 2;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk)
-                acc = mfma(load_row8(qr + (ti * 16 + c16) * KS, kk, G), load_row8(kr + (tj * 16 + c16) * KS, kk, G),
-                           acc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = ti * 16 + G * 4 + r, j = tj * 16 + c16;
-                const float v = j <= i ? __expf(lsh[i] - lsh[j]) * acc[r] : 0.f;
-                pm[i * TS + j] = __builtin_bit_cast(uint16_t, (__bf16)v);
-            }
-        }
-        // (2) X = K S0^T and Y = Q S0^T for this wave's 16 dv columns
-        bf16x8 sb[DK / 32];
-#pragma unroll
-        for (int ks2 = 0; ks2 < DK / 32; ++ks2) sb[ks2] = pack(st[2 * ks2], st[2 * ks2 + 1]);
-        f32x4 xa[C / 16], ya[C / 16];
-#pragma unroll
-        for (int mt = 0; mt < C / 16; ++mt) {
-            xa[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            ya[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < C / 16; ++mt) xa[mt] = ya[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks2 = 0; ks2 < DK / 32; ++ks2) {
-                xa[mt] = mfma(load_perm(kr + (mt * 16 + c16) * KS, ks2, G), sb[ks2], xa[mt]);
-                ya[mt] = mfma(load_perm(qr + (mt * 16 + c16) * KS, ks2, G), sb[ks2], ya[mt]);
+                const bf16x8 sb = pack(st[2 * ks2], st[2 * ks2 + 1]);
+#pragma unroll
+                for (int mt = 0; mt < C / 16; ++mt) {
+                    xa[mt] = mfma(load_perm(B.kr + (mt * 16 + c16) * KS, ks2, G), sb, xa[mt]);
+                    ya[mt] = mfma(load_perm(B.qr + (mt * 16 + c16) * KS, ks2, G), sb, ya[mt]);
+                }
             }
-        }
-        // (3) R = diag(b) (V - diag(e^l) X);  U = T R
-#pragma unroll
-        for (int mt = 0; mt < C / 16; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = mt * 16 + G * 4 + r;
-                float vv = 0.f;
-                if (i < n) vv = bf16_to_f32(A.v[((t0 + i) * A.Hv + h) * DV + dvc]);
-                xa[mt][r] = esh[i] * (vv - gsh[i] * xa[mt][r]);
-            }
-        bf16x8 rb[2] = {pack(xa[0], xa[1]), pack(xa[2], xa[3])};
-        f32x4 ua[C / 16];
-#pragma unroll
-        for (int mt = 0; mt < C / 16; ++mt) {
-            ua[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks2 = 0; ks2 < 2; ++ks2) ua[mt] = mfma(load_perm(tm + (mt * 16 + c16) * TS, ks2, G), rb[ks2], ua[mt]);
-        }
-        __syncthreads();   // P complete
-        // (4) O = diag(e^l) Y + P U
-        bf16x8 ub[2] = {pack(ua[0], ua[1]), pack(ua[2], ua[3])};
-#pragma unroll
-        for (int mt = 0; mt < C / 16; ++mt) {
-            f32x4 oa;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) oa[r] = gsh[mt * 16 + G * 4 + r] * ya[mt][r];
-#pragma unroll
-            for (int ks2 = 0; ks2 < 2; ++ks2) oa = mfma(load_perm(pm + (mt * 16 + c16) * TS, ks2, G), ub[ks2], oa);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = mt * 16 + G * 4 + r;
-                if (i < n) A.out[((t0 + i) * A.Hv + h) * DV + dvc] = __builtin_bit_cast(uint16_t, (__bf16)oa[r]);
-            }
-        }
-        // (5) fork points strictly inside this chunk: state after `off` tokens
-        while (e < e_end && A.emit_pos[e] < c * C + n) {
-            const int off = A.emit_pos[e] - c * C;   // 1 .. n-1
-            const float lr = lsh[off - 1];
-            f32x4 u0[C / 16];
+            // R = diag(b) (V - diag(e^l) X);  U = T R
 #pragma unroll
             for (int mt = 0; mt < C / 16; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int j = mt * 16 + G * 4 + r;
-                    u0[mt][r] = j < off ? __expf(lr - lsh[j]) * ua[mt][r] : 0.f;
+                    const int i = mt * 16 + G * 4 + r;
+                    const float vv = bf16_to_f32(B.vs[i * VS + w * 16 + c16]);
+                    xa[mt][r] = B.esh[i] * (vv - B.gsh[i] * xa[mt][r]);
                 }
-            const bf16x8 eb[2] = {pack(u0[0], u0[1]), pack(u0[2], u0[3])};
-            const float gr = __expf(lr);
-            f32x4 tmp[DK / 16];
+            const bf16x8 rb0 = pack(xa[0], xa[1]), rb1 = pack(xa[2], xa[3]);
+            f32x4 ua[C / 16];
+#pragma unroll
+            for (int mt = 0; mt < C / 16; ++mt) {
+                ua[mt] = mfma(load_perm(B.tm + (mt * 16 + c16) * TS, 0, G), rb0, f32x4{0.f, 0.f, 0.f, 0.f});
+                ua[mt] = mfma(load_perm(B.tm + (mt * 16 + c16) * TS, 1, G), rb1, ua[mt]);
+            }
+            // O = diag(e^l) Y + P U.  P = Gamma o Q K^T is built per 16-row tile
+            // as P^T tiles K_j Q_i^T, whose accumulators already have the
+            // layout of the A operand of P U (the permuted reduction index).
+            const bf16x8 ub0 = pack(ua[0], ua[1]), ub1 = pack(ua[2], ua[3]);
+#pragma unroll
+            for (int mt = 0; mt < C / 16; ++mt) {
+                f32x4 pt[4];
+                const float li = B.lsh[mt * 16 + c16];
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) {
+                    pt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (jt > mt) continue;
+#pragma unroll
+                    for (int kk = 0; kk < DK / 32; ++kk)
+                        pt[jt] = mfma(load_row8(B.kr + (jt * 16 + c16) * KS, kk, G),
+                                      load_row8(B.qr + (mt * 16 + c16) * KS, kk, G), pt[jt]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = jt * 16 + G * 4 + r, i = mt * 16 + c16;
+                        pt[jt][r] = j <= i ? __expf(li - B.lsh[j]) * pt[jt][r] : 0.f;
+                    }
+                }
+                f32x4 oa;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) oa[r] = B.gsh[mt * 16 + G * 4 + r] * ya[mt][r];
+                oa = mfma(pack(pt[0], pt[1]), ub0, oa);
+                if (mt >= 2) oa = mfma(pack(pt[2], pt[3]), ub1, oa);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = mt * 16 + G * 4 + r;
+                    if (i < n) A.out[((t0 + i) * A.Hv + h) * DV + dvc] = __builtin_bit_cast(uint16_t, (__bf16)oa[r]);
+                }
+            }
+            // fork points strictly inside this chunk: state after `off` tokens
+            while (e < e_end && A.emit_pos[e] < c * C + n) {
+                const int off = A.emit_pos[e] - c * C;   // 1 .. n-1
+                const float lr = B.lsh[off - 1];
+                f32x4 u0[C / 16];
+#pragma unroll
+                for (int mt = 0; mt < C / 16; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = mt * 16 + G * 4 + r;
+                        u0[mt][r] = j < off ? __expf(lr - B.lsh[j]) * ua[mt][r] : 0.f;
+                    }
+                const bf16x8 eb0 = pack(u0[0], u0[1]), eb1 = pack(u0[2], u0[3]);
+                const float gr = __expf(lr);
+                f32x4 tmp[DK / 16];
+#pragma unroll
+                for (int i = 0; i < DK / 16; ++i) {
+                    tmp[i] = mfma(load_perm(B.kt + (i * 16 + c16) * TS, 0, G), eb0, st[i] * gr);
+                    tmp[i] = mfma(load_perm(B.kt + (i * 16 + c16) * TS, 1, G), eb1, tmp[i]);
+                }
+                store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, tmp);
+                ++e;
+            }
+            // S^T <- e^{l_last} S^T + K^T diag(e^{l_last - l}) U
+            const float ll = B.lsh[C - 1];
+#pragma unroll
+            for (int mt = 0; mt < C / 16; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ua[mt][r] *= __expf(ll - B.lsh[mt * 16 + G * 4 + r]);
+            const bf16x8 wb0 = pack(ua[0], ua[1]), wb1 = pack(ua[2], ua[3]);
+            const float gl = __expf(ll);
 #pragma unroll
             for (int i = 0; i < DK / 16; ++i) {
-                tmp[i] = st[i] * gr;
-#pragma unroll
-                for (int ks2 = 0; ks2 < 2; ++ks2) tmp[i] = mfma(load_perm(kt + (i * 16 + c16) * TS, ks2, G), eb[ks2], tmp[i]);
+                st[i] = mfma(load_perm(B.kt + (i * 16 + c16) * TS, 0, G), wb0, st[i] * gl);
+                st[i] = mfma(load_perm(B.kt + (i * 16 + c16) * TS, 1, G), wb1, st[i]);
             }
-            store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, tmp);
-            ++e;
+            // a fork point at the end of this chunk
+            while (e < e_end && A.emit_pos[e] == c * C + n) {
+                store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, st);
+                ++e;
+            }
         }
-        // (6) S^T <- e^{l_last} S^T + K^T diag(e^{l_last - l}) U
-        const float ll = lsh[C - 1];
-#pragma unroll
-        for (int mt = 0; mt < C / 16; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ua[mt][r] *= __expf(ll - lsh[mt * 16 + G * 4 + r]);
-        const bf16x8 wb[2] = {pack(ua[0], ua[1]), pack(ua[2], ua[3])};
-        const float gl = __expf(ll);
-#pragma unroll
-        for (int i = 0; i < DK / 16; ++i) {
-            st[i] *= gl;
-#pragma unroll
-            for (int ks2 = 0; ks2 < 2; ++ks2) st[i] = mfma(load_perm(kt + (i * 16 + c16) * TS, ks2, G), wb[ks2], st[i]);
-        }
-        // (7) a fork point at the end of this chunk
-        while (e < e_end && A.emit_pos[e] == c * C + n) {
-            store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, st);
-            ++e;
-        }
+        __syncthreads();   // chunk c consumed, chunk c+1 staged
     }
-    const int so = A.seg_state_out[s];
-    if (so >= 0) store_state(A.state_out + ((size_t)so * A.Hv + h) * SZ, dvc, G, st);
+    if (!producer) {
+        const int so = A.seg_state_out[s];
+        if (so >= 0) store_state(A.state_out + ((size_t)so * A.Hv + h) * SZ, dvc, G, st);
+    }
 }
 
 }  // namespace gdnk
@@ -388,8 +457,9 @@ int fk_launch_gdn_bf16_prep(const fk_tree_meta *meta, const void *k, const float
                             const void *ws, hipStream_t st)
 {
     const WsLayout L = ws_layout(*meta, Hv, gdnk::DK, gdnk::DV);
-    dim3 grid((unsigned)L.chunk_cap, (unsigned)Hv);
-    gdnk::k_gdn_prep<<<grid, 64, 0, st>>>((const uint16_t *)k, a, b, Hk, Hv, ws_at<int32_t>(ws, L.header),
+    const int64_t items = L.chunk_cap * Hv;
+    dim3 grid((unsigned)((items + gdnk::PREP_WAVES - 1) / gdnk::PREP_WAVES));
+    gdnk::k_gdn_prep<<<grid, 64 * gdnk::PREP_WAVES, 0, st>>>((const uint16_t *)k, a, b, Hk, Hv, ws_at<int32_t>(ws, L.header),
                                           ws_at<int32_t>(ws, L.chunk_seg), ws_at<int32_t>(ws, L.chunk_row0),
                                           ws_at<int32_t>(ws, L.seg_start), ws_at<int32_t>(ws, L.seg_len),
                                           const_cast<uint16_t *>(ws_at<uint16_t>(ws, L.tmat)));
@@ -425,7 +495,14 @@ int fk_launch_gdn_bf16(const fk_tree_meta *meta, int level, const void *q, const
     A.state_in = state_in;
     A.state_out = state_out;
     A.fork_states = fork_states;
-    dim3 grid((unsigned)meta->level_cap, (unsigned)Hv, (unsigned)(gdnk::DV / gdnk::DVS));
-    gdnk::k_gdn_chunk<<<grid, 256, 0, st>>>(A);
+    dim3 grid((unsigned)((int64_t)meta->level_cap * Hv * (gdnk::DV / gdnk::DVS)));
+    static bool configured = false;
+    const size_t lds = 2 * sizeof(gdnk::ChunkBuf);
+    if (!configured) {
+        FK_HIP(hipFuncSetAttribute((const void *)gdnk::k_gdn_chunk, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)lds));
+        configured = true;
+    }
+    gdnk::k_gdn_chunk<<<grid, gdnk::CHUNK_THREADS, lds, st>>>(A);
     return launch_status();
 }
