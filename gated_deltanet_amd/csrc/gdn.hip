@@ -14,8 +14,8 @@
 
 #include "fk_common.h"
 
-int fk_launch_gdn_bf16_prep(const fk_tree_meta *meta, const void *k, const float *a, const float *b, int Hk, int Hv,
-                            const void *ws, hipStream_t st);
+int fk_launch_gdn_bf16_prep(const fk_tree_meta *meta, const void *q, const void *k, const float *a, const float *b,
+                            int Hk, int Hv, const void *ws, hipStream_t st);
 int fk_launch_gdn_bf16(const fk_tree_meta *meta, int level, const void *q, const void *k, const void *v,
                        const float *a, const float *b, int Hk, int Hv, const float *state_in, float *state_out,
                        void *out, const void *ws, float *fork_states, hipStream_t st);
@@ -163,8 +163,8 @@ extern "C" int gdn_fork_forward(const fk_tree_meta *meta, const void *q, const v
     if (!meta->seg_state_out) return FK_E_INVALID_ARG;
     if (meta->T == 0) return FK_OK;
     if (dtype == FK_BF16) {
-        // per-chunk (I + A)^-1 of every chunk of the round, before any level
-        rc = fk_launch_gdn_bf16_prep(meta, k, a, b, Hk, Hv, ws, st);
+        // per-chunk T = (I + A)^-1 and P of every chunk of the round, before any level
+        rc = fk_launch_gdn_bf16_prep(meta, q, k, a, b, Hk, Hv, ws, st);
         if (rc) return rc;
     }
     for (int level = 0; level < meta->max_depth; ++level) {

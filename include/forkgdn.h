@@ -124,7 +124,7 @@ typedef struct fk_tree_meta {
  * Workspace bytes for a round: derived metadata (segment starts, positions,
  * ancestor chains, attention tiles, GDN chunks, level lists, fork-point
  * routing, status) plus the scratch of one Gated DeltaNet layer: fork_cap
- * fork-point states (Hv * dv * dk floats each) and one bf16 64 x 64 matrix
+ * fork-point states (Hv * dv * dk floats each) and two bf16 64 x 64 matrices
  * per chunk and v-head.  gdn_Hv, gdn_dk, gdn_dv describe the largest GDN
  * layer that will use the workspace (all 0 if none).  `meta` is (host); only
  * its scalar fields are read.

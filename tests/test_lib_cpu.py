@@ -87,8 +87,8 @@ def test_workspace_bytes_grow_with_round():
     L = _lib.load()
     a = L.fk_workspace_bytes(ctypes.byref(m), 0, 0, 0)
     b = L.fk_workspace_bytes(ctypes.byref(m), 2, 32, 32)
-    # one fork-point state plus one 64 x 64 bf16 matrix per chunk and v-head
-    assert b - a >= 2 * 32 * 32 * 4 + (2 + 4) * 2 * 64 * 64 * 2 and a > 0
+    # one fork-point state plus two 64 x 64 bf16 matrices per chunk and v-head
+    assert b - a >= 2 * 32 * 32 * 4 + 2 * (2 + 4) * 2 * 64 * 64 * 2 and a > 0
 
 
 def test_bad_arguments_rejected_on_host():
