@@ -50,26 +50,71 @@ __device__ __forceinline__ uint4 pack8(const float *x)
     return __builtin_bit_cast(uint4, v);
 }
 
-// Stage keys [BN][D] and transposed values [D][BN] of one 64-key block of a
-// range into LDS.  Pages past the range's valid keys are zero-filled, so no
-// page-list entry beyond the range is ever read.
-__device__ __forceinline__ void stage_block(uint16_t *__restrict__ ks, uint16_t *__restrict__ vs,
-                                            const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
-                                            const int32_t *__restrict__ plist, int key0, int count, int g, int Hkv)
+// One 64-key block of a range = 4 pages of 16 keys.  Keys [BN][D] and
+// transposed values [D][BN] of a block are loaded into registers (two 16-byte
+// pieces per page and thread) and later written into one of two LDS buffers.
+// Pages past the range's valid keys are zero, so no page-list entry beyond
+// the range is ever read.
+struct BlockRegs {
+    uint4 k[BN / FK_TILE_TOKENS], v[BN / FK_TILE_TOKENS];
+};
+
+__device__ __forceinline__ void load_block(BlockRegs &R, const uint16_t *__restrict__ kp,
+                                           const uint16_t *__restrict__ vp, const int32_t *__restrict__ plist,
+                                           int key0, int count, int g, int Hkv)
 {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int p = 0; p < BN / FK_TILE_TOKENS; ++p) {
         const int kbase = key0 + p * FK_TILE_TOKENS;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+        R.k[p] = R.v[p] = make_uint4(0, 0, 0, 0);
         if (kbase < count) {
             const size_t pb = ((size_t)plist[kbase / FK_TILE_TOKENS] * Hkv + g) * (FK_TILE_TOKENS * D);
-            kv = *reinterpret_cast<const uint4 *>(kp + pb + tid * 8);   // slot tid/16, dims (tid%16)*8
-            vv = *reinterpret_cast<const uint4 *>(vp + pb + tid * 8);   // dim tid/2, slots (tid%2)*8
+            R.k[p] = *reinterpret_cast<const uint4 *>(kp + pb + tid * 8);   // slot tid/16, dims (tid%16)*8
+            R.v[p] = *reinterpret_cast<const uint4 *>(vp + pb + tid * 8);   // dim tid/2, slots (tid%2)*8
         }
-        *reinterpret_cast<uint4 *>(ks + (p * FK_TILE_TOKENS + tid / 16) * K_STRIDE + (tid % 16) * 8) = kv;
-        *reinterpret_cast<uint4 *>(vs + (tid / 2) * V_STRIDE + p * FK_TILE_TOKENS + (tid % 2) * 8) = vv;
     }
+}
+
+__device__ __forceinline__ void store_block(uint16_t *__restrict__ ks, uint16_t *__restrict__ vs, const BlockRegs &R)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < BN / FK_TILE_TOKENS; ++p) {
+        *reinterpret_cast<uint4 *>(ks + (p * FK_TILE_TOKENS + tid / 16) * K_STRIDE + (tid % 16) * 8) = R.k[p];
+        *reinterpret_cast<uint4 *>(vs + (tid / 2) * V_STRIDE + p * FK_TILE_TOKENS + (tid % 2) * 8) = R.v[p];
+    }
+}
+
+// Walks a tile's key blocks in order: each ancestor's visible prefix, then the
+// own segment; blocks are anchored at the start of every range.
+struct BlockCursor {
+    int lvl, key0, count;
+    bool own;
+    const int32_t *plist;
+};
+
+__device__ __forceinline__ void cursor_level(BlockCursor &c, int lvl, int depth, const int *anc,
+                                             const int32_t *seg_fork, const int32_t *page_off,
+                                             const int32_t *pages, int row0, int len)
+{
+    c.lvl = lvl;
+    c.key0 = 0;
+    c.own = lvl == depth;
+    c.count = c.own ? min(row0 + FK_TILE_TOKENS, len) : seg_fork[anc[lvl + 1]];
+    c.plist = pages + page_off[anc[lvl]];
+}
+
+// move to the next non-empty block; returns false past the last one
+__device__ __forceinline__ bool cursor_next(BlockCursor &c, int depth, const int *anc, const int32_t *seg_fork,
+                                            const int32_t *page_off, const int32_t *pages, int row0, int len)
+{
+    c.key0 += BN;
+    while (c.key0 >= c.count) {
+        if (c.lvl >= depth) return false;
+        cursor_level(c, c.lvl + 1, depth, anc, seg_fork, page_off, pages, row0, len);
+    }
+    return true;
 }
 
 __global__ void __launch_bounds__(THREADS, 2)
@@ -81,8 +126,8 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             const int32_t *__restrict__ seg_fork, const int32_t *__restrict__ page_off,
             const int32_t *__restrict__ pages)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[K_LDS];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[V_LDS];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][K_LDS];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][V_LDS];
     if (header[H_STATUS] != FK_OK) return;
     const int tile = blockIdx.x, g = blockIdx.y;
     if (tile >= header[H_NTILES]) return;
@@ -113,75 +158,96 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     // MFMA row m of a 32-key tile holds key perm(m): bits 2 and 3 swapped
     const int prow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
-    for (int lvl = 0; lvl <= depth; ++lvl) {
-        const int a = anc[lvl];
-        const bool own = lvl == depth;
-        const int count = own ? min(row0 + FK_TILE_TOKENS, len) : seg_fork[anc[lvl + 1]];
-        const int32_t *plist = pages + page_off[a];
-        for (int key0 = 0; key0 < count; key0 += BN) {
-            __syncthreads();   // previous block fully consumed
-            stage_block(k_lds, v_lds, kp, vp, plist, key0, count, g, Hkv);
-            __syncthreads();
-            // S^T = K . Q^T
-            f32x16 sacc[2];
+    BlockCursor cur;
+    cursor_level(cur, 0, depth, anc, seg_fork, page_off, pages, row0, len);
+    while (cur.count == 0) cursor_level(cur, cur.lvl + 1, depth, anc, seg_fork, page_off, pages, row0, len);
+    {
+        BlockRegs R;
+        load_block(R, kp, vp, cur.plist, 0, cur.count, g, Hkv);
+        store_block(k_lds[0], v_lds[0], R);
+    }
+    __syncthreads();
+    for (int buf = 0;; buf ^= 1) {
+        // prefetch the next block into registers while this one is computed
+        BlockCursor nxt = cur;
+        const bool more = cursor_next(nxt, depth, anc, seg_fork, page_off, pages, row0, len);
+        BlockRegs R;
+        if (more) load_block(R, kp, vp, nxt.plist, nxt.key0, nxt.count, g, Hkv);
+        const int key0 = cur.key0, count = cur.count;
+        const bool own = cur.own;
+        const uint16_t *kl = k_lds[buf], *vl = v_lds[buf];
+        // S^T = K . Q^T
+        f32x16 sacc[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                sacc[mt] = f32x16{};
-                const uint16_t *krow = k_lds + (mt * 32 + prow) * K_STRIDE + half * 8;
+        for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = f32x16{};
+            const uint16_t *krow = kl + (mt * 32 + prow) * K_STRIDE + half * 8;
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + ks * 16));
-                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
-                }
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + ks * 16));
+                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
             }
-            // mask: register r of tile mt holds key 32*mt + 16*(r/8) + 8*half + r%8
-            const bool full = own ? (key0 + BN - 1 <= row0) : (key0 + BN <= count);
-            float mloc = -INFINITY;
+        }
+        // mask: register r of tile mt holds key 32*mt + 16*(r/8) + 8*half + r%8.
+        // The row max is taken on raw scores (scale > 0), then one FMA per
+        // score gives the exponent in log2 units.
+        const bool full = own ? (key0 + BN - 1 <= row0) : (key0 + BN <= count);
+        float mloc = -INFINITY;
+        if (full) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[mt][r]);
+        } else {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float x = sacc[mt][r] * scale_log2e;
-                    if (!full) {
-                        const int key = key0 + mt * 32 + (r / 8) * 16 + half * 8 + (r % 8);
-                        const bool vis = own ? key <= tok : key < count;
-                        if (!vis) x = -INFINITY;
-                    }
-                    sacc[mt][r] = x;
-                    mloc = fmaxf(mloc, x);
+                    const int key = key0 + mt * 32 + (r / 8) * 16 + half * 8 + (r % 8);
+                    const bool vis = own ? key <= tok : key < count;
+                    if (!vis) sacc[mt][r] = -INFINITY;
+                    mloc = fmaxf(mloc, sacc[mt][r]);
                 }
-            const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-            const float mnew = fmaxf(m, mrow);
-            const float corr = exp2f(m - mnew);
-            m = mnew;
-            float psum = 0.f;
-            bf16x8 pf[4];
+        }
+        const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * scale_log2e;
+        const float mnew = fmaxf(m, mrow);
+        float psum = 0.f;
+        bf16x8 pf[4];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    float pv[8];
+            for (int hh = 0; hh < 2; ++hh) {
+                float pv[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        pv[e] = exp2f(sacc[mt][hh * 8 + e] - mnew);
-                        psum += pv[e];
-                    }
-                    pf[mt * 2 + hh] = as_bf16x8(pack8(pv));
+                for (int e = 0; e < 8; ++e) {
+                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][hh * 8 + e], scale_log2e, -mnew));
+                    psum += pv[e];
                 }
-            l = l * corr + psum;
+                pf[mt * 2 + hh] = as_bf16x8(pack8(pv));
+            }
+        // rescale only when some row's max moved (a factor of exactly 1 is a no-op)
+        if (__any(mnew != m)) {   // wave-uniform branch
+            const float corr = __builtin_amdgcn_exp2f(m - mnew);
+            l *= corr;
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) o[i] *= corr;
-            // O^T += V^T . P^T ; k-step kk covers keys 16*kk + [0, 16)
+        }
+        l += psum;
+        m = mnew;
+        // O^T += V^T . P^T ; k-step kk covers keys 16*kk + [0, 16)
 #pragma unroll
-            for (int i = 0; i < D / 32; ++i) {
-                const uint16_t *vrow = v_lds + (i * 32 + n) * V_STRIDE + half * 8;
+        for (int i = 0; i < D / 32; ++i) {
+            const uint16_t *vrow = vl + (i * 32 + n) * V_STRIDE + half * 8;
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + kk * 16));
-                    o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[i], 0, 0, 0);
-                }
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + kk * 16));
+                o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[i], 0, 0, 0);
             }
         }
+        if (!more) break;
+        store_block(k_lds[buf ^ 1], v_lds[buf ^ 1], R);
+        cur = nxt;
+        __syncthreads();   // next block staged; this buffer free for reuse
     }
     // epilogue: the row's sum is split over the two halves of the wave
     const float lsum = l + __shfl_xor(l, 32, 64);
