@@ -42,7 +42,45 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests of the workload in the CPU oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain copy of 256 MiB (gdn_checkpoint_save) before timing, so a "
+                         "counter run can scale FETCH_SIZE / WRITE_SIZE to bytes")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_mixture_traffic.txt")
+ATTN_SRC = os.path.join(ROOT, "gated_deltanet_amd", "csrc", "attn_bf16.hip")
+
+
+def kernel_hash(path: str) -> str:
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(config: int):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing, for another workload, or the kernel changed."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        parts = line.split()
+        if len(parts) == 2 and not line.startswith("#"):
+            kv[parts[0]] = parts[1]
+    if kv.get("kernel_sha256_16") != kernel_hash(ATTN_SRC) or kv.get("config") != str(config):
+        return None
+    return float(kv["bytes_per_launch"])
+
+
+def calibrate_copy():
+    """One plain 256 MiB device copy through the checkpoint-save kernel."""
+    import torch
+    import gated_deltanet_amd as fk
+    src = torch.ones((1, 4096, 128, 128), dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src[0])
+    fk.gdn_checkpoint_save(src, 0, dst)
+    torch.cuda.synchronize()
+    return src.numel() * 4
 
 
 def visible_pairs(tree) -> int:
@@ -163,6 +201,8 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.calibrate_copy:
+        calibrate_copy()
     wl = Workload(args.config)
     tree, sh = wl.tree, wl.sh
     for _ in range(args.warmup):
@@ -203,7 +243,8 @@ def main():
                       "fork_attention": attn_ms, "gdn": float(phase[:, 3].mean())},
         "roofline": {"kernel": "fork attention (bf16 MFMA)", "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None, "algorithmic_flops": flops, "visible_pairs_per_head": nvis},
+                     "traffic": measured_traffic(args.config), "algorithmic_flops": flops,
+                     "visible_pairs_per_head": nvis},
     }
     if not wl.gdn_ok:
         line["incomplete"] = "gdn_fork_forward unsupported for this dtype in this build: step lacks GDN"
