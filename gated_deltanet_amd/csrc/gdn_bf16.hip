@@ -214,10 +214,10 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
 // ---------------------------------------------------------------------------
 // Sequential chunk walk of one (segment, v-head, dv slice).
 // Waves 0-3 (consumers) own the state and run the state-dependent products
-// of chunk c; waves 4-5 (producers) meanwhile stage chunk c+1 into the other
+// of chunk c; waves 4-7 (producers) meanwhile stage chunk c+1 into the other
 // LDS buffer -- key rows and their transpose, query rows, T, P, the dv slice
-// of the values, decay vectors -- each producer one half of the columns,
-// with every global load of its half in flight at once.  Consumers leave
+// of the values, decay vectors -- each producer 16 token rows, with every
+// global load of its rows in flight at once.  Consumers leave
 // O in the value buffer; producers store it to HBM with 16-byte writes.
 // ---------------------------------------------------------------------------
 struct ChunkArgs {
@@ -233,7 +233,7 @@ struct ChunkArgs {
 };
 
 constexpr int CONSUMERS = DVS / 16;           // 4 waves, 16 dv columns each
-constexpr int PRODUCERS = 2;
+constexpr int PRODUCERS = 4;
 constexpr int CHUNK_THREADS = (CONSUMERS + PRODUCERS) * 64;
 constexpr int VS = DVS + 8;                   // LDS stride (bf16) of the value / output slice
 
@@ -258,7 +258,7 @@ __device__ __forceinline__ void store_state(float *base, int dvc, int G, const f
         *reinterpret_cast<f32x4 *>(base + (size_t)dvc * DK + i * 16 + G * 4) = st[i];
 }
 
-// producer `part`: store token rows [32 part, +32) of the output slice of
+// producer `part`: store token rows [16 part, +16) of the output slice of
 // chunk `c` (left in B.vs by the consumers), 8 lanes x 16 B per row
 __device__ __forceinline__ void flush_out(const ChunkBuf &B, const ChunkArgs &A, int s, int c, int h, int lane,
                                           int part, int dv0)
@@ -266,7 +266,7 @@ __device__ __forceinline__ void flush_out(const ChunkBuf &B, const ChunkArgs &A,
     const int n = min(C, A.seg_len[s] - c * C);
     const size_t t0 = (size_t)A.seg_start[s] + (size_t)c * C;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
         const int idx = j * 64 + lane, row = part * (C / PRODUCERS) + (idx >> 3), c8 = idx & 7;
         if (row < n)
             *reinterpret_cast<uint4 *>(A.out + ((t0 + row) * A.Hv + h) * DV + dv0 + c8 * 8) =
@@ -289,7 +289,7 @@ __device__ __forceinline__ bf16x8 load_kt(const uint16_t *kt, int d, int ks, int
     return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// producer `part` stages token rows [32 part, 32 part + 32) of chunk `c`
+// producer `part` stages token rows [16 part, 16 part + 16) of chunk `c`
 // into `B`.  Loads are coalesced (consecutive lanes read consecutive 16 B of
 // a row), and all of them are issued before the first LDS write.
 __device__ __forceinline__ void stage_chunk(ChunkBuf &B, const ChunkArgs &A, int s, int c, int h, int g, int lane,
@@ -310,59 +310,44 @@ __device__ __forceinline__ void stage_chunk(ChunkBuf &B, const ChunkArgs &A, int
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(A.tmat + mat, (size_t)C * C * 2);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(A.pmat + mat, (size_t)C * C * 2);
     const int kq_row = A.Hk * DK * 2, v_row = A.Hv * DV * 2;   // bytes between tokens
-    // batch 1 (keys, queries, T): one round trip with all loads in flight
-    {
-        uint4 kv[8], qv[8], tv[4];
+    uint4 kv[4], qv[4], tv[2], pv[2], vv[2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {           // 4 rows x 16 lanes per instruction
-            const int idx = j * 64 + lane, row = rb + (idx >> 4), c8 = idx & 15;
-            kv[j] = buf_load(rk, row * kq_row + c8 * 16);
-            qv[j] = buf_load(rq, row * kq_row + c8 * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {           // 8 rows x 8 lanes per instruction
-            const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
-            tv[j] = buf_load(rt, row * C * 2 + c8 * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int idx = j * 64 + lane, row = rb + (idx >> 4), c8 = idx & 15;
-            if (row >= n) kv[j] = qv[j] = make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(B.kr + row * KS + c8 * 8) = kv[j];
-            *reinterpret_cast<uint4 *>(B.qr + row * KS + c8 * 8) = qv[j];
-            const uint16_t *k8 = reinterpret_cast<const uint16_t *>(&kv[j]);
-            const int col = row ^ kt_swz(c8 * 8);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) B.kt[(c8 * 8 + x) * KTS + col] = k8[x];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
-            *reinterpret_cast<uint4 *>(B.tm + row * TS + c8 * 8) = tv[j];
-        }
+    for (int j = 0; j < 4; ++j) {               // 4 rows x 16 lanes per instruction
+        const int idx = j * 64 + lane, row = rb + (idx >> 4), c8 = idx & 15;
+        kv[j] = buf_load(rk, row * kq_row + c8 * 16);
+        qv[j] = buf_load(rq, row * kq_row + c8 * 16);
     }
-    // batch 2 (P, the value slice, decays)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {               // 8 rows x 8 lanes per instruction
+        const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
+        tv[j] = buf_load(rt, row * C * 2 + c8 * 16);
+        pv[j] = buf_load(rp, row * C * 2 + c8 * 16);
+        vv[j] = buf_load(rv, row * v_row + c8 * 16);
+    }
     float a_raw = 1.f, b_raw = 0.f;
-    {
-        uint4 pv[4], vv[4];
+    if (part == 0) {
+        const int rr = lane < n ? lane : n - 1;
+        a_raw = A.a[(t0 + rr) * A.Hv + h];
+        b_raw = A.b[(t0 + rr) * A.Hv + h];
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
-            pv[j] = buf_load(rp, row * C * 2 + c8 * 16);
-            vv[j] = buf_load(rv, row * v_row + c8 * 16);
-        }
-        if (part == 0) {
-            const int rr = lane < n ? lane : n - 1;
-            a_raw = A.a[(t0 + rr) * A.Hv + h];
-            b_raw = A.b[(t0 + rr) * A.Hv + h];
-        }
+    for (int j = 0; j < 4; ++j) {
+        const int idx = j * 64 + lane, row = rb + (idx >> 4), c8 = idx & 15;
+        if (row >= n) kv[j] = qv[j] = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(B.kr + row * KS + c8 * 8) = kv[j];
+        *reinterpret_cast<uint4 *>(B.qr + row * KS + c8 * 8) = qv[j];
+        const uint16_t *k8 = reinterpret_cast<const uint16_t *>(&kv[j]);
+        const int col = row ^ kt_swz(c8 * 8);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
-            if (row >= n) vv[j] = make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(B.pm + row * TS + c8 * 8) = pv[j];
-            *reinterpret_cast<uint4 *>(B.vs + row * VS + c8 * 8) = vv[j];
-        }
+        for (int x = 0; x < 8; ++x) B.kt[(c8 * 8 + x) * KTS + col] = k8[x];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
+        if (row >= n) vv[j] = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(B.tm + row * TS + c8 * 8) = tv[j];
+        *reinterpret_cast<uint4 *>(B.pm + row * TS + c8 * 8) = pv[j];
+        *reinterpret_cast<uint4 *>(B.vs + row * VS + c8 * 8) = vv[j];
     }
     if (part == 0) {
         const bool live = lane < n;
