@@ -66,8 +66,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kv_append.argtypes = [mp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     L.fork_attn_forward.argtypes = [mp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
     L.gdn_fork_forward.argtypes = [mp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
-    L.gdn_checkpoint_save.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp]
-    L.gdn_checkpoint_resume.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp]
+    L.gdn_checkpoint_save.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp]
+    L.gdn_checkpoint_resume.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp]
     L.fk_read_status.argtypes = [vp, vp, _i32p]
     L.fk_strerror.argtypes = [ctypes.c_int]
     L.fk_strerror.restype = ctypes.c_char_p

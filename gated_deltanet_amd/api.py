@@ -176,16 +176,20 @@ def gdn_fork_forward(meta: TreeMeta, q, k, v, a, b, ws, state_in=None, state_out
     return out
 
 
-def gdn_checkpoint_save(state_out, slot, ckpt, stream=None):
+def gdn_checkpoint_save(state_out, slot, ckpt, count=1, stream=None):
+    """Copy state_out[slot:slot+count] into ckpt ([count, Hv, dv, dk] or [Hv, dv, dk])."""
     n, Hv, dv, dk = state_out.shape
+    assert ckpt.numel() == count * Hv * dv * dk
     check("gdn_checkpoint_save", _lib.load().gdn_checkpoint_save(
-        _ptr(state_out), int(slot), n, Hv, dk, dv, _ptr(ckpt), _stream(stream)))
+        _ptr(state_out), int(slot), int(count), n, Hv, dk, dv, _ptr(ckpt), _stream(stream)))
 
 
-def gdn_checkpoint_resume(ckpt, state_in, slot, stream=None):
+def gdn_checkpoint_resume(ckpt, state_in, slot, count=1, stream=None):
+    """Copy saved states ckpt into state_in[slot:slot+count]."""
     n, Hv, dv, dk = state_in.shape
+    assert ckpt.numel() == count * Hv * dv * dk
     check("gdn_checkpoint_resume", _lib.load().gdn_checkpoint_resume(
-        _ptr(ckpt), _ptr(state_in), int(slot), n, Hv, dk, dv, _stream(stream)))
+        _ptr(ckpt), _ptr(state_in), int(slot), int(count), n, Hv, dk, dv, _stream(stream)))
 
 
 def fk_read_status(ws, stream=None) -> int:

@@ -28,27 +28,28 @@ int copy_state(const float *src, float *dst, size_t elems, hipStream_t st)
 
 using namespace fk;
 
-static int check_ckpt(const float *a, const float *b, int32_t slot, int32_t n_slots, int32_t Hv, int32_t dk,
-                      int32_t dv)
+static int check_ckpt(const float *a, const float *b, int32_t slot, int32_t count, int32_t n_slots, int32_t Hv,
+                      int32_t dk, int32_t dv)
 {
-    if (!a || !b || slot < 0 || slot >= n_slots || Hv < 1 || dk < 1 || dv < 1) return FK_E_INVALID_ARG;
+    if (!a || !b || slot < 0 || count < 1 || (int64_t)slot + count > n_slots || Hv < 1 || dk < 1 || dv < 1)
+        return FK_E_INVALID_ARG;
     return FK_OK;
 }
 
-extern "C" int gdn_checkpoint_save(const float *state_out, int32_t slot, int32_t n_slots, int32_t Hv, int32_t dk,
-                                   int32_t dv, float *ckpt, fk_stream_t stream)
+extern "C" int gdn_checkpoint_save(const float *state_out, int32_t slot, int32_t count, int32_t n_slots, int32_t Hv,
+                                   int32_t dk, int32_t dv, float *ckpt, fk_stream_t stream)
 {
-    int rc = check_ckpt(state_out, ckpt, slot, n_slots, Hv, dk, dv);
+    int rc = check_ckpt(state_out, ckpt, slot, count, n_slots, Hv, dk, dv);
     if (rc) return rc;
     const size_t elems = (size_t)Hv * dk * dv;
-    return copy_state(state_out + (size_t)slot * elems, ckpt, elems, (hipStream_t)stream);
+    return copy_state(state_out + (size_t)slot * elems, ckpt, elems * count, (hipStream_t)stream);
 }
 
-extern "C" int gdn_checkpoint_resume(const float *ckpt, float *state_in, int32_t slot, int32_t n_slots, int32_t Hv,
-                                     int32_t dk, int32_t dv, fk_stream_t stream)
+extern "C" int gdn_checkpoint_resume(const float *ckpt, float *state_in, int32_t slot, int32_t count, int32_t n_slots,
+                                     int32_t Hv, int32_t dk, int32_t dv, fk_stream_t stream)
 {
-    int rc = check_ckpt(ckpt, state_in, slot, n_slots, Hv, dk, dv);
+    int rc = check_ckpt(ckpt, state_in, slot, count, n_slots, Hv, dk, dv);
     if (rc) return rc;
     const size_t elems = (size_t)Hv * dk * dv;
-    return copy_state(ckpt, state_in + (size_t)slot * elems, elems, (hipStream_t)stream);
+    return copy_state(ckpt, state_in + (size_t)slot * elems, elems * count, (hipStream_t)stream);
 }

@@ -215,20 +215,22 @@ int gdn_fork_forward(const fk_tree_meta *meta, const void *q, const void *k, con
                      fk_stream_t stream);
 
 /*
- * gdn_checkpoint_save -- copy the float32 recurrent state in
- * state_out[slot] ([Hv, dv, dk]) into caller storage `ckpt` (Flide section
- * 3.4: a checkpoint keeps the float32 state; the K/V before the checkpoint
- * stay in their pages, which the caller retains by id).
+ * gdn_checkpoint_save -- copy the float32 recurrent states of `count`
+ * consecutive slots state_out[slot .. slot+count) ([count, Hv, dv, dk])
+ * into caller storage `ckpt` (Flide section 3.4: a checkpoint keeps the
+ * float32 state; the keys/values before the checkpoint stay in their pages,
+ * which the caller retains by id).  n_slots: slots in state_out.
  */
-int gdn_checkpoint_save(const float *state_out, int32_t slot, int32_t n_slots, int32_t Hv,
+int gdn_checkpoint_save(const float *state_out, int32_t slot, int32_t count, int32_t n_slots, int32_t Hv,
                         int32_t dk, int32_t dv, float *ckpt, fk_stream_t stream);
 
 /*
- * gdn_checkpoint_resume -- copy a saved state `ckpt` ([Hv, dv, dk] float)
- * into state_in[slot], so that a cached segment of a later round continues
- * exactly where the saved pass stopped (Flide section 3.4).
+ * gdn_checkpoint_resume -- copy `count` saved states `ckpt` ([count, Hv, dv,
+ * dk] float) into state_in[slot .. slot+count), so that cached segments of a
+ * later round continue exactly where the saved pass stopped (Flide section
+ * 3.4).  n_slots: slots in state_in.
  */
-int gdn_checkpoint_resume(const float *ckpt, float *state_in, int32_t slot, int32_t n_slots,
+int gdn_checkpoint_resume(const float *ckpt, float *state_in, int32_t slot, int32_t count, int32_t n_slots,
                           int32_t Hv, int32_t dk, int32_t dv, fk_stream_t stream);
 
 /*

@@ -94,8 +94,10 @@ def test_workspace_bytes_grow_with_round():
 def test_bad_arguments_rejected_on_host():
     L = _lib.load()
     assert L.fk_tree_build(None, None, 0, None) == -1
-    assert L.gdn_checkpoint_save(ctypes.c_void_p(16), 3, 2, 1, 16, 16, ctypes.c_void_p(16), None) == -1
-    assert L.gdn_checkpoint_resume(None, ctypes.c_void_p(16), 0, 1, 1, 16, 16, None) == -1
+    assert L.gdn_checkpoint_save(ctypes.c_void_p(16), 3, 1, 2, 1, 16, 16, ctypes.c_void_p(16), None) == -1
+    assert L.gdn_checkpoint_save(ctypes.c_void_p(16), 1, 2, 2, 1, 16, 16, ctypes.c_void_p(16), None) == -1
+    assert L.gdn_checkpoint_resume(None, ctypes.c_void_p(16), 0, 1, 1, 1, 16, 16, None) == -1
+    assert L.gdn_checkpoint_resume(ctypes.c_void_p(16), ctypes.c_void_p(16), 0, 0, 1, 1, 16, 16, None) == -1
     m = _lib.TreeMetaC()
     m.T, m.S, m.max_depth, m.level_cap, m.fork_cap, m.page_size = 0, 1, 1, 1, 0, 16
     assert L.gdn_fork_forward(ctypes.byref(m), None, None, None, None, None, 0, 1, 1, 48, 48, None,
