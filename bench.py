@@ -113,8 +113,7 @@ class Workload:
 
         self.torch, self.fk = torch, fk
         cfg, tree = make_config(index)
-        if any(s.cached for s in tree.segs):
-            raise SystemExit("the resume workload needs its history pass; not wired into the bench yet")
+        assert not any(s.cached for s in tree.segs), "the resume workload uses ResumeWorkload"
         self.cfg, self.tree = cfg, tree
         inp = draw_inputs(tree, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
         sh = cfg.shapes
@@ -168,6 +167,131 @@ class Workload:
             ev[4].record()
 
 
+class ResumeWorkload:
+    """The expanding-history workload: every request resumes from a checkpoint
+    -- the fp32 GDN state and the 16,384-token paged K/V of its history, made
+    by an untimed GPU pass over that history -- appends 1,024 new tokens and
+    forks a mixed tree of 32-token branches.  A step resumes the saved
+    states, runs the round, and saves the new roots' states for the next step.
+
+    Inputs are drawn on the GPU (seeded); ``sampled`` requests instead use the
+    host generator's values so an oracle can check them.
+    """
+
+    def __init__(self, device="cuda", sampled=()):
+        import torch
+
+        import gated_deltanet_amd as fk
+        from workloads import make_config
+        from workloads.device import draw_stream
+        from workloads.tensors import SeedTree, draw_segment
+
+        self.torch, self.fk = torch, fk
+        cfg, tree = make_config(4)
+        self.cfg, self.tree, self.sh = cfg, tree, cfg.shapes
+        sh = cfg.shapes
+        hist = [i for i, sg in enumerate(tree.segs) if sg.cached]
+        self.hist = hist
+        R, H = len(hist), tree.segs[hist[0]].length
+        self.R, self.H = R, H
+        # pass 1: every history as a live root, laid out request by request
+        self.hx = draw_stream(R * H, sh, cfg.seed * 7 + 1, cfg.mu_a, device,
+                              names=("ak", "av", "gq", "gk", "gv", "ga", "gb"))
+        # the round: live stream in tree order
+        self.x = draw_stream(tree.T, sh, cfg.seed * 7 + 2, cfg.mu_a, device)
+        starts, acc = {}, 0
+        for sid in tree.order:
+            starts[sid] = acc
+            acc += tree.segs[sid].length
+        self.starts = starts
+        seeds = SeedTree(cfg.seed)
+
+        def put(dst, t0, vals):
+            for name, arr in vals.items():
+                if name not in dst:
+                    continue
+                t = torch.from_numpy(np.ascontiguousarray(arr))
+                if arr.dtype == np.uint16:
+                    t = t.view(torch.bfloat16)
+                dst[name][t0:t0 + len(arr)] = t.to(device)
+
+        for r in sampled:
+            for sid, sg in enumerate(tree.segs):
+                if sg.request != r:
+                    continue
+                vals = draw_segment(seeds, r, sg.key, sg.length, sh, cfg.mu_a, "bf16")
+                if sg.cached:
+                    put(self.hx, hist.index(sid) * H, vals)
+                else:
+                    put(self.x, starts[sid], vals)
+        n_hist_pages = R * H // 16
+        n_pages = n_hist_pages + sum(-(-sg.length // 16) for sg in tree.segs if not sg.cached)
+        ts, par, fkk, cl = tree.arrays()
+        ssi = np.full(tree.S, -1, np.int32)
+        sso = np.full(tree.S, -1, np.int32)
+        cached_pages = {}
+        for r, sid in enumerate(hist):
+            ssi[sid] = r
+            cached_pages[sid] = np.arange(r * (H // 16), (r + 1) * (H // 16))
+            (root,) = tree.children(sid)
+            sso[root] = r
+        self.plan = fk.plan_round(ts, par, fkk, cl, cached_pages=cached_pages, first_page=n_hist_pages,
+                                  n_pages=n_pages, seg_state_in=ssi, seg_state_out=sso, n_state_in=R,
+                                  n_state_out=R, device=device)
+        assert n_hist_pages + self.plan.pages_used == n_pages
+        self.meta = self.plan.meta
+        self.hplan = fk.plan_round(np.repeat(np.arange(R, dtype=np.int32), H), np.full(R, -1), np.zeros(R),
+                                   np.zeros(R), first_page=0, n_pages=n_pages,
+                                   seg_state_out=np.arange(R, dtype=np.int32), n_state_out=R, device=device)
+        dt = torch.bfloat16
+        self.k_pool = torch.zeros((n_pages, sh.Hkv, 16, sh.d), dtype=dt, device=device)
+        self.v_pool = torch.zeros((n_pages, sh.Hkv, sh.d, 16), dtype=dt, device=device)
+        st = (R, sh.Hv, sh.dv, sh.dk)
+        self.state_in = torch.zeros(st, dtype=torch.float32, device=device)
+        self.state_out = torch.zeros(st, dtype=torch.float32, device=device)
+        self.ckpt = torch.zeros(st, dtype=torch.float32, device=device)
+        self.ckpt_next = torch.zeros(st, dtype=torch.float32, device=device)
+        self.attn_out = torch.empty_like(self.x["aq"])
+        self.gdn_out = torch.empty_like(self.x["gv"])
+        self.scale = sh.d ** -0.5
+        self.ws = fk.alloc_workspace(self.meta, sh.Hv, sh.dk, sh.dv, device=device)
+
+    def checkpoint(self):
+        """Untimed pass 1: page the histories' K/V, run GDN over them, save."""
+        fk, torch, sh = self.fk, self.torch, self.sh
+        hws = fk.alloc_workspace(self.hplan.meta, sh.Hv, sh.dk, sh.dv)
+        fk.fk_tree_build(self.hplan.meta, hws)
+        fk.kv_append(self.hplan.meta, self.hx["ak"], self.hx["av"], self.k_pool, self.v_pool, hws)
+        hst = torch.empty((self.R, sh.Hv, sh.dv, sh.dk), dtype=torch.float32, device="cuda")
+        fk.gdn_fork_forward(self.hplan.meta, self.hx["gq"], self.hx["gk"], self.hx["gv"], self.hx["ga"],
+                            self.hx["gb"], hws, state_out=hst)
+        assert fk.fk_read_status(hws) == 0
+        fk.gdn_checkpoint_save(hst, 0, self.ckpt, count=self.R)
+        torch.cuda.synchronize()
+        del hws, hst
+
+    def step(self, ev=None):
+        fk, x = self.fk, self.x
+        if ev:
+            ev[0].record()
+        fk.gdn_checkpoint_resume(self.ckpt, self.state_in, 0, count=self.R)
+        fk.fk_tree_build(self.meta, self.ws)
+        if ev:
+            ev[1].record()
+        fk.kv_append(self.meta, x["ak"], x["av"], self.k_pool, self.v_pool, self.ws)
+        if ev:
+            ev[2].record()
+        fk.fork_attn_forward(self.meta, x["aq"], None, None, self.k_pool, self.v_pool, self.ws,
+                             scale=self.scale, out=self.attn_out)
+        if ev:
+            ev[3].record()
+        fk.gdn_fork_forward(self.meta, x["gq"], x["gk"], x["gv"], x["ga"], x["gb"], self.ws,
+                            state_in=self.state_in, state_out=self.state_out, out=self.gdn_out)
+        fk.gdn_checkpoint_save(self.state_out, 0, self.ckpt_next, count=self.R)
+        if ev:
+            ev[4].record()
+
+
 def cpu_baseline(index: int, n_req: int):
     """The fp64 oracle, as it stands, on the first ``n_req`` requests of the
     same workload: every root-to-leaf path as its own isolated sequence
@@ -176,6 +300,8 @@ def cpu_baseline(index: int, n_req: int):
     from workloads import make_config
     from workloads.tensors import draw_inputs
 
+    if index == 4:
+        return cpu_baseline_resume(n_req)
     cfg, tree = make_config(index, n_requests=n_req)
     inp = draw_inputs(tree, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
     ts, par, fkk, cl = tree.arrays()
@@ -193,6 +319,51 @@ def cpu_baseline(index: int, n_req: int):
                       f"attention + GDN, {dt:.1f} s"}
 
 
+def cpu_baseline_resume(n_req: int):
+    """The oracle on the first ``n_req`` requests of the resume workload.  The
+    history states are made first (untimed, like the GPU's checkpoint pass);
+    the timed part is the round: tree-mode attention over history + live
+    tokens and GDN resumed from the saved states (literal per-path mode would
+    re-read each 16,384-token history once per leaf), on a quarter of the
+    heads, scaled to the whole request."""
+    import oracle
+    from workloads import make_config
+    from workloads.tensors import draw_inputs
+
+    cfg, tree = make_config(4, n_requests=n_req)
+    inp = draw_inputs(tree, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
+    ts, par, fkk, cl = tree.arrays()
+    hist = [i for i, sg in enumerate(tree.segs) if sg.cached]
+    ssi = np.full(tree.S, -1, np.int32)
+    for r, sid in enumerate(hist):
+        ssi[sid] = r
+    n_h = [tree.segs[i].length for i in hist]
+    h_ts = np.repeat(np.arange(len(hist), dtype=np.int32), n_h)
+    z = np.zeros(len(hist), np.int32)
+    _, st, _ = oracle.gdn(h_ts, z - 1, z, z, inp.f64("gq", True), inp.f64("gk", True), inp.f64("gv", True),
+                          inp.f64("ga", True), inp.f64("gb", True), seg_state_out=np.arange(len(hist)),
+                          n_state_out=len(hist), mode=1)
+    args = {n: inp.f64(n) for n in inp.raw}
+    sh = cfg.shapes
+    # a quarter of the heads: the first kv group's q heads, the first quarter of the v heads
+    frac = 4
+    a_sel = (np.arange(sh.Hq) < sh.Hq // frac).astype(np.uint8)
+    g_sel = (np.arange(sh.Hv) < sh.Hv // frac).astype(np.uint8)
+    t0 = time.perf_counter()
+    oracle.attention(ts, par, fkk, cl, inp.hist_off, args["aq"], args["ak"], args["av"], inp.f64("ak", True),
+                     inp.f64("av", True), sh.d ** -0.5, mode=1, head_sel=a_sel)
+    oracle.gdn(ts, par, fkk, cl, args["gq"], args["gk"], args["gv"], args["ga"], args["gb"], state_in=st,
+               seg_state_in=ssi, mode=1, head_sel=g_sel)
+    dt = (time.perf_counter() - t0) * frac
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    bt = tree.branch_tokens()
+    return {"value": bt / dt, "unit": "branch tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_req} request(s) of the workload ({tree.T} stream tokens after "
+                      f"{sum(n_h)} history tokens, {bt} branch tokens), 1/{frac} of the attention and "
+                      f"GDN heads timed and scaled by {frac}: fp64 tree-mode attention + GDN resumed "
+                      f"from oracle-made history states, {dt / frac:.1f} s measured"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -203,7 +374,11 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
-    wl = Workload(args.config)
+    if args.config == 4:
+        wl = ResumeWorkload()
+        wl.checkpoint()
+    else:
+        wl = Workload(args.config)
     tree, sh = wl.tree, wl.sh
     for _ in range(args.warmup):
         wl.step()
@@ -239,18 +414,21 @@ def main():
         "config": {"workload": wl.cfg.name, "index": args.config, "requests": tree.n_requests,
                    "stream_tokens": tree.T, "branch_tokens": bt, "segments": tree.S,
                    "attn_heads": [sh.Hq, sh.Hkv, sh.d], "gdn_heads": [sh.Hk, sh.Hv, sh.dk, sh.dv]},
-        "phases_ms": {"tree_build": float(phase[:, 0].mean()), "kv_append": float(phase[:, 1].mean()),
-                      "fork_attention": attn_ms, "gdn": float(phase[:, 3].mean())},
+        "phases_ms": {("resume+tree_build" if args.config == 4 else "tree_build"): float(phase[:, 0].mean()),
+                      "kv_append": float(phase[:, 1].mean()),
+                      "fork_attention": attn_ms,
+                      ("gdn+checkpoint_save" if args.config == 4 else "gdn"): float(phase[:, 3].mean())},
         "roofline": {"kernel": "fork attention (bf16 MFMA)", "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(args.config), "algorithmic_flops": flops,
                      "visible_pairs_per_head": nvis},
     }
-    if not wl.gdn_ok:
+    if not getattr(wl, "gdn_ok", True):
         line["incomplete"] = "gdn_fork_forward unsupported for this dtype in this build: step lacks GDN"
         line["phases_ms"]["gdn"] = None
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_requests)
+        n_cpu = args.cpu_requests if args.config != 4 else min(args.cpu_requests, 1)
+        line["cpu_baseline"] = cpu_baseline(args.config, n_cpu)
     print(json.dumps(line))
 
 
