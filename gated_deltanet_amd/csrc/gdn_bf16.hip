@@ -16,9 +16,9 @@
 // k_gdn_prep  (all chunks of the round at once, before the level launches):
 //             T of every (chunk, v-head) in fp32 by forward substitution,
 //             stored as bf16.  It depends only on k, a, b -- never on a state.
-// k_gdn_chunk (one launch per tree level): one work-group per (segment,
-//             v-head, 64-wide dv slice) walks the segment's chunks in order.
-//             Each wave keeps its 128 x 16 slice of S^T in fp32 MFMA
+// k_gdn_chunk (one launch per tree level, persistent work-groups): each
+//             item (segment, v-head, 64-wide dv slice) walks its chunks in
+//             order.  Each wave keeps its 128 x 16 slice of S^T in fp32 MFMA
 //             accumulator registers for the whole segment and feeds it
 //             straight back as an MFMA operand (a fixed permutation of the
 //             reduction index makes the accumulator layout the operand
@@ -41,7 +41,6 @@ constexpr int DK = 128, DV = 128;
 constexpr int DVS = 64;           // dv columns of one work-group (4 waves x 16)
 constexpr int KS = DK + 8;        // LDS stride (bf16) of key/query rows
 constexpr int TS = C + 8;         // LDS stride (bf16) of 64-wide rows written 16 B at a time (T, P)
-constexpr int KTS = C + 4;        // LDS stride (bf16) of the transposed keys (written 2 B at a time)
 constexpr int AS = C + 4;         // LDS stride (fp32) of the prep matrix
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -62,14 +61,21 @@ __device__ __forceinline__ bf16x8 pack(f32x4 lo, f32x4 hi)
     return v;
 }
 
-// Operand with a permuted reduction index: for a k-step over 32 positions,
+// Operands with a permuted reduction index: for a k-step over 32 positions,
 // lane group G = lane/16 supplies positions 4G..4G+3 and 16+4G..16+4G+3 --
-// exactly the rows a 16x16 accumulator pair holds in that lane group.
+// exactly the rows a 16x16 accumulator pair holds in that lane group.  Rows
+// that serve as such operands are stored with each 32-position block
+// reordered so that those eight positions are contiguous: the group of four
+// positions q (0..7) of a block sits at element perm4(q) of the block.
+// One 16-byte LDS read then gives a lane its operand.
+__device__ __forceinline__ int perm4(int q) { return 8 * (q & 3) + 4 * (q >> 2); }
+
+// element offset, within a row, of the group of four positions starting at p (p % 4 == 0)
+__device__ __forceinline__ int perm_off(int p) { return (p & ~31) + perm4((p >> 2) & 7); }
+
 __device__ __forceinline__ bf16x8 load_perm(const uint16_t *row, int ks, int G)
 {
-    const uint2 lo = *reinterpret_cast<const uint2 *>(row + ks * 32 + 4 * G);
-    const uint2 hi = *reinterpret_cast<const uint2 *>(row + ks * 32 + 16 + 4 * G);
-    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    return as_bf16x8(*reinterpret_cast<const uint4 *>(row + ks * 32 + 8 * G));
 }
 
 // raw buffer resource (gfx9 data format dword) over `bytes` bytes at `p`
@@ -166,7 +172,8 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
             __bf16 p4[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) p4[r] = (__bf16)acc[r];
-            if (valid) *reinterpret_cast<uint2 *>(pdst + i * C + jt * 16 + G * 4) = __builtin_bit_cast(uint2, p4);
+            if (valid)
+                *reinterpret_cast<uint2 *>(pdst + i * C + perm_off(jt * 16 + G * 4)) = __builtin_bit_cast(uint2, p4);
         }
     }
     // A = strictly lower part of diag(b) (Gamma o K K^T)
@@ -201,24 +208,33 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     for (int i = 0; i < C; ++i) am[i * AS + lane] = x[i];
     __syncthreads();
     if (!valid) return;
+    // row `lane` of T, stored permuted (both T and P serve as A operands)
     uint16_t *dst = tmat + (((size_t)c * Hv + h) * C + lane) * C;
 #pragma unroll
     for (int j8 = 0; j8 < C / 8; ++j8) {
         bf16x8 v;
+        // stored elements [8 j8, 8 j8 + 8): positions 4G'..4G'+3 and
+        // 16+4G'..16+4G'+3 of block j8/4, G' = j8 % 4
+        const int base = (j8 >> 2) * 32 + 4 * (j8 & 3);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)am[lane * AS + j8 * 8 + e];
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)am[lane * AS + base + (e < 4 ? e : 12 + e)];
         *reinterpret_cast<uint4 *>(dst + j8 * 8) = __builtin_bit_cast(uint4, v);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Sequential chunk walk of one (segment, v-head, dv slice).
-// Waves 0-3 (consumers) own the state and run the state-dependent products
-// of chunk c; waves 4-7 (producers) meanwhile stage chunk c+1 into the other
-// LDS buffer -- key rows and their transpose, query rows, T, P, the dv slice
-// of the values, decay vectors -- each producer 16 token rows, with every
-// global load of its rows in flight at once.  Consumers leave
-// O in the value buffer; producers store it to HBM with 16-byte writes.
+// Chunk walk of one tree level, persistent: work-group b runs the items
+// b, b + G, b + 2G, ... (G = grid size), item = (segment, v-head, 64-wide dv
+// slice), and within an item its chunks in order -- one flat sequence of
+// steps.  Waves 0-3 (consumers) own the state slice and run the
+// state-dependent products of step j; waves 4-7 (producers) meanwhile write
+// step j+1 (already in their registers) into the other LDS buffer, issue the
+// global loads of step j+2, and store the output of step j-1 that the
+// consumers left in the value buffer.  When a step starts an item, the
+// producers have staged that item's entering state (zero, state_in, or the
+// parent's fork-point state) in LDS, so no wave waits on HBM at an item
+// boundary.  The assignment of items to work-groups never changes an item's
+// arithmetic.
 // ---------------------------------------------------------------------------
 struct ChunkArgs {
     const uint16_t *q, *k, *v;
@@ -236,11 +252,12 @@ constexpr int CONSUMERS = DVS / 16;           // 4 waves, 16 dv columns each
 constexpr int PRODUCERS = 4;
 constexpr int CHUNK_THREADS = (CONSUMERS + PRODUCERS) * 64;
 constexpr int VS = DVS + 8;                   // LDS stride (bf16) of the value / output slice
+constexpr int S0S = DK + 4;                   // LDS stride (fp32) of the staged entering state
+constexpr int NSL = DV / DVS;                 // dv slices per v-head
 
 struct ChunkBuf {
     uint16_t kr[C * KS];     // key rows
     uint16_t qr[C * KS];     // query rows
-    uint16_t kt[DK * KTS];   // keys transposed
     uint16_t tm[C * TS];     // T = (I + A)^-1
     uint16_t pm[C * TS];     // P = Gamma o Q K^T
     uint16_t vs[C * VS];     // values of this dv slice, then the chunk's output
@@ -249,6 +266,68 @@ struct ChunkBuf {
     float gsh[C];            // e^{l_i}
     float dsh[C];            // e^{l_last - l_i}
 };
+
+constexpr size_t CHUNK_LDS = 2 * sizeof(ChunkBuf) + sizeof(float) * DVS * S0S;
+
+// Round metadata is never written while the level runs, so it is read
+// through the constant address space: uniform indices then become scalar
+// loads, which wait on nothing but themselves (a vector load's wait would
+// also drain the producers' prefetches).
+__device__ __forceinline__ int ldc(const int32_t *p, int i)
+{
+    return ((const __attribute__((address_space(4))) int32_t *)p)[i];
+}
+
+struct Item {
+    int s, h, g, dv0, len, nch, chunk0, t0, src;
+};
+
+__device__ __forceinline__ Item item_at(const ChunkArgs &A, int it)
+{
+    Item I;
+    const int rank = it / (A.Hv * NSL);
+    I.s = ldc(A.lvl_seg, A.level * A.level_cap + rank);
+    I.h = (it / NSL) % A.Hv;
+    I.g = I.h / (A.Hv / A.Hk);
+    I.dv0 = (it % NSL) * DVS;
+    I.len = ldc(A.seg_len, I.s);
+    I.nch = (I.len + C - 1) / C;
+    I.chunk0 = ldc(A.seg_chunk0, I.s);
+    I.t0 = ldc(A.seg_start, I.s);
+    I.src = ldc(A.seg_src, I.s);
+    return I;
+}
+
+// the entering state of an item: null = zero state
+__device__ __forceinline__ const float *item_s0(const ChunkArgs &A, const Item &I)
+{
+    const size_t SZ = (size_t)DV * DK;
+    if (I.src == -1) return nullptr;
+    return I.src >= 0 ? A.fork_states + ((size_t)I.src * A.Hv + I.h) * SZ
+                      : A.state_in + ((size_t)(-2 - I.src) * A.Hv + I.h) * SZ;
+}
+
+// fork points of an item's segment (range e .. e_end of emit_pos), the
+// offset of the next one (INT_MAX when none is left) and its state_out slot
+struct Emits {
+    int e, e_end, next, so;
+};
+
+__device__ __forceinline__ Emits item_emits(const ChunkArgs &A, const Item &I)
+{
+    Emits E;
+    E.e = ldc(A.emit_off, I.s);
+    E.e_end = ldc(A.emit_off, I.s + 1);
+    E.next = E.e < E.e_end ? ldc(A.emit_pos, E.e) : 0x7fffffff;
+    E.so = ldc(A.seg_state_out, I.s);
+    return E;
+}
+
+__device__ __forceinline__ void emit_advance(const ChunkArgs &A, Emits &E)
+{
+    ++E.e;
+    E.next = E.e < E.e_end ? ldc(A.emit_pos, E.e) : 0x7fffffff;
+}
 
 // 16 dk x 4-row fp32 state fragment <-> global [dv][dk] row (4 consecutive dk)
 __device__ __forceinline__ void store_state(float *base, int dvc, int G, const f32x4 *st)
@@ -259,100 +338,140 @@ __device__ __forceinline__ void store_state(float *base, int dvc, int G, const f
 }
 
 // producer `part`: store token rows [16 part, +16) of the output slice of
-// chunk `c` (left in B.vs by the consumers), 8 lanes x 16 B per row
-__device__ __forceinline__ void flush_out(const ChunkBuf &B, const ChunkArgs &A, int s, int c, int h, int lane,
-                                          int part, int dv0)
+// chunk `c` of item I (left in B.vs by the consumers), 8 lanes x 16 B per row
+__device__ __forceinline__ void flush_out(const ChunkBuf &B, const ChunkArgs &A, const Item &I, int c, int lane,
+                                          int part)
 {
-    const int n = min(C, A.seg_len[s] - c * C);
-    const size_t t0 = (size_t)A.seg_start[s] + (size_t)c * C;
+    const int n = min(C, I.len - c * C);
+    const size_t t0 = (size_t)I.t0 + (size_t)c * C;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int idx = j * 64 + lane, row = part * (C / PRODUCERS) + (idx >> 3), c8 = idx & 7;
         if (row < n)
-            *reinterpret_cast<uint4 *>(A.out + ((t0 + row) * A.Hv + h) * DV + dv0 + c8 * 8) =
+            *reinterpret_cast<uint4 *>(A.out + ((t0 + row) * A.Hv + I.h) * DV + I.dv0 + c8 * 8) =
                 *reinterpret_cast<const uint4 *>(B.vs + row * VS + c8 * 8);
     }
 }
 
-// The transposed keys are stored with the token index XOR-swizzled per key
-// dim (a multiple of 4, so groups of 4 tokens stay contiguous for the MFMA
-// operand reads): row d holds token t at column t ^ kt_swz(d).  This spreads
-// the producers' 2-byte transposed writes over the LDS banks.
-__device__ __forceinline__ int kt_swz(int d) { return ((d >> 3) & 15) << 2; }
-
-__device__ __forceinline__ bf16x8 load_kt(const uint16_t *kt, int d, int ks, int G)
+// Operand of K^T for the state update, read from the key rows with the LDS
+// transpose read: within each 16-lane group, source lane s points at token
+// row t0 + s/4, key dims d0 + 4(s%4) .. +3 (a group of four, wherever the
+// permuted row stores it), and lane i receives key dim d0 + i of tokens
+// t0 .. t0+3.  Two reads give the permuted reduction index
+// (tokens 32 ks + 4G .. +3 and 32 ks + 16 + 4G .. +3) of lane group G.
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 load_kT(const uint16_t *kr, int d0, int ks, int lane)
 {
-    const uint16_t *row = kt + d * KTS;
-    const int m = kt_swz(d);
-    const uint2 lo = *reinterpret_cast<const uint2 *>(row + ((ks * 32 + 4 * G) ^ m));
-    const uint2 hi = *reinterpret_cast<const uint2 *>(row + ((ks * 32 + 16 + 4 * G) ^ m));
-    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    const int G = lane >> 4, sl = lane & 15;
+    const uint16_t *p = kr + (ks * 32 + 4 * G + (sl >> 2)) * KS + perm_off(d0 + 4 * (sl & 3));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)p);
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p + 16 * KS));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
 }
 
-// producer `part` stages token rows [16 part, 16 part + 16) of chunk `c`
-// into `B`.  Loads are coalesced (consecutive lanes read consecutive 16 B of
-// a row), and all of them are issued before the first LDS write.
-__device__ __forceinline__ void stage_chunk(ChunkBuf &B, const ChunkArgs &A, int s, int c, int h, int g, int lane,
-                                            int part, int dv0, int chunk0)
+// transpose read (see load_kT) of four consecutive rows of 16 columns
+__device__ __forceinline__ v4s load_tr(const uint16_t *p)
 {
-    const int len = A.seg_len[s];
-    const int n = min(C, len - c * C);
-    const size_t t0 = (size_t)A.seg_start[s] + (size_t)c * C;
-    const size_t mat = ((size_t)(chunk0 + c) * A.Hv + h) * C * C;
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)p);
+}
+
+// two fp32 -> two bf16 (RNE) in one word, the first in the low half
+__device__ __forceinline__ uint32_t pack2(float a, float b)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+// One step's worth of a producer's loads, held in registers between the
+// interval that issues them and the interval that writes them to LDS.
+struct StepRegs {
+    uint4 kv[4], qv[4], tv[2], pv[2], vv[2];
+    f32x4 s0[8];
+    float a_raw, b_raw;
+};
+
+// issue the loads of chunk c of item I (and, when c == 0, of its entering
+// state); rows [16 part, 16 part + 16) of the chunk, dv rows of the state
+// likewise.  Coalesced: consecutive lanes read consecutive 16 B of a row.
+__device__ __forceinline__ void load_step(StepRegs &R, const ChunkArgs &A, const Item &I, int c, int lane, int part)
+{
+    const int n = min(C, I.len - c * C);
+    const size_t t0 = (size_t)I.t0 + (size_t)c * C;
+    const size_t mat = ((size_t)(I.chunk0 + c) * A.Hv + I.h) * C * C;
     const int rb = part * (C / PRODUCERS);
     // buffer resources based at this chunk's first row: 32-bit offsets, and
     // the hardware range check returns zeros past the end of each tensor
-    const size_t kq_base = (t0 * A.Hk + g) * DK, kq_end = (size_t)A.T * A.Hk * DK;
-    const size_t v_base = (t0 * A.Hv + h) * DV + dv0, v_end = (size_t)A.T * A.Hv * DV;
+    const size_t kq_base = (t0 * A.Hk + I.g) * DK, kq_end = (size_t)A.T * A.Hk * DK;
+    const size_t v_base = (t0 * A.Hv + I.h) * DV + I.dv0, v_end = (size_t)A.T * A.Hv * DV;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(A.k + kq_base, (kq_end - kq_base) * 2);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(A.q + kq_base, (kq_end - kq_base) * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(A.v + v_base, (v_end - v_base) * 2);
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(A.tmat + mat, (size_t)C * C * 2);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(A.pmat + mat, (size_t)C * C * 2);
     const int kq_row = A.Hk * DK * 2, v_row = A.Hv * DV * 2;   // bytes between tokens
-    uint4 kv[4], qv[4], tv[2], pv[2], vv[2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {               // 4 rows x 16 lanes per instruction
         const int idx = j * 64 + lane, row = rb + (idx >> 4), c8 = idx & 15;
-        kv[j] = buf_load(rk, row * kq_row + c8 * 16);
-        qv[j] = buf_load(rq, row * kq_row + c8 * 16);
+        R.kv[j] = buf_load(rk, row * kq_row + c8 * 16);
+        R.qv[j] = buf_load(rq, row * kq_row + c8 * 16);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {               // 8 rows x 8 lanes per instruction
         const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
-        tv[j] = buf_load(rt, row * C * 2 + c8 * 16);
-        pv[j] = buf_load(rp, row * C * 2 + c8 * 16);
-        vv[j] = buf_load(rv, row * v_row + c8 * 16);
+        R.tv[j] = buf_load(rt, row * C * 2 + c8 * 16);
+        R.pv[j] = buf_load(rp, row * C * 2 + c8 * 16);
+        R.vv[j] = buf_load(rv, row * v_row + c8 * 16);
     }
-    float a_raw = 1.f, b_raw = 0.f;
+    R.a_raw = 1.f;
+    R.b_raw = 0.f;
     if (part == 0) {
         const int rr = lane < n ? lane : n - 1;
-        a_raw = A.a[(t0 + rr) * A.Hv + h];
-        b_raw = A.b[(t0 + rr) * A.Hv + h];
+        R.a_raw = A.a[(t0 + rr) * A.Hv + I.h];
+        R.b_raw = A.b[(t0 + rr) * A.Hv + I.h];
     }
+    if (c == 0) {
+        // dv rows [16 part, +16) of the slice, 32 lanes x 16 B per row
+        const float *S0 = item_s0(A, I);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int idx = j * 64 + lane, row = part * 16 + (idx >> 5), c4 = idx & 31;
+            R.s0[j] = S0 ? *reinterpret_cast<const f32x4 *>(S0 + (size_t)(I.dv0 + row) * DK + c4 * 4)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+}
+
+// write a step's registers into LDS buffer B (and the entering state into s0)
+__device__ __forceinline__ void write_step(ChunkBuf &B, float *s0, StepRegs &R, const Item &I, int c, int lane,
+                                           int part)
+{
+    const int n = min(C, I.len - c * C);
+    const int rb = part * (C / PRODUCERS);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int idx = j * 64 + lane, row = rb + (idx >> 4), c8 = idx & 15;
-        if (row >= n) kv[j] = qv[j] = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(B.kr + row * KS + c8 * 8) = kv[j];
-        *reinterpret_cast<uint4 *>(B.qr + row * KS + c8 * 8) = qv[j];
-        const uint16_t *k8 = reinterpret_cast<const uint16_t *>(&kv[j]);
-        const int col = row ^ kt_swz(c8 * 8);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) B.kt[(c8 * 8 + x) * KTS + col] = k8[x];
+        if (row >= n) R.kv[j] = R.qv[j] = make_uint4(0, 0, 0, 0);
+        // key dims 8 c8 .. 8 c8 + 7 = position groups 2 c8 and 2 c8 + 1
+        const int o0 = row * KS + perm_off(c8 * 8), o1 = row * KS + perm_off(c8 * 8 + 4);
+        *reinterpret_cast<uint2 *>(B.kr + o0) = make_uint2(R.kv[j].x, R.kv[j].y);
+        *reinterpret_cast<uint2 *>(B.kr + o1) = make_uint2(R.kv[j].z, R.kv[j].w);
+        *reinterpret_cast<uint2 *>(B.qr + o0) = make_uint2(R.qv[j].x, R.qv[j].y);
+        *reinterpret_cast<uint2 *>(B.qr + o1) = make_uint2(R.qv[j].z, R.qv[j].w);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
-        if (row >= n) vv[j] = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(B.tm + row * TS + c8 * 8) = tv[j];
-        *reinterpret_cast<uint4 *>(B.pm + row * TS + c8 * 8) = pv[j];
-        *reinterpret_cast<uint4 *>(B.vs + row * VS + c8 * 8) = vv[j];
+        if (row >= n) R.vv[j] = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(B.tm + row * TS + c8 * 8) = R.tv[j];
+        *reinterpret_cast<uint4 *>(B.pm + row * TS + c8 * 8) = R.pv[j];
+        *reinterpret_cast<uint4 *>(B.vs + row * VS + c8 * 8) = R.vv[j];
     }
     if (part == 0) {
         const bool live = lane < n;
-        float la = live ? logf(a_raw) : 0.f;
-        const float eta = live ? b_raw : 0.f;
+        float la = live ? logf(R.a_raw) : 0.f;
+        const float eta = live ? R.b_raw : 0.f;
         for (int o = 1; o < 64; o <<= 1) {
             const float y = __shfl_up(la, o, 64);
             if (lane >= o) la += y;
@@ -363,70 +482,119 @@ __device__ __forceinline__ void stage_chunk(ChunkBuf &B, const ChunkArgs &A, int
         B.gsh[lane] = __expf(la);
         B.dsh[lane] = __expf(last - la);
     }
+    if (c == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int idx = j * 64 + lane, row = part * 16 + (idx >> 5), c4 = idx & 31;
+            *reinterpret_cast<f32x4 *>(s0 + row * S0S + c4 * 4) = R.s0[j];
+        }
+    }
 }
 
 __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     ChunkBuf *buf = reinterpret_cast<ChunkBuf *>(smem);
-    if (A.header[H_STATUS] != FK_OK) return;
-    // 1-D grid, work item = (segment rank, v-head, dv slice) with the slice
-    // fastest: the live items are the lowest ids, so they spread over all XCDs
-    constexpr int NSL = DV / DVS;
-    const int rank = blockIdx.x / (A.Hv * NSL);
-    if (rank >= A.header[H_LEVEL0 + A.level]) return;
-    const int s = A.lvl_seg[A.level * A.level_cap + rank];
-    const int h = (blockIdx.x / NSL) % A.Hv, g = h / (A.Hv / A.Hk);
+    float *s0buf = reinterpret_cast<float *>(smem + 2 * sizeof(ChunkBuf));
+    if (ldc(A.header, H_STATUS) != FK_OK) return;
+    // item ids: (segment rank, v-head, dv slice), slice fastest
+    const int n_items = ldc(A.header, H_LEVEL0 + A.level) * A.Hv * NSL;
+    const int stride = gridDim.x;
+    if ((int)blockIdx.x >= n_items) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const bool producer = w >= CONSUMERS;
-    const int part = w - CONSUMERS;
     const int G = lane >> 4, c16 = lane & 15;
-    const int dv0 = (blockIdx.x % NSL) * DVS;
-    const int dvc = dv0 + w * 16 + c16;   // a consumer lane's state column (dv index)
-    const size_t SZ = (size_t)DV * DK;
-    const int len = A.seg_len[s], chunk0 = A.seg_chunk0[s];
-    const int nch = (len + C - 1) / C;
 
-    // The two roles run separate loops with the same number of barriers, so
-    // their registers are allocated independently (roles are wave-uniform).
-    if (producer) {
-        stage_chunk(buf[0], A, s, 0, h, g, lane, part, dv0, chunk0);
+    // Both roles walk the same step sequence and meet at the same barriers:
+    // one before step 0, one extra at the start of every item (the entering
+    // state has been read), one at the end of every step.  Roles are
+    // wave-uniform and run separate loops, so their registers are allocated
+    // independently.
+    if (w >= CONSUMERS) {
+        const int part = w - CONSUMERS;
+        StepRegs R;
+        int it = blockIdx.x, c = 0;
+        Item cur = item_at(A, it);
+        load_step(R, A, cur, 0, lane, part);
+        write_step(buf[0], s0buf, R, cur, 0, lane, part);
+        // step 1 into registers
+        int it1 = it, c1 = 1;
+        bool has1 = true;
+        if (c1 == cur.nch) {
+            it1 = it + stride;
+            c1 = 0;
+            has1 = it1 < n_items;
+        }
+        Item nx1 = has1 ? (c1 == 0 ? item_at(A, it1) : cur) : cur;
+        if (has1) load_step(R, A, nx1, c1, lane, part);
         __syncthreads();
-        for (int c = 0; c < nch; ++c) {
-            if (c + 1 < nch) {
-                ChunkBuf &Bn = buf[(c + 1) & 1];
-                if (c >= 1) flush_out(Bn, A, s, c - 1, h, lane, part, dv0);
-                stage_chunk(Bn, A, s, c + 1, h, g, lane, part, dv0, chunk0);
+        Item prev = cur;
+        int pc = -1;
+        for (int j = 0;; ++j) {
+            // step j = (cur, c) is being consumed; step j+1 = (nx1, c1) sits in R
+            if (c == 0) __syncthreads();   // consumers have read the entering state
+            // step j+2
+            int it2 = it1, c2 = c1 + 1;
+            bool has2 = has1;
+            if (has1 && c2 == nx1.nch) {
+                it2 = it1 + stride;
+                c2 = 0;
+                has2 = it2 < n_items;
             }
-            __syncthreads();   // chunk c consumed, chunk c+1 staged
+            if (has1) {
+                ChunkBuf &Bn = buf[(j + 1) & 1];
+                if (pc >= 0) flush_out(Bn, A, prev, pc, lane, part);
+                write_step(Bn, s0buf, R, nx1, c1, lane, part);
+            }
+            Item nx2 = has2 ? (c2 == 0 ? item_at(A, it2) : nx1) : nx1;
+            if (has2) load_step(R, A, nx2, c2, lane, part);
+            __syncthreads();   // step j consumed, step j+1 staged
+            if (!has1) {
+                // outputs of steps j-1 and j are still in LDS
+                if (pc >= 0) flush_out(buf[(j + 1) & 1], A, prev, pc, lane, part);
+                flush_out(buf[j & 1], A, cur, c, lane, part);
+                return;
+            }
+            prev = cur;
+            pc = c;
+            cur = nx1;
+            c = c1;
+            it1 = it2;
+            c1 = c2;
+            has1 = has2;
+            nx1 = nx2;
         }
-        // the last two chunks' outputs have not been flushed yet
-        if (nch >= 2) flush_out(buf[(nch - 2) & 1], A, s, nch - 2, h, lane, part, dv0);
-        flush_out(buf[(nch - 1) & 1], A, s, nch - 1, h, lane, part, dv0);
-        return;
     }
 
+    const int wv = w;   // consumer wave: dv columns [16 w, 16 w + 16) of the slice
     f32x4 st[DK / 16];
-    int e = A.emit_off[s];
-    const int e_end = A.emit_off[s + 1];
-    {
-        const int src = A.seg_src[s];
-        const float *S0 = src == -1 ? nullptr
-                                    : (src >= 0 ? A.fork_states + ((size_t)src * A.Hv + h) * SZ
-                                                : A.state_in + ((size_t)(-2 - src) * A.Hv + h) * SZ);
-#pragma unroll
-        for (int i = 0; i < DK / 16; ++i)
-            st[i] = S0 ? *reinterpret_cast<const f32x4 *>(S0 + (size_t)dvc * DK + i * 16 + G * 4)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
-        while (e < e_end && A.emit_pos[e] == 0) {
-            store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, st);
-            ++e;
-        }
-    }
+    int it = blockIdx.x, c = 0;
+    Item cur = item_at(A, it);
+    Emits E = item_emits(A, cur);
+    const size_t SZ = (size_t)DV * DK;
     __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-        ChunkBuf &B = buf[c & 1];
-        const int n = min(C, len - c * C);
+    for (int j = 0;; ++j) {
+        ChunkBuf &B = buf[j & 1];
+        const int dvc = cur.dv0 + wv * 16 + c16;   // this lane's state column (dv index)
+        const bool last = c + 1 == cur.nch;
+        // the next item's metadata, fetched while this step computes
+        const bool more = !last || it + stride < n_items;
+        Item nxt = cur;
+        Emits nE = E;
+        if (last && more) {
+            nxt = item_at(A, it + stride);
+            nE = item_emits(A, nxt);
+        }
+        if (c == 0) {
+#pragma unroll
+            for (int i = 0; i < DK / 16; ++i)
+                st[i] = *reinterpret_cast<const f32x4 *>(s0buf + (wv * 16 + c16) * S0S + i * 16 + G * 4);
+            __syncthreads();   // the producers may now stage the next entering state
+            while (E.next == 0) {
+                store_state(A.fork_states + ((size_t)E.e * A.Hv + cur.h) * SZ, dvc, G, st);
+                emit_advance(A, E);
+            }
+        }
+        const int n = min(C, cur.len - c * C);
         // X = K S0^T, Y = Q S0^T for this wave's 16 dv columns
         f32x4 xa[C / 16], ya[C / 16];
 #pragma unroll
@@ -441,15 +609,18 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
             }
         }
         __builtin_amdgcn_sched_barrier(0);   // bound the operand loads kept in flight
-        // R = diag(b) (V - diag(e^l) X);  U = T R
+        // R = diag(b) (V - diag(e^l) X);  U = T R.  A lane's four rows are
+        // 4 consecutive tokens of one dv column: one transpose read of V.
 #pragma unroll
-        for (int mt = 0; mt < C / 16; ++mt)
+        for (int mt = 0; mt < C / 16; ++mt) {
+            const int i0 = mt * 16 + G * 4;
+            const v4s vq = load_tr(B.vs + (i0 + (c16 >> 2)) * VS + wv * 16 + 4 * (c16 & 3));
+            const f32x4 eb = *reinterpret_cast<const f32x4 *>(B.esh + i0);
+            const f32x4 gb = *reinterpret_cast<const f32x4 *>(B.gsh + i0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = mt * 16 + G * 4 + r;
-                const float vv = bf16_to_f32(B.vs[i * VS + w * 16 + c16]);
-                xa[mt][r] = B.esh[i] * (vv - B.gsh[i] * xa[mt][r]);
-            }
+            for (int r = 0; r < 4; ++r)
+                xa[mt][r] = eb[r] * (bf16_to_f32((uint16_t)vq[r]) - gb[r] * xa[mt][r]);
+        }
         const bf16x8 rb0 = pack(xa[0], xa[1]), rb1 = pack(xa[2], xa[3]);
         f32x4 ua[C / 16];
 #pragma unroll
@@ -460,62 +631,87 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
         __builtin_amdgcn_sched_barrier(0);
         // O = diag(e^l) Y + P U  -> left in the value buffer for the producers
         const bf16x8 ub0 = pack(ua[0], ua[1]), ub1 = pack(ua[2], ua[3]);
+        const bool odd = c16 & 1;
 #pragma unroll
         for (int mt = 0; mt < C / 16; ++mt) {
+            const int i0 = mt * 16 + G * 4;
+            const f32x4 gb = *reinterpret_cast<const f32x4 *>(B.gsh + i0);
             f32x4 oa;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) oa[r] = B.gsh[mt * 16 + G * 4 + r] * ya[mt][r];
+            for (int r = 0; r < 4; ++r) oa[r] = gb[r] * ya[mt][r];
             oa = mfma(load_perm(B.pm + (mt * 16 + c16) * TS, 0, G), ub0, oa);
             if (mt >= 2) oa = mfma(load_perm(B.pm + (mt * 16 + c16) * TS, 1, G), ub1, oa);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                B.vs[(mt * 16 + G * 4 + r) * VS + w * 16 + c16] = __builtin_bit_cast(uint16_t, (__bf16)oa[r]);
+            // lanes c16 and c16^1 hold neighbouring dv columns of the same 4
+            // rows: swap halves so each lane writes two rows x two columns
+            const uint32_t lo = pack2(oa[0], oa[1]), hi = pack2(oa[2], oa[3]);   // (row0,row1), (row2,row3)
+            const uint32_t mine = odd ? lo : hi;                                   // what the partner needs
+            const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xB1, 0xF, 0xF, false);
+            const uint32_t keep = odd ? hi : lo;                                   // rows this lane writes
+            // even lane: rows 0,1 of columns (c16, c16+1); odd lane: rows 2,3 of (c16-1, c16)
+            const int col = wv * 16 + (c16 & ~1), rr = i0 + (odd ? 2 : 0);
+            const uint32_t w0 = odd ? ((got & 0xffffu) | (keep << 16)) : ((keep & 0xffffu) | (got << 16));
+            const uint32_t w1 = odd ? ((got >> 16) | (keep & 0xffff0000u)) : ((keep >> 16) | (got & 0xffff0000u));
+            *reinterpret_cast<uint32_t *>(B.vs + rr * VS + col) = w0;
+            *reinterpret_cast<uint32_t *>(B.vs + (rr + 1) * VS + col) = w1;
         }
         // fork points strictly inside this chunk: state after `off` tokens
-        while (e < e_end && A.emit_pos[e] < c * C + n) {
-            const int off = A.emit_pos[e] - c * C;   // 1 .. n-1
+        while (E.next < c * C + n) {
+            const int off = E.next - c * C;   // 1 .. n-1
             const float lr = B.lsh[off - 1];
             f32x4 u0[C / 16];
 #pragma unroll
             for (int mt = 0; mt < C / 16; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int j = mt * 16 + G * 4 + r;
-                    u0[mt][r] = j < off ? __expf(lr - B.lsh[j]) * ua[mt][r] : 0.f;
+                    const int jj = mt * 16 + G * 4 + r;
+                    u0[mt][r] = jj < off ? __expf(lr - B.lsh[jj]) * ua[mt][r] : 0.f;
                 }
             const bf16x8 eb0 = pack(u0[0], u0[1]), eb1 = pack(u0[2], u0[3]);
             const float gr = __expf(lr);
             f32x4 tmp[DK / 16];
 #pragma unroll
             for (int i = 0; i < DK / 16; ++i) {
-                tmp[i] = mfma(load_kt(B.kt, i * 16 + c16, 0, G), eb0, st[i] * gr);
-                tmp[i] = mfma(load_kt(B.kt, i * 16 + c16, 1, G), eb1, tmp[i]);
+                tmp[i] = mfma(load_kT(B.kr, i * 16, 0, lane), eb0, st[i] * gr);
+                tmp[i] = mfma(load_kT(B.kr, i * 16, 1, lane), eb1, tmp[i]);
             }
-            store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, tmp);
-            ++e;
+            store_state(A.fork_states + ((size_t)E.e * A.Hv + cur.h) * SZ, dvc, G, tmp);
+            emit_advance(A, E);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // S^T <- e^{l_last} S^T + K^T diag(e^{l_last - l}) U
+        // S^T <- e^{l_last} S^T + K^T diag(e^{l_last - l}) U, unless nothing
+        // reads the state after the item's last chunk
+        if (!last || E.e < E.e_end || E.so >= 0) {
 #pragma unroll
-        for (int mt = 0; mt < C / 16; ++mt)
+            for (int mt = 0; mt < C / 16; ++mt) {
+                const f32x4 db = *reinterpret_cast<const f32x4 *>(B.dsh + mt * 16 + G * 4);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ua[mt][r] *= B.dsh[mt * 16 + G * 4 + r];
-        const bf16x8 wb0 = pack(ua[0], ua[1]), wb1 = pack(ua[2], ua[3]);
-        const float gl = B.gsh[C - 1];
+                for (int r = 0; r < 4; ++r) ua[mt][r] *= db[r];
+            }
+            const bf16x8 wb0 = pack(ua[0], ua[1]), wb1 = pack(ua[2], ua[3]);
+            const float gl = B.gsh[C - 1];
 #pragma unroll
-        for (int i = 0; i < DK / 16; ++i) {
-            st[i] = mfma(load_kt(B.kt, i * 16 + c16, 0, G), wb0, st[i] * gl);
-            st[i] = mfma(load_kt(B.kt, i * 16 + c16, 1, G), wb1, st[i]);
+            for (int i = 0; i < DK / 16; ++i) {
+                st[i] = mfma(load_kT(B.kr, i * 16, 0, lane), wb0, st[i] * gl);
+                st[i] = mfma(load_kT(B.kr, i * 16, 1, lane), wb1, st[i]);
+            }
+            // a fork point at the end of this chunk
+            while (E.next == c * C + n) {
+                store_state(A.fork_states + ((size_t)E.e * A.Hv + cur.h) * SZ, dvc, G, st);
+                emit_advance(A, E);
+            }
+            if (last && E.so >= 0) store_state(A.state_out + ((size_t)E.so * A.Hv + cur.h) * SZ, dvc, G, st);
         }
-        // a fork point at the end of this chunk
-        while (e < e_end && A.emit_pos[e] == c * C + n) {
-            store_state(A.fork_states + ((size_t)e * A.Hv + h) * SZ, dvc, G, st);
-            ++e;
+        __syncthreads();   // step j consumed, step j+1 staged
+        if (!more) return;
+        if (!last) {
+            ++c;
+        } else {
+            it += stride;
+            cur = nxt;
+            E = nE;
+            c = 0;
         }
-        __syncthreads();   // chunk c consumed, chunk c+1 staged
     }
-    const int so = A.seg_state_out[s];
-    if (so >= 0) store_state(A.state_out + ((size_t)so * A.Hv + h) * SZ, dvc, G, st);
 }
 
 }  // namespace gdnk
@@ -569,14 +765,19 @@ int fk_launch_gdn_bf16(const fk_tree_meta *meta, int level, const void *q, const
     A.state_in = state_in;
     A.state_out = state_out;
     A.fork_states = fork_states;
-    dim3 grid((unsigned)((int64_t)meta->level_cap * Hv * (gdnk::DV / gdnk::DVS)));
-    static bool configured = false;
-    const size_t lds = 2 * sizeof(gdnk::ChunkBuf);
-    if (!configured) {
+    // persistent: at most one work-group per compute unit (the LDS holds one)
+    int dev = 0;
+    FK_HIP(hipGetDevice(&dev));
+    static int n_cu[64] = {0};
+    if (dev < 0 || dev >= 64) return FK_E_HIP;
+    if (!n_cu[dev]) {
+        FK_HIP(hipDeviceGetAttribute(&n_cu[dev], hipDeviceAttributeMultiprocessorCount, dev));
         FK_HIP(hipFuncSetAttribute((const void *)gdnk::k_gdn_chunk, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)lds));
-        configured = true;
+                                   (int)gdnk::CHUNK_LDS));
     }
+    const int64_t cap = (int64_t)meta->level_cap * Hv * gdnk::NSL;
+    dim3 grid((unsigned)(cap < n_cu[dev] ? cap : n_cu[dev]));
+    const size_t lds = gdnk::CHUNK_LDS;
     gdnk::k_gdn_chunk<<<grid, gdnk::CHUNK_THREADS, lds, st>>>(A);
     return launch_status();
 }
