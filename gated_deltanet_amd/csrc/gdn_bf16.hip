@@ -39,7 +39,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int C = FK_GDN_CHUNK;   // 64 tokens
 constexpr int DK = 128, DV = 128;
 constexpr int DVS = 64;           // dv columns of one work-group (4 waves x 16)
-constexpr int KS = DK + 8;        // LDS stride (bf16) of key/query rows
+constexpr int KS = DK;            // LDS stride (bf16) of key/query rows (swizzled, unpadded)
 constexpr int TS = C + 8;         // LDS stride (bf16) of 64-wide rows written 16 B at a time (T, P)
 constexpr int AS = C + 4;         // LDS stride (fp32) of the prep matrix
 
@@ -76,6 +76,21 @@ __device__ __forceinline__ int perm_off(int p) { return (p & ~31) + perm4((p >> 
 __device__ __forceinline__ bf16x8 load_perm(const uint16_t *row, int ks, int G)
 {
     return as_bf16x8(*reinterpret_cast<const uint4 *>(row + ks * 32 + 8 * G));
+}
+
+// Key and query rows in LDS: 256 B per row, no padding; the 16-byte units of
+// row r are XOR-swizzled by the two 2-bit halves of r's low nibble swapped.
+// Both readers are then free of bank conflicts: the operand read (16 rows,
+// one unit each) sees 16 different units, and the transpose read (4 rows x
+// 4 units of one block) sees 16 different units as well.
+__device__ __forceinline__ int kq_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// element offset of element `e` (a multiple of 4) of row `row`
+__device__ __forceinline__ int kq_off(int row, int e) { return row * KS + ((((e >> 3) ^ kq_swz(row)) << 3) | (e & 7)); }
+
+__device__ __forceinline__ bf16x8 load_kq(const uint16_t *buf, int row, int ks, int G)
+{
+    return as_bf16x8(*reinterpret_cast<const uint4 *>(buf + kq_off(row, ks * 32 + 8 * G)));
 }
 
 // raw buffer resource (gfx9 data format dword) over `bytes` bytes at `p`
@@ -363,10 +378,10 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8 load_kT(const uint16_t *kr, int d0, int ks, int lane)
 {
     const int G = lane >> 4, sl = lane & 15;
-    const uint16_t *p = kr + (ks * 32 + 4 * G + (sl >> 2)) * KS + perm_off(d0 + 4 * (sl & 3));
+    const int row = ks * 32 + 4 * G + (sl >> 2), e = perm_off(d0 + 4 * (sl & 3));
     typedef __attribute__((address_space(3))) v4s lds_v4s;
-    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)p);
-    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p + 16 * KS));
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(kr + kq_off(row, e)));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(kr + kq_off(row + 16, e)));
     const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
     return as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
 }
@@ -454,7 +469,7 @@ __device__ __forceinline__ void write_step(ChunkBuf &B, float *s0, StepRegs &R, 
         const int idx = j * 64 + lane, row = rb + (idx >> 4), c8 = idx & 15;
         if (row >= n) R.kv[j] = R.qv[j] = make_uint4(0, 0, 0, 0);
         // key dims 8 c8 .. 8 c8 + 7 = position groups 2 c8 and 2 c8 + 1
-        const int o0 = row * KS + perm_off(c8 * 8), o1 = row * KS + perm_off(c8 * 8 + 4);
+        const int o0 = kq_off(row, perm_off(c8 * 8)), o1 = kq_off(row, perm_off(c8 * 8 + 4));
         *reinterpret_cast<uint2 *>(B.kr + o0) = make_uint2(R.kv[j].x, R.kv[j].y);
         *reinterpret_cast<uint2 *>(B.kr + o1) = make_uint2(R.kv[j].z, R.kv[j].w);
         *reinterpret_cast<uint2 *>(B.qr + o0) = make_uint2(R.qv[j].x, R.qv[j].y);
@@ -604,8 +619,8 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
             const bf16x8 sb = pack(st[2 * ks2], st[2 * ks2 + 1]);
 #pragma unroll
             for (int mt = 0; mt < C / 16; ++mt) {
-                xa[mt] = mfma(load_perm(B.kr + (mt * 16 + c16) * KS, ks2, G), sb, xa[mt]);
-                ya[mt] = mfma(load_perm(B.qr + (mt * 16 + c16) * KS, ks2, G), sb, ya[mt]);
+                xa[mt] = mfma(load_kq(B.kr, mt * 16 + c16, ks2, G), sb, xa[mt]);
+                ya[mt] = mfma(load_kq(B.qr, mt * 16 + c16, ks2, G), sb, ya[mt]);
             }
         }
         __builtin_amdgcn_sched_barrier(0);   // bound the operand loads kept in flight
