@@ -112,11 +112,12 @@ __device__ __forceinline__ bf16x8 load_row8(const uint16_t *row, int ks, int G)
 
 // ---------------------------------------------------------------------------
 // Per (chunk, v-head), everything that does not depend on a state:
-//   T = (I + A)^-1 (fp32 forward substitution, lane = column) and
+//   T = (I + A)^-1 (fp32, by 16 x 16 blocks) and
 //   P = Gamma o Q K^T (lower triangle incl. the diagonal), both stored bf16.
 // Key and query rows are loaded straight into MFMA operand registers (the
-// A and B operand layouts of a 16x16x32 product coincide), so LDS holds
-// only the fp32 A matrix.  Four items per work-group, one wave each.
+// A and B operand layouts of a 16x16x32 product coincide); LDS holds the
+// diagonal blocks and the finished T.  Four items per work-group, one wave
+// each.
 // ---------------------------------------------------------------------------
 constexpr int PREP_WAVES = 4;
 
@@ -191,36 +192,99 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
                 *reinterpret_cast<uint2 *>(pdst + i * C + perm_off(jt * 16 + G * 4)) = __builtin_bit_cast(uint2, p4);
         }
     }
-    // A = strictly lower part of diag(b) (Gamma o K K^T)
+    // T = (I + A)^-1 by 16 x 16 blocks, A = the strictly lower part of
+    // diag(b) (Gamma o K K^T):  diagonal blocks T_bb = (I + A_bb)^-1 by
+    // forward substitution (lane = block x column), then
+    //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj   (i > j)
+    // on fp32 MFMA, in an order where every T_kj on the right is known.  The
+    // 16x16x4 fp32 products take reduction position 4G + s in instruction s
+    // from lane group G, so a product's accumulator (rows 4G..4G+3 of a
+    // column) is directly the B operand of the next one.
+    // (1) off-diagonal blocks of A as A operands: lane (G, c16) holds
+    //     A_{bi,bk}[c16][4G + s] in register s, from the tile K_bk K_bi^T
+    constexpr int BI[6] = {1, 2, 2, 3, 3, 3}, BK[6] = {0, 0, 1, 0, 1, 2};
+    f32x4 aop[6];
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
+    for (int p = 0; p < 6; ++p) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tj = 0; tj <= ti; ++tj) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[BK[p]][kk], kf[BI[p]][kk], acc);
+        const int i = BI[p] * 16 + c16;
+        const float ei = esh[i], li = lsh[i];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[ti][kk], kf[tj][kk], acc);
+        for (int r = 0; r < 4; ++r) aop[p][r] = ei * __expf(li - lsh[BK[p] * 16 + G * 4 + r]) * acc[r];
+    }
+    // (2) diagonal blocks of A, row-major in LDS: ad[b][row][col]
+    constexpr int DB = 16 * 16 + 16;   // block stride (floats): blocks on different banks
+    float *ad = am;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = ti * 16 + G * 4 + r, j = tj * 16 + c16;
-                am[i * AS + j] = j < i ? esh[i] * __expf(lsh[i] - lsh[j]) * acc[r] : 0.f;
-            }
+    for (int bk = 0; bk < 4; ++bk) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[bk][kk], kf[bk][kk], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ri = G * 4 + r, i = bk * 16 + ri, j = bk * 16 + c16;
+            ad[bk * DB + ri * 16 + c16] = c16 < ri ? esh[i] * __expf(lsh[i] - lsh[j]) * acc[r] : 0.f;
         }
-    __syncthreads();
-    // forward substitution: T[i][col] = delta(i, col) - sum_{j<i} A[i][j] T[j][col]
-    float x[C];
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        float acc0 = i == lane ? 1.f : 0.f, acc1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < i; j += 2) {
-            acc0 -= am[i * AS + j] * x[j];
-            if (j + 1 < i) acc1 -= am[i * AS + j + 1] * x[j + 1];
-        }
-        x[i] = acc0 + acc1;
     }
     __syncthreads();
+    // (3) T_bb column cc in lane (bb, cc)
+    const int bb = lane >> 4, cc = lane & 15;
+    float x[16];
 #pragma unroll
-    for (int i = 0; i < C; ++i) am[i * AS + lane] = x[i];
+    for (int kr = 0; kr < 16; ++kr) {
+        float acc0 = kr == cc ? 1.f : 0.f, acc1 = 0.f;
+        const float *arow = ad + bb * DB + kr * 16;
+#pragma unroll
+        for (int j = 0; j < kr; j += 2) {
+            acc0 -= arow[j] * x[j];
+            if (j + 1 < kr) acc1 -= arow[j + 1] * x[j + 1];
+        }
+        x[kr] = acc0 + acc1;
+    }
+    __syncthreads();
+    float *td = am;   // T_bb, row-major, same place
+#pragma unroll
+    for (int kr = 0; kr < 16; ++kr) td[bb * DB + kr * 16 + cc] = x[kr];
+    __syncthreads();
+    auto tB = [&](int b_) {   // T_bb as a B operand: rows 4G..4G+3, column c16
+        f32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = td[b_ * DB + (G * 4 + r) * 16 + c16];
+        return v;
+    };
+    auto tA = [&](int b_) {   // T_bb as an A operand: row c16, columns 4G..4G+3
+        return *reinterpret_cast<const f32x4 *>(td + b_ * DB + c16 * 16 + G * 4);
+    };
+    auto mm = [](f32x4 A_, f32x4 B_, f32x4 acc) {
+#pragma unroll
+        for (int s_ = 0; s_ < 4; ++s_) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A_[s_], B_[s_], acc, 0, 0, 0);
+        return acc;
+    };
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 t00 = tB(0), t11 = tB(1), t22 = tB(2);
+    const f32x4 a1 = tA(1), a2 = tA(2), a3 = tA(3);
+    const f32x4 t10 = -mm(a1, mm(aop[0], t00, z), z);
+    const f32x4 t21 = -mm(a2, mm(aop[2], t11, z), z);
+    const f32x4 t32 = -mm(a3, mm(aop[5], t22, z), z);
+    const f32x4 t20 = -mm(a2, mm(aop[2], t10, mm(aop[1], t00, z)), z);
+    const f32x4 t31 = -mm(a3, mm(aop[5], t21, mm(aop[4], t11, z)), z);
+    const f32x4 t30 = -mm(a3, mm(aop[5], t20, mm(aop[4], t10, mm(aop[3], t00, z))), z);
+    __syncthreads();
+    // (4) T into am, row-major (the blocks above the diagonal are never read)
+#pragma unroll
+    for (int kr = 0; kr < 16; ++kr) am[(bb * 16 + kr) * AS + bb * 16 + cc] = x[kr];
+    auto put = [&](int bi, int bj, f32x4 t) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) am[(bi * 16 + G * 4 + r) * AS + bj * 16 + c16] = t[r];
+    };
+    put(1, 0, t10);
+    put(2, 1, t21);
+    put(3, 2, t32);
+    put(2, 0, t20);
+    put(3, 1, t31);
+    put(3, 0, t30);
     __syncthreads();
     if (!valid) return;
     // row `lane` of T, stored permuted (both T and P serve as A operands)
@@ -232,7 +296,10 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
         // 16+4G'..16+4G'+3 of block j8/4, G' = j8 % 4
         const int base = (j8 >> 2) * 32 + 4 * (j8 & 3);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)am[lane * AS + base + (e < 4 ? e : 12 + e)];
+        for (int e = 0; e < 8; ++e) {
+            const int col = base + (e < 4 ? e : 12 + e);
+            v[e] = (col >> 4) > (lane >> 4) ? (__bf16)0.f : (__bf16)am[lane * AS + col];
+        }
         *reinterpret_cast<uint4 *>(dst + j8 * 8) = __builtin_bit_cast(uint4, v);
     }
 }
