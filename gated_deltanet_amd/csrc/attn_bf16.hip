@@ -121,16 +121,19 @@ __global__ void __launch_bounds__(THREADS, 2)
 k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, const uint16_t *__restrict__ kp,
             const uint16_t *__restrict__ vp, uint16_t *__restrict__ out, const int32_t *__restrict__ header,
             const int32_t *__restrict__ tile_seg, const int32_t *__restrict__ tile_row0,
-            const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_len,
-            const int32_t *__restrict__ seg_depth, const int32_t *__restrict__ seg_anc,
-            const int32_t *__restrict__ seg_fork, const int32_t *__restrict__ page_off,
-            const int32_t *__restrict__ pages)
+            const int32_t *__restrict__ tile_order, const int32_t *__restrict__ seg_start,
+            const int32_t *__restrict__ seg_len, const int32_t *__restrict__ seg_depth,
+            const int32_t *__restrict__ seg_anc, const int32_t *__restrict__ seg_fork,
+            const int32_t *__restrict__ page_off, const int32_t *__restrict__ pages)
 {
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][K_LDS];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][V_LDS];
     if (header[H_STATUS] != FK_OK) return;
-    const int tile = blockIdx.x, g = blockIdx.y;
-    if (tile >= header[H_NTILES]) return;
+    // heaviest tiles first (both kv heads of a tile side by side), so the
+    // launch does not end on a long tile started late
+    const int rank = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+    if (rank >= header[H_NTILES]) return;
+    const int tile = tile_order[rank];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int half = lane >> 5, n = lane & 31;
     const int s = tile_seg[tile], row0 = tile_row0[tile];
@@ -278,11 +281,12 @@ int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv
                         const void *v_pool, void *out, const void *ws, hipStream_t st)
 {
     const WsLayout L = ws_layout(*meta, 0, 0, 0);
-    dim3 grid((unsigned)L.tile_cap, (unsigned)Hkv);
+    dim3 grid((unsigned)(L.tile_cap * Hkv));
     attn::k_attn_bf16<<<grid, attn::THREADS, 0, st>>>(
         (const uint16_t *)q, Hq, Hkv, scale * 1.4426950408889634f, (const uint16_t *)k_pool,
         (const uint16_t *)v_pool, (uint16_t *)out, ws_at<int32_t>(ws, L.header), ws_at<int32_t>(ws, L.tile_seg),
-        ws_at<int32_t>(ws, L.tile_row0), ws_at<int32_t>(ws, L.seg_start), ws_at<int32_t>(ws, L.seg_len),
+        ws_at<int32_t>(ws, L.tile_row0), ws_at<int32_t>(ws, L.tile_order), ws_at<int32_t>(ws, L.seg_start),
+        ws_at<int32_t>(ws, L.seg_len),
         ws_at<int32_t>(ws, L.seg_depth), ws_at<int32_t>(ws, L.seg_anc), meta->seg_fork, meta->seg_page_off,
         meta->seg_pages);
     return launch_status();

@@ -84,6 +84,7 @@ struct BuildArgs {
     int32_t *header, *seg_start, *seg_end, *seg_nrun, *seg_len, *seg_pos0, *seg_depth, *seg_anc;
     int32_t *seg_src, *seg_owner, *kid_cnt, *kid_off, *kid_fill, *kids, *emit_off, *emit_pos;
     int32_t *tile_seg, *tile_row0, *lvl_seg, *chunk_seg, *chunk_row0, *seg_chunk0;
+    int32_t *seg_tile0, *seg_coff;
 };
 
 __device__ bool block_failed(int32_t *header, int *flag)
@@ -152,17 +153,14 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
         int tot;
         const int toff = tile_base + block_scan(ntile, lds, &tot);
         tile_base += tot;
-        for (int r = 0; r < ntile; ++r) {
-            A.tile_seg[toff + r] = s;
-            A.tile_row0[toff + r] = r * FK_TILE_TOKENS;
-        }
         const int nchunk = live ? (len + FK_GDN_CHUNK - 1) / FK_GDN_CHUNK : 0;
         const int coff = chunk_base + block_scan(nchunk, lds, &tot);
         chunk_base += tot;
-        if (in) A.seg_chunk0[s] = live ? coff : -1;
-        for (int r = 0; r < nchunk; ++r) {
-            A.chunk_seg[coff + r] = s;
-            A.chunk_row0[coff + r] = r * FK_GDN_CHUNK;
+        if (in) {
+            // the tile and chunk lists themselves are written by k_lists
+            A.seg_tile0[s] = toff;
+            A.seg_coff[s] = coff;
+            A.seg_chunk0[s] = live ? coff : -1;
         }
         const int kc = in ? A.kid_cnt[s] : 0;
         const int koff = kid_base + block_scan(kc, lds, &tot);
@@ -247,6 +245,74 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
     }
 }
 
+// the segment of list entry i: the last s with first[s] <= i (segments with
+// no entries share the next one's offset, so the last such s owns entry i)
+__device__ __forceinline__ int owner_of(const int32_t *__restrict__ first, int S, int i)
+{
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (first[mid] <= i) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Attention tiles and GDN chunks of every live segment, one thread per entry.
+__global__ void k_lists(int S, const int32_t *__restrict__ header, const int32_t *__restrict__ seg_tile0,
+                        const int32_t *__restrict__ seg_coff, int32_t *__restrict__ tile_seg,
+                        int32_t *__restrict__ tile_row0, int32_t *__restrict__ chunk_seg,
+                        int32_t *__restrict__ chunk_row0)
+{
+    if (header[H_STATUS] != FK_OK) return;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < header[H_NTILES]) {
+        const int s = owner_of(seg_tile0, S, i);
+        tile_seg[i] = s;
+        tile_row0[i] = (i - seg_tile0[s]) * FK_TILE_TOKENS;
+    }
+    if (i < header[H_NCHUNKS]) {
+        const int s = owner_of(seg_coff, S, i);
+        chunk_seg[i] = s;
+        chunk_row0[i] = (i - seg_coff[s]) * FK_GDN_CHUNK;
+    }
+}
+
+// Tiles by decreasing count of visible 64-key blocks (a bucket sort; order
+// within a bucket is whatever the atomics give).  Only the schedule of the
+// attention launch depends on it -- every tile computes the same way in any
+// order -- so the heaviest tiles start first and the launch ends evenly.
+constexpr int ORDER_BUCKETS = 2 * BUILD_THREADS;
+__global__ void __launch_bounds__(BUILD_THREADS)
+k_tile_order(const int32_t *__restrict__ header, const int32_t *__restrict__ tile_seg,
+             const int32_t *__restrict__ tile_row0, const int32_t *__restrict__ seg_pos0,
+             const int32_t *__restrict__ seg_len, int32_t *__restrict__ tile_order)
+{
+    __shared__ int cnt[ORDER_BUCKETS];
+    __shared__ int lds[32];
+    if (header[H_STATUS] != FK_OK) return;
+    const int n = header[H_NTILES];
+    for (int b = threadIdx.x; b < ORDER_BUCKETS; b += blockDim.x) cnt[b] = 0;
+    __syncthreads();
+    auto bucket = [&](int t) {
+        const int s = tile_seg[t], r0 = tile_row0[t];
+        const int keys = seg_pos0[s] + min(r0 + FK_TILE_TOKENS, seg_len[s]);
+        return min((keys + 63) / 64, ORDER_BUCKETS - 1);
+    };
+    for (int t = threadIdx.x; t < n; t += blockDim.x) atomicAdd(&cnt[bucket(t)], 1);
+    __syncthreads();
+    // offsets with the largest bucket first: thread j owns buckets B-1-2j, B-2-2j
+    const int b0 = ORDER_BUCKETS - 1 - 2 * threadIdx.x, b1 = b0 - 1;
+    int tot;
+    const int before = block_scan(cnt[b0] + cnt[b1], lds, &tot);
+    const int c0 = cnt[b0];
+    __syncthreads();
+    cnt[b0] = before;
+    cnt[b1] = before + c0;
+    __syncthreads();
+    for (int t = threadIdx.x; t < n; t += blockDim.x) tile_order[atomicAdd(&cnt[bucket(t)], 1)] = t;
+}
+
 // Phase 3 (pages): one block per segment checks the page ids the segment
 // uses, in parallel.  Runs only when the tree passed every other check.
 __global__ void k_check_pages(int S, const int32_t *__restrict__ seg_len, const int32_t *__restrict__ page_off,
@@ -325,6 +391,8 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
     A.chunk_seg = ws_at<int32_t>(ws, L.chunk_seg);
     A.chunk_row0 = ws_at<int32_t>(ws, L.chunk_row0);
     A.seg_chunk0 = ws_at<int32_t>(ws, L.seg_chunk0);
+    A.seg_tile0 = ws_at<int32_t>(ws, L.seg_tile0);
+    A.seg_coff = ws_at<int32_t>(ws, L.seg_coff);
     const int S = meta->S, T = meta->T;
     k_init<<<(S + 255) / 256 > 0 ? (S + 255) / 256 : 1, 256, 0, st>>>(A.header, A.seg_nrun, A.kid_cnt,
                                                                    A.kid_fill, S);
@@ -336,6 +404,15 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
     }
     k_build<<<1, BUILD_THREADS, 0, st>>>(A);
     if ((rc = launch_status())) return rc;
+    {
+        const int64_t n = L.tile_cap > L.chunk_cap ? L.tile_cap : L.chunk_cap;
+        k_lists<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(S, A.header, A.seg_tile0, A.seg_coff, A.tile_seg,
+                                                           A.tile_row0, A.chunk_seg, A.chunk_row0);
+        if ((rc = launch_status())) return rc;
+        k_tile_order<<<1, BUILD_THREADS, 0, st>>>(A.header, A.tile_seg, A.tile_row0, A.seg_pos0, A.seg_len,
+                                                 ws_at<int32_t>(ws, L.tile_order));
+        if ((rc = launch_status())) return rc;
+    }
     if (meta->seg_page_off) {
         k_check_pages<<<S, 256, 0, st>>>(S, A.seg_len, meta->seg_page_off, meta->seg_pages, meta->page_size,
                                          meta->n_pages, A.header);
