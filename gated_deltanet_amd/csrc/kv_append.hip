@@ -7,7 +7,8 @@
 // One block per (16-token tile = one page, kv head).  Keys keep their row
 // layout [slot][d]; values are stored transposed inside the page, [d][slot],
 // so the attention kernel's value operand reads keys contiguously.  Slots
-// after a segment's last token are zero-filled.
+// after a segment's last token are zero-filled.  bf16 at d = 128 (the
+// attention kernel's shape) has a 16-byte-access kernel of its own.
 #include <hip/hip_runtime.h>
 
 #include "fk_common.h"
@@ -48,6 +49,55 @@ __global__ void __launch_bounds__(256) k_kv_append(const E *__restrict__ k, cons
     }
 }
 
+// bf16, d = 128: 16-byte accesses on both sides.  Thread (r, c8) moves key
+// dims [8 c8, 8 c8 + 8) of slot r; values go through LDS ([slot][d], padded
+// rows) and leave as 8 consecutive slots of one dim row of the page.
+constexpr int KV_D = 128;
+constexpr int KV_VS = KV_D + 8;   // LDS row stride (bf16): slot rows on different banks
+
+__global__ void __launch_bounds__(256) k_kv_append_bf16(const uint16_t *__restrict__ k,
+                                                        const uint16_t *__restrict__ v, int Hkv,
+                                                        const int32_t *__restrict__ header,
+                                                        const int32_t *__restrict__ tile_seg,
+                                                        const int32_t *__restrict__ tile_row0,
+                                                        const int32_t *__restrict__ seg_start,
+                                                        const int32_t *__restrict__ seg_len,
+                                                        const int32_t *__restrict__ page_off,
+                                                        const int32_t *__restrict__ pages, uint16_t *__restrict__ kp,
+                                                        uint16_t *__restrict__ vp)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t vt[FK_TILE_TOKENS * KV_VS];
+    if (header[H_STATUS] != FK_OK) return;
+    const int tile = blockIdx.x, h = blockIdx.y;
+    if (tile >= header[H_NTILES]) return;
+    const int s = tile_seg[tile], row0 = tile_row0[tile];
+    const int count = min(FK_TILE_TOKENS, seg_len[s] - row0);
+    const int page = pages[page_off[s] + row0 / FK_TILE_TOKENS];
+    const int t0 = seg_start[s] + row0;
+    const size_t page_base = ((size_t)page * Hkv + h) * (size_t)FK_TILE_TOKENS * KV_D;
+    const int r = threadIdx.x >> 4, c8 = threadIdx.x & 15;
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (r < count) {
+        const size_t src = ((size_t)(t0 + r) * Hkv + h) * KV_D + c8 * 8;
+        kv = *reinterpret_cast<const uint4 *>(k + src);
+        vv = *reinterpret_cast<const uint4 *>(v + src);
+    }
+    *reinterpret_cast<uint4 *>(kp + page_base + r * KV_D + c8 * 8) = kv;
+    *reinterpret_cast<uint4 *>(vt + r * KV_VS + c8 * 8) = vv;
+    __syncthreads();
+    // dim x = tid / 2, slots [8 (tid % 2), +8)
+    const int x = threadIdx.x >> 1, r8 = (threadIdx.x & 1) * 8;
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = vt[(r8 + j) * KV_VS + x];
+    uint4 out;
+    out.x = e[0] | ((uint32_t)e[1] << 16);
+    out.y = e[2] | ((uint32_t)e[3] << 16);
+    out.z = e[4] | ((uint32_t)e[5] << 16);
+    out.w = e[6] | ((uint32_t)e[7] << 16);
+    *reinterpret_cast<uint4 *>(vp + page_base + x * FK_TILE_TOKENS + r8) = out;
+}
+
 }  // namespace fk
 
 using namespace fk;
@@ -61,7 +111,11 @@ int fk_launch_kv_append(const fk_tree_meta *meta, const void *k, const void *v, 
     const int32_t *hdr = ws_at<int32_t>(ws, L.header);
     const int32_t *ts = ws_at<int32_t>(ws, L.tile_seg), *tr = ws_at<int32_t>(ws, L.tile_row0);
     const int32_t *ss = ws_at<int32_t>(ws, L.seg_start), *sl = ws_at<int32_t>(ws, L.seg_len);
-    if (dtype == FK_BF16)
+    if (dtype == FK_BF16 && d == KV_D)
+        k_kv_append_bf16<<<grid, 256, 0, st>>>((const uint16_t *)k, (const uint16_t *)v, Hkv, hdr, ts, tr, ss, sl,
+                                               meta->seg_page_off, meta->seg_pages, (uint16_t *)k_pool,
+                                               (uint16_t *)v_pool);
+    else if (dtype == FK_BF16)
         k_kv_append<uint16_t><<<grid, 256, 0, st>>>((const uint16_t *)k, (const uint16_t *)v, Hkv, d, hdr, ts, tr,
                                                    ss, sl, meta->seg_page_off, meta->seg_pages,
                                                    (uint16_t *)k_pool, (uint16_t *)v_pool);
