@@ -594,19 +594,28 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
     if (w >= CONSUMERS) {
         const int part = w - CONSUMERS;
         StepRegs R;
-        int it = blockIdx.x, c = 0;
-        Item cur = item_at(A, it);
+        int c = 0;
+        Item cur = item_at(A, blockIdx.x);
+        // the item after the last one handed to a step, looked up one item
+        // ahead so its (dependent) scalar loads are long done when it is used
+        int la_it = blockIdx.x + stride;
+        Item la = la_it < n_items ? item_at(A, la_it) : cur;
+        auto take = [&](Item &I) {
+            I = la;
+            la_it += stride;
+            if (la_it < n_items) la = item_at(A, la_it);
+        };
         load_step(R, A, cur, 0, lane, part);
         write_step(buf[0], s0buf, R, cur, 0, lane, part);
         // step 1 into registers
-        int it1 = it, c1 = 1;
+        int c1 = 1;
         bool has1 = true;
+        Item nx1 = cur;
         if (c1 == cur.nch) {
-            it1 = it + stride;
             c1 = 0;
-            has1 = it1 < n_items;
+            has1 = la_it < n_items;
+            if (has1) take(nx1);
         }
-        Item nx1 = has1 ? (c1 == 0 ? item_at(A, it1) : cur) : cur;
         if (has1) load_step(R, A, nx1, c1, lane, part);
         __syncthreads();
         Item prev = cur;
@@ -615,19 +624,19 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
             // step j = (cur, c) is being consumed; step j+1 = (nx1, c1) sits in R
             if (c == 0) __syncthreads();   // consumers have read the entering state
             // step j+2
-            int it2 = it1, c2 = c1 + 1;
+            int c2 = c1 + 1;
             bool has2 = has1;
+            Item nx2 = nx1;
             if (has1 && c2 == nx1.nch) {
-                it2 = it1 + stride;
                 c2 = 0;
-                has2 = it2 < n_items;
+                has2 = la_it < n_items;
+                if (has2) take(nx2);
             }
             if (has1) {
                 ChunkBuf &Bn = buf[(j + 1) & 1];
                 if (pc >= 0) flush_out(Bn, A, prev, pc, lane, part);
                 write_step(Bn, s0buf, R, nx1, c1, lane, part);
             }
-            Item nx2 = has2 ? (c2 == 0 ? item_at(A, it2) : nx1) : nx1;
             if (has2) load_step(R, A, nx2, c2, lane, part);
             __syncthreads();   // step j consumed, step j+1 staged
             if (!has1) {
@@ -640,7 +649,6 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
             pc = c;
             cur = nx1;
             c = c1;
-            it1 = it2;
             c1 = c2;
             has1 = has2;
             nx1 = nx2;
