@@ -58,7 +58,7 @@ def _sample_rows(tree, rng, per_seg=3):
     return sel
 
 
-@pytest.mark.parametrize("which", [1, 2])
+@pytest.mark.parametrize("which", [1, 2, 3])
 def test_attention_bf16_configs_sampled(which):
     cfg, t = make_config(which)
     inp = draw_inputs(t, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
