@@ -41,7 +41,6 @@ constexpr int DK = 128, DV = 128;
 constexpr int DVS = 64;           // dv columns of one work-group (4 waves x 16)
 constexpr int KS = DK;            // LDS stride (bf16) of key/query rows (swizzled, unpadded)
 constexpr int TS = C + 8;         // LDS stride (bf16) of 64-wide rows written 16 B at a time (T, P)
-constexpr int AS = C + 4;         // LDS stride (fp32) of the prep matrix
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -120,15 +119,19 @@ __device__ __forceinline__ bf16x8 load_row8(const uint16_t *row, int ks, int G)
 // each.
 // ---------------------------------------------------------------------------
 constexpr int PREP_WAVES = 4;
+constexpr int TBS = C + 8;        // LDS stride (bf16) of the finished T rows
+constexpr int PREP_SCR = C * TBS * 2 > 4 * (16 * 16 + 16) * 4 ? C * TBS * 2 : 4 * (16 * 16 + 16) * 4;
 
-__global__ void __launch_bounds__(64 * PREP_WAVES)
+__global__ void __launch_bounds__(64 * PREP_WAVES, 3)
 k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ a,
            const float *__restrict__ b, int Hk, int Hv, const int32_t *__restrict__ header,
            const int32_t *__restrict__ chunk_seg, const int32_t *__restrict__ chunk_row0,
            const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_len,
            uint16_t *__restrict__ tmat, uint16_t *__restrict__ pmat)
 {
-    __shared__ __attribute__((aligned(16))) float am_all[PREP_WAVES][C * AS];
+    // per wave: the fp32 diagonal blocks of A (then of T), later the finished
+    // T as bf16 rows -- the two uses never overlap in time
+    __shared__ __attribute__((aligned(16))) char scr_all[PREP_WAVES][PREP_SCR];
     __shared__ float lsh_all[PREP_WAVES][C], esh_all[PREP_WAVES][C];
     if (header[H_STATUS] != FK_OK) return;
     const int nitems = header[H_NCHUNKS] * Hv;
@@ -137,7 +140,8 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     const int item = blockIdx.x * PREP_WAVES + w;
     const bool valid = item < nitems;   // every wave reaches every barrier
     const int c = valid ? item / Hv : 0, h = valid ? item % Hv : 0;
-    float *am = am_all[w], *lsh = lsh_all[w], *esh = esh_all[w];
+    float *am = reinterpret_cast<float *>(scr_all[w]), *lsh = lsh_all[w], *esh = esh_all[w];
+    uint16_t *tb = reinterpret_cast<uint16_t *>(scr_all[w]);
     const int s = chunk_seg[c], r0 = chunk_row0[c];
     const int n = valid ? min(C, seg_len[s] - r0) : 1;
     const size_t t0 = (size_t)seg_start[s] + r0;
@@ -272,12 +276,13 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     const f32x4 t31 = -mm(a3, mm(aop[5], t21, mm(aop[4], t11, z)), z);
     const f32x4 t30 = -mm(a3, mm(aop[5], t20, mm(aop[4], t10, mm(aop[3], t00, z))), z);
     __syncthreads();
-    // (4) T into am, row-major (the blocks above the diagonal are never read)
+    // (4) T as bf16 rows (the blocks above the diagonal are never read)
+    auto tbw = [&](int row, int col, float v_) { tb[row * TBS + col] = __builtin_bit_cast(uint16_t, (__bf16)v_); };
 #pragma unroll
-    for (int kr = 0; kr < 16; ++kr) am[(bb * 16 + kr) * AS + bb * 16 + cc] = x[kr];
+    for (int kr = 0; kr < 16; ++kr) tbw(bb * 16 + kr, bb * 16 + cc, x[kr]);
     auto put = [&](int bi, int bj, f32x4 t) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) am[(bi * 16 + G * 4 + r) * AS + bj * 16 + c16] = t[r];
+        for (int r = 0; r < 4; ++r) tbw(bi * 16 + G * 4 + r, bj * 16 + c16, t[r]);
     };
     put(1, 0, t10);
     put(2, 1, t21);
@@ -291,16 +296,15 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     uint16_t *dst = tmat + (((size_t)c * Hv + h) * C + lane) * C;
 #pragma unroll
     for (int j8 = 0; j8 < C / 8; ++j8) {
-        bf16x8 v;
         // stored elements [8 j8, 8 j8 + 8): positions 4G'..4G'+3 and
-        // 16+4G'..16+4G'+3 of block j8/4, G' = j8 % 4
+        // 16+4G'..16+4G'+3 of block j8/4, G' = j8 % 4 (each group of four
+        // lies in one 16-column block, above the diagonal block or not)
         const int base = (j8 >> 2) * 32 + 4 * (j8 & 3);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int col = base + (e < 4 ? e : 12 + e);
-            v[e] = (col >> 4) > (lane >> 4) ? (__bf16)0.f : (__bf16)am[lane * AS + col];
-        }
-        *reinterpret_cast<uint4 *>(dst + j8 * 8) = __builtin_bit_cast(uint4, v);
+        uint2 lo = *reinterpret_cast<const uint2 *>(tb + lane * TBS + base);
+        uint2 hi = *reinterpret_cast<const uint2 *>(tb + lane * TBS + base + 16);
+        if ((base >> 4) > (lane >> 4)) lo = make_uint2(0, 0);
+        if (((base + 16) >> 4) > (lane >> 4)) hi = make_uint2(0, 0);
+        *reinterpret_cast<uint4 *>(dst + j8 * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
 }
 
