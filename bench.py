@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=16,
                     help="requests of the workload in the CPU oracle sample")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of replays of the step captured as a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain copy of 256 MiB (gdn_checkpoint_save) before timing, so a "
                          "counter run can scale FETCH_SIZE / WRITE_SIZE to bytes")
@@ -384,6 +386,8 @@ def main():
         wl.step()
     torch.cuda.synchronize()
     assert wl.fk.fk_read_status(wl.ws) == 0, "tree build reported an error"
+    # eager pass: per-phase times with HIP events on the launch stream (these
+    # give the phases and the attention kernel's duration for the roofline)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -392,7 +396,22 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     phase = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # ms
-    ms_step = wall * 1e3 / args.steps
+    ms_eager = wall * 1e3 / args.steps
+    ms_step, mode = ms_eager, "eager launches"
+    if not args.eager:
+        # the same step recorded once as a HIP graph and replayed: the
+        # headline timing (no launch gaps between the step's kernels)
+        graph = wl.fk.StepGraph(wl.step, warmup=1)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        mode = "HIP graph replay"
+        assert wl.fk.fk_read_status(wl.ws) == 0, "tree build reported an error"
     attn_ms = float(phase[:, 2].mean())
     nvis = visible_pairs(tree)
     flops = 4.0 * sh.d * sh.Hq * nvis
@@ -414,6 +433,8 @@ def main():
         "config": {"workload": wl.cfg.name, "index": args.config, "requests": tree.n_requests,
                    "stream_tokens": tree.T, "branch_tokens": bt, "segments": tree.S,
                    "attn_heads": [sh.Hq, sh.Hkv, sh.d], "gdn_heads": [sh.Hk, sh.Hv, sh.dk, sh.dv]},
+        "execution": mode,
+        "ms_per_step_eager": ms_eager,
         "phases_ms": {("resume+tree_build" if args.config == 4 else "tree_build"): float(phase[:, 0].mean()),
                       "kv_append": float(phase[:, 1].mean()),
                       "fork_attention": attn_ms,

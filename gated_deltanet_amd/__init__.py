@@ -11,3 +11,4 @@ from .api import (TreeMeta, alloc_workspace, fk_read_status, fk_strerror,  # noq
                   fork_attn_forward, gdn_checkpoint_resume, gdn_checkpoint_save, gdn_fork_forward,
                   kv_append, make_tree_meta)
 from .rounds import RoundPlan, capacities, plan_round  # noqa: F401,E402
+from .graph import StepGraph  # noqa: F401,E402
