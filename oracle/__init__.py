@@ -57,6 +57,9 @@ def lib(path: Optional[str] = None) -> ctypes.CDLL:
                              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                              f64p, f64p, f64p, f64p, f64p, f64p, i32p, ctypes.c_int, u8p,
                              f64p, i32p, f64p, i64p]
+        L.or_conv.argtypes = [ctypes.c_int, ctypes.c_int, i32p, i32p, i32p, i32p, i64p,
+                              ctypes.c_int, ctypes.c_int, f64p, f64p, f64p, i32p, ctypes.c_int,
+                              f64p, f64p]
         _lib_cache[path] = L
     return _lib_cache[path]
 
@@ -159,3 +162,34 @@ def gdn(tok_seg, seg_parent, seg_fork, seg_cached_len, q, k, v, a, b, state_in=N
     if rc:
         raise OracleError(rc)
     return out[:T], st_out[:n_state_out], int(mism[0])
+
+
+def conv(tok_seg, seg_parent, seg_fork, seg_cached_len, hist_off, x, hx, w, seg_state_out=None,
+         n_state_out=0, libpath=None):
+    """Short causal convolution along every isolated path (fp64).
+
+    x [T, C] stream rows, hx [Nh, C] cached-history rows (``hist_off`` as for
+    attention), w [C, W] with w[:, i] applied to the i-th predecessor (i = 0:
+    the token itself).  Returns (y [T, C], window_out [n_state_out, W-1, C]):
+    the window of a segment with a ``seg_state_out`` slot is the input of the
+    last W-1 rows of its isolated sequence, oldest first, zero where that
+    sequence is shorter (Flide, section 3.2.2 and section 3.4).
+    """
+    tok_seg, seg_parent, seg_fork, seg_cached_len = map(_i32, (tok_seg, seg_parent, seg_fork, seg_cached_len))
+    x, w = _f64(x), _f64(w)
+    T, C = x.shape
+    W = w.shape[1]
+    hx = _f64(hx) if hx is not None and len(hx) else np.zeros((1, C))
+    hist_off = np.ascontiguousarray(hist_off, np.int64)
+    S = len(seg_parent)
+    sso = _i32(seg_state_out if seg_state_out is not None else np.full(S, -1))
+    y = np.full((max(T, 1), C), np.nan)
+    win = np.zeros((max(n_state_out, 1), max(W - 1, 1), C))
+    rc = lib(libpath).or_conv(T, S, _p(tok_seg, ctypes.c_int32), _p(seg_parent, ctypes.c_int32),
+                              _p(seg_fork, ctypes.c_int32), _p(seg_cached_len, ctypes.c_int32),
+                              _p(hist_off, ctypes.c_int64), C, W, _p(w, ctypes.c_double),
+                              _p(x, ctypes.c_double), _p(hx, ctypes.c_double), _p(sso, ctypes.c_int32),
+                              int(n_state_out), _p(y, ctypes.c_double), _p(win, ctypes.c_double))
+    if rc:
+        raise OracleError(rc)
+    return y[:T], win[:n_state_out, : W - 1]

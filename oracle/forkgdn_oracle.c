@@ -27,6 +27,14 @@
  *    with S in R^{dv x dk}, a zero initial state for a fresh root, and the
  *    saved fp32 state for a cached history (Flide, section 3.4).
  *
+ *  - Short causal convolution (Flide, section 3.2.2: in front of the Gated
+ *    DeltaNet rule a short causal convolution mixes each token with its few
+ *    predecessors, and the first tokens of a question see the last tokens
+ *    of its state; section 3.4: a checkpoint keeps the convolution window):
+ *    along the same isolated sequence, y_t[c] = sum_{i<W} w[c][i] x_{t-i}[c],
+ *    zero before the sequence's first row.  The pages give neither the width
+ *    nor an activation: here it is depthwise, linear, width W.
+ *
  * Two evaluation modes give identical bits (same operations, same order):
  *   mode 0 (literal): every live leaf's whole root-to-leaf path runs as its own
  *      sequence; tokens shared by several paths are compared bit for bit, and
@@ -464,6 +472,64 @@ int or_gdn(int T, int S, const int *tok_seg, const int *seg_parent, const int *s
     free(has_child); free(kid_off); free(kids);
 done:
     if (n_mismatch) *n_mismatch = mism;
+    free(seg_start); free(seg_len); free(seg_pos0); free(seg_depth); free(seg_root); free(tok_pos);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Short causal convolution                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* x [T, C] stream rows and hx [Nh, C] history rows (cached segment s owns
+ * history rows hist_off[s] ..); w [C, W] with w[c][0] on the token itself and
+ * w[c][i] on its i-th predecessor along P(s).  y [T, C].  For every segment
+ * with a state_out slot, window_out[slot] [W-1, C] holds the inputs of the
+ * last W-1 rows of P(s) (oldest first; zero where P(s) is shorter), i.e. the
+ * window a continuation of s reads. */
+int or_conv(int T, int S, const int *tok_seg, const int *seg_parent, const int *seg_fork,
+            const int *seg_cached_len, const int64_t *hist_off, int C, int W, const double *w,
+            const double *x, const double *hx, const int *seg_state_out, int n_state_out, double *y,
+            double *window_out)
+{
+    if (C <= 0 || W <= 0) return OR_E_ARG;
+    int *seg_start = malloc(S * sizeof(int)), *seg_len = malloc(S * sizeof(int));
+    int *seg_pos0 = malloc(S * sizeof(int)), *seg_depth = malloc(S * sizeof(int));
+    int *seg_root = malloc(S * sizeof(int)), *tok_pos = malloc((T + 1) * sizeof(int));
+    int rc = or_index(T, S, tok_seg, seg_parent, seg_fork, seg_cached_len, seg_start, seg_len,
+                      seg_pos0, seg_depth, seg_root, tok_pos);
+    if (rc) goto done;
+    for (int s = 0; s < S; ++s) {
+        if (seg_cached_len[s] > 0) continue;
+        path_t P;
+        build_path(s, seg_len[s], seg_parent, seg_fork, seg_cached_len, seg_start, seg_pos0, hist_off, &P);
+        /* planted: rows before the segment's own first row are not read */
+        const int first = MUT(9) ? seg_pos0[s] : 0;
+#pragma omp parallel for schedule(static)
+        for (int r = seg_pos0[s]; r < P.L; ++r) {
+            const int src = P.src[r];
+            for (int c = 0; c < C; ++c) {
+                double acc = 0.0;
+                for (int i = 0; i < W; ++i) {
+                    /* planted: predecessors taken one row too far back */
+                    const int rr = r - i - (MUT(10) && i > 0);
+                    if (rr < first) continue;
+                    acc += w[(size_t)c * W + i] * row_ptr(x, hx, P.src[rr], 1, C, 0)[c];
+                }
+                y[(size_t)src * C + c] = acc;
+            }
+        }
+        const int slot = seg_state_out ? seg_state_out[s] : -1;
+        if (slot >= 0 && slot < n_state_out && W > 1) {
+            for (int k = 0; k < W - 1; ++k) {
+                const int rr = P.L - (W - 1) + k;
+                for (int c = 0; c < C; ++c)
+                    window_out[((size_t)slot * (W - 1) + k) * C + c] =
+                        rr >= 0 ? row_ptr(x, hx, P.src[rr], 1, C, 0)[c] : 0.0;
+            }
+        }
+        free(P.src);
+    }
+done:
     free(seg_start); free(seg_len); free(seg_pos0); free(seg_depth); free(seg_root); free(tok_pos);
     return rc;
 }

@@ -484,4 +484,142 @@ def pin_chain_merge(libpath=None):
     assert np.array_equal(run_gdn(inp3, 1, libpath)[0], run_gdn(inp1, 1, libpath)[0])
 
 
+
+# --------------------------------------------------------------------------
+# short causal convolution in front of the GDN rule (Flide section 3.2.2:
+# the conv reads each token's predecessors through the tree index, so a
+# question's first tokens see the last tokens of its state; section 3.4:
+# a checkpoint keeps the conv window)
+# --------------------------------------------------------------------------
+
+def run_conv(tree, cin, libpath=None, seg_state_out=None, n_out=0, w=None):
+    ts, par, fk, cl = tree.arrays()
+    return oracle.conv(ts, par, fk, cl, cin.hist_off, cin.f64(), cin.f64(True),
+                       cin.w if w is None else w, seg_state_out=seg_state_out,
+                       n_state_out=n_out, libpath=libpath)
+
+
+def brute_predecessors(tree, depth):
+    """Per stream token, its 0..depth-th predecessors as ('s', token) /
+    ('h', history row) / None, by walking the tree one step at a time: the
+    previous token of the same segment, else the parent's token at index
+    fork - 1, else (fork 0) the predecessor of the parent's first token."""
+    segs = tree.segs
+    tok = token_table(tree)
+    start = {}
+    for x, (sg, i) in enumerate(tok):
+        start.setdefault(sg, x)
+    hist_off = {}
+    acc = 0
+    for i, sg in enumerate(segs):
+        if sg.cached:
+            hist_off[i] = acc
+            acc += sg.length
+
+    def row(sg, i):
+        return ("h", hist_off[sg] + i) if segs[sg].cached else ("s", start[sg] + i)
+
+    def prev(sg, i):
+        while True:
+            if i > 0:
+                return sg, i - 1
+            p = segs[sg].parent
+            if p < 0:
+                return None
+            sg, i = p, segs[sg].fork
+
+    out = []
+    for (sg, i) in tok:
+        chain, cur = [row(sg, i)], (sg, i)
+        for _ in range(depth):
+            cur = prev(*cur) if cur is not None else None
+            chain.append(row(*cur) if cur is not None else None)
+        out.append(chain)
+    return out
+
+
+def _conv_tree_inputs(rng, C=5, W=4, **kw):
+    t = random_tree(rng, **kw).flatten()
+    from workloads import draw_conv
+    return t, draw_conv(t, C, W, int(rng.integers(1 << 30)), "f32")
+
+
+def pin_conv_bruteforce(libpath=None, n=12):
+    """Random trees (cached roots, internal forks, fork 0): y_t = sum_i
+    w[:, i] x_{pred_i(t)} with predecessors found by walking the tree."""
+    rng = np.random.default_rng(23)
+    for _ in range(n):
+        W = int(rng.integers(1, 6))
+        t, cin = _conv_tree_inputs(rng, C=4, W=W, p_cached_root=0.4, p_internal_fork=0.4, max_len=9)
+        x, hx = cin.f64(), cin.f64(True)
+        y, _ = run_conv(t, cin, libpath)
+        ref = np.zeros_like(x)
+        for tt, chain in enumerate(brute_predecessors(t, W - 1)):
+            for i, src in enumerate(chain):
+                if src is not None:
+                    ref[tt] += cin.w[:, i] * (x[src[1]] if src[0] == "s" else hx[src[1]])
+        np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-13)
+
+
+def pin_conv_single_path_conv1d(libpath=None):
+    """A chain (with forks at segment ends) is one causal sequence: torch's
+    fp64 depthwise conv1d with W-1 zeros of left padding (weights flipped,
+    conv1d being a cross-correlation)."""
+    from workloads import draw_conv
+    for W in (1, 2, 4):
+        t = _chain_tree(0, [7, 5, 1, 6])
+        cin = draw_conv(t, 6, W, 5 + W, "f32")
+        y, _ = run_conv(t, cin, libpath)
+        x = torch.from_numpy(cin.f64().T.copy())[None]                      # [1, C, T]
+        wt = torch.from_numpy(cin.w.astype(np.float64)[:, ::-1].copy())[:, None, :]
+        ref = torch.nn.functional.conv1d(x, wt, padding=W - 1, groups=6)[0, :, : t.T].T.numpy()
+        np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-13)
+
+
+def pin_conv_closed_forms(libpath=None):
+    """w = e_0 is the identity; w = e_j shifts by j rows along each path
+    (zero before the path's first row)."""
+    t = build_tree([[(-1, 0, 6), (0, None, 3), (0, 2, 4), (2, 0, 2)]]).flatten()
+    from workloads import draw_conv
+    cin = draw_conv(t, 3, 4, 99, "f32")
+    x = cin.f64()
+    for j in range(4):
+        w = np.zeros((3, 4))
+        w[:, j] = 1.0
+        y, _ = run_conv(t, cin, libpath, w=w)
+        for tt, chain in enumerate(brute_predecessors(t, 3)):
+            src = chain[j]
+            np.testing.assert_array_equal(y[tt], x[src[1]] if src is not None else 0.0)
+
+
+def pin_conv_window_and_resume(libpath=None):
+    """The window saved at a segment end holds its path's last W-1 inputs;
+    a pass over a cached history equals the full pass (Flide section 3.4);
+    trunk rows do not depend on the branches."""
+    from workloads import draw_conv
+    W = 4
+    full = build_tree([[(-1, 0, 2), (0, None, 1), (1, None, 4), (1, 0, 3)]]).flatten()
+    cin = draw_conv(full, 5, W, 31, "f32")
+    y_full, win = run_conv(full, cin, libpath, seg_state_out=np.array([0, 1, 2, 3]), n_out=4)
+    x = cin.f64()
+    # trunk has 2 rows: window = [0, x0, x1]; trunk+1 = [x0, x1, x2]
+    np.testing.assert_array_equal(win[0], np.stack([np.zeros(5), x[0], x[1]]))
+    np.testing.assert_array_equal(win[1], x[0:3])
+    # the fork-0 child of segment 1 (3 rows) sees the trunk: [x1, xc0.., ]
+    c3 = [tt for tt, s in enumerate(full.tok_seg) if s == 3]
+    np.testing.assert_array_equal(win[3], np.stack([x[c3[0]], x[c3[1]], x[c3[2]]]))
+    # resume: the trunk and segment 1 as cached history rows
+    res = build_tree([[(-1, 0, 2, True), (0, None, 1, True), (1, None, 4)]]).flatten()
+    cr = draw_conv(res, 5, W, 31, "f32")
+    y_r, _ = run_conv(res, cr, libpath)
+    tail = [tt for tt, s in enumerate(full.tok_seg) if s == 2]
+    assert np.array_equal(y_full[tail], y_r)
+    # trunk rows alone
+    tr = build_tree([[(-1, 0, 2), (0, None, 1)]]).flatten()
+    ct = draw_conv(tr, 5, W, 31, "f32")
+    y_t, _ = run_conv(tr, ct, libpath)
+    head = [tt for tt, s in enumerate(full.tok_seg) if s < 2]
+    assert np.array_equal(y_full[head], y_t)
+
+
 ALL_PINS = [v for k, v in list(globals().items()) if k.startswith("pin_")]

@@ -8,6 +8,8 @@ and check that the pin suite catches every one of them:
  6 softmax scale dropped
  7 output read from the state before the update (S_{t-1} q_t)
  8 positions off by one below a fork
+ 9 conv: rows before the segment's own first row not read (window lost at a fork)
+10 conv: predecessors taken one row too far back
 """
 import pytest
 
@@ -15,7 +17,7 @@ import oracle
 from tests import pins
 
 
-@pytest.mark.parametrize("mutant", range(1, 9))
+@pytest.mark.parametrize("mutant", range(1, 11))
 def test_mutant_is_caught(mutant):
     path = oracle.build(force=False, extra_flags=(f"-DORACLE_MUTANT={mutant}",))
     caught = []

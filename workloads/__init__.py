@@ -7,5 +7,5 @@ no attention, no recurrence), so both the fp64 oracle and the HIP path can
 consume the same inputs without sharing any code of the method.
 """
 from .trees import Seg, Tree, build_tree, subtree_path, random_tree  # noqa: F401
-from .tensors import draw_inputs, to_bf16, Inputs  # noqa: F401
+from .tensors import draw_inputs, draw_conv, to_bf16, Inputs, ConvInputs  # noqa: F401
 from .configs import CONFIGS, make_config  # noqa: F401

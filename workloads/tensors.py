@@ -152,3 +152,58 @@ def draw_inputs(tree: Tree, shapes: Shapes, seed: int, dtype: str = "bf16",
         hx = [vals[i][name] for i in cached_ids]
         hist[name] = np.concatenate(hx, 0) if hx else empty
     return Inputs(dtype=dtype, shapes=shapes, tree=tree, raw=raw, hist=hist, hist_off=hist_off)
+
+
+@dataclass
+class ConvInputs:
+    """Inputs of the short causal convolution in front of the GDN rule.
+
+    ``x`` [T, C] stream rows and ``hx`` [Nh, C] cached-history rows (raw
+    storage, laid out like ``Inputs``), ``w`` [C, W] fp32 weights.
+    """
+    dtype: str
+    C: int
+    W: int
+    x: np.ndarray
+    hx: np.ndarray
+    hist_off: np.ndarray
+    w: np.ndarray
+
+    def f64(self, hist: bool = False) -> np.ndarray:
+        a = self.hx if hist else self.x
+        return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def draw_conv(tree: Tree, C: int, W: int, seed: int, dtype: str = "bf16",
+              request_streams: Optional[List[int]] = None) -> ConvInputs:
+    """Conv inputs of every segment, x ~ N(0, 1), and weights w ~ N(0, 1/W).
+
+    Each segment draws from ``SeedSequence(seed, spawn_key=(request, key, 1))``
+    -- a stream of its own, so the tensors of ``draw_inputs`` are unchanged
+    and a branch again gets the same values alone or in any mixture.  The
+    weights come from ``spawn_key=(2**30 + 1,)``.
+    """
+    assert tree.tok_seg is not None, "flatten() the tree first"
+    assert dtype in ("bf16", "f32")
+    rnd = to_bf16 if dtype == "bf16" else to_f32
+    vals = []
+    for s in tree.segs:
+        r = request_streams[s.request] if request_streams is not None else s.request
+        ss = np.random.SeedSequence(int(seed), spawn_key=(int(r), int(s.key), 1))
+        gen = np.random.Generator(np.random.PCG64(ss))
+        vals.append(rnd(gen.standard_normal((s.length, C), dtype=np.float32)))
+    wgen = np.random.Generator(np.random.PCG64(np.random.SeedSequence(int(seed), spawn_key=(2**30 + 1,))))
+    w = to_f32(wgen.standard_normal((C, W)) / np.sqrt(W))
+    store = np.uint16 if dtype == "bf16" else np.float32
+    live = [vals[i] for i in tree.order]
+    cached_ids = [i for i, s in enumerate(tree.segs) if s.cached]
+    hist_off = np.zeros(tree.S + 1, np.int64)
+    acc = 0
+    for i in range(tree.S):
+        hist_off[i] = acc
+        if tree.segs[i].cached:
+            acc += tree.segs[i].length
+    hist_off[tree.S] = acc
+    x = np.concatenate(live, 0) if live else np.zeros((0, C), store)
+    hx = np.concatenate([vals[i] for i in cached_ids], 0) if cached_ids else np.zeros((0, C), store)
+    return ConvInputs(dtype=dtype, C=C, W=W, x=x, hx=hx, hist_off=hist_off, w=w)
