@@ -294,6 +294,47 @@ class ResumeWorkload:
             ev[4].record()
 
 
+def measure_conv(wl, steps: int, W: int = 4):
+    """The forked short convolution in front of the GDN layer (a row beyond
+    the step), timed on its own over the same round: channels = the q|k|v
+    projections of the GDN layer (2 Hk dk + Hv dv), width 4, bf16, windows
+    read for cached histories and written for every state_out slot.
+    HBM-bound: algorithmic bytes = the input read once + the output written
+    once (+ windows)."""
+    torch, fk, sh, meta = wl.torch, wl.fk, wl.sh, wl.meta
+    C = 2 * sh.Hk * sh.dk + sh.Hv * sh.dv
+    T = wl.tree.T
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.cfg.seed * 7 + 3)
+    x = torch.empty((T, C), dtype=torch.bfloat16, device="cuda")
+    for t0 in range(0, T, 1 << 14):
+        x[t0:t0 + (1 << 14)] = torch.randn((min(1 << 14, T - t0), C), generator=g, device="cuda")
+    w = (torch.rand((C, W), generator=g, device="cuda") * 2 - 1) / W ** 0.5
+    win_in = torch.randn((max(meta.n_state_in, 1), W - 1, C), generator=g, device="cuda").to(torch.bfloat16)
+    win_out = torch.empty((max(meta.n_state_out, 1), W - 1, C), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+
+    def run():
+        fk.gdn_conv_forward(meta, x, w, wl.ws, window_in=win_in if meta.n_state_in else None,
+                            window_out=win_out if meta.n_state_out else None, out=y)
+
+    run()
+    torch.cuda.synchronize()
+    assert fk.fk_read_status(wl.ws) == 0, "conv reported an error"
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = 2.0 * T * C * 2 + (meta.n_state_in + meta.n_state_out) * (W - 1) * C * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "forked short conv (bf16)", "channels": C, "width": W, "ms": ms, "bound": "hbm",
+            "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "algorithmic_bytes": nbytes}
+
+
 def cpu_baseline(index: int, n_req: int):
     """The fp64 oracle, as it stands, on the first ``n_req`` requests of the
     same workload: every root-to-leaf path as its own isolated sequence
@@ -444,6 +485,7 @@ def main():
                      "traffic": measured_traffic(args.config), "algorithmic_flops": flops,
                      "visible_pairs_per_head": nvis},
     }
+    line["next_rows"] = {"conv": measure_conv(wl, args.steps)}
     if not getattr(wl, "gdn_ok", True):
         line["incomplete"] = "gdn_fork_forward unsupported for this dtype in this build: step lacks GDN"
         line["phases_ms"]["gdn"] = None

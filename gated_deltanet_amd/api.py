@@ -176,6 +176,20 @@ def gdn_fork_forward(meta: TreeMeta, q, k, v, a, b, ws, state_in=None, state_out
     return out
 
 
+def gdn_conv_forward(meta: TreeMeta, x, w, ws, window_in=None, window_out=None, out=None,
+                     stream=None) -> torch.Tensor:
+    """x [T, C], w [C, W] float; windows [slots, W-1, C] in x's dtype."""
+    T, C = x.shape
+    W = w.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    m = meta.c()
+    check("gdn_conv_forward", _lib.load().gdn_conv_forward(
+        ctypes.byref(m), _ptr(x), _DT[x.dtype], C, W, _ptr(w), _ptr(window_in), _ptr(window_out),
+        _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
 def gdn_checkpoint_save(state_out, slot, ckpt, count=1, stream=None):
     """Copy state_out[slot:slot+count] into ckpt ([count, Hv, dv, dk] or [Hv, dv, dk])."""
     n, Hv, dv, dk = state_out.shape

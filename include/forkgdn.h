@@ -214,6 +214,40 @@ int gdn_fork_forward(const fk_tree_meta *meta, const void *q, const void *k, con
                      const float *state_in, float *state_out, void *out, void *ws, size_t ws_bytes,
                      fk_stream_t stream);
 
+/* Widest short convolution of gdn_conv_forward. */
+#define FK_CONV_MAX_W 8
+
+/*
+ * gdn_conv_forward -- the short causal convolution in front of the Gated
+ * DeltaNet rule, forked through the tree (Flide section 3.2.2: it mixes each
+ * token with its few predecessors, read through the same kind of index as
+ * the recurrent state, so the first tokens of a question see the last tokens
+ * of the state it forks from; section 3.4: a checkpoint keeps the
+ * convolution window).  Depthwise and linear, width W:
+ *   y[t, c] = sum_{i < W} w[c, i] * x[p_i(t), c]
+ * where p_0(t) = t and p_i(t) is the i-th predecessor of t along t's
+ * isolated root-to-leaf sequence (a zero row before the sequence's first
+ * row).  Accumulates in float32, i = 0 .. W-1 in order; bf16 output rounds to
+ * nearest even.  (Any activation after the convolution is pointwise and is
+ * the caller's.)
+ * x, y: [T, C] in `dtype`, 16-byte aligned; w: [C, W] float.
+ * window_in: [n_state_in, W-1, C] in `dtype`: the saved window of every
+ * cached segment, in the segment's state_in slot (seg_state_in) -- the
+ * inputs of the last W-1 rows of the cached sequence, oldest first, zero rows
+ * where it is shorter.  May be NULL if no live segment has a cached parent
+ * (otherwise the status word records FK_E_STATE_SLOT).
+ * window_out: [n_state_out, W-1, C] in `dtype`: every live segment with
+ * seg_state_out >= 0 writes its own window there (same definition), which a
+ * later round reads back as window_in.  Required when n_state_out > 0 and
+ * W > 1; both windows are ignored when W == 1.
+ * Needs fk_tree_build of the same round in `ws` (any GDN sizes).
+ * Supported: FK_BF16 with C % 8 == 0, FK_F32 with C % 4 == 0; 1 <= W <=
+ * FK_CONV_MAX_W.
+ */
+int gdn_conv_forward(const fk_tree_meta *meta, const void *x, int dtype, int C, int W, const float *w,
+                     const void *window_in, void *window_out, void *y, void *ws, size_t ws_bytes,
+                     fk_stream_t stream);
+
 /*
  * gdn_checkpoint_save -- copy the float32 recurrent states of `count`
  * consecutive slots state_out[slot .. slot+count) ([count, Hv, dv, dk])

@@ -32,6 +32,10 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert L.fk_abi_version() == 1
+    # the Python binding carries the same names (host-only helpers aside)
+    for n in names:
+        if n not in ("fk_abi_version",):
+            assert callable(getattr(fk, n, None)), f"binding lacks {n}"
 
 
 def test_strerror_covers_codes():

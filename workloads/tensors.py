@@ -176,7 +176,10 @@ class ConvInputs:
 
 def draw_conv(tree: Tree, C: int, W: int, seed: int, dtype: str = "bf16",
               request_streams: Optional[List[int]] = None) -> ConvInputs:
-    """Conv inputs of every segment, x ~ N(0, 1), and weights w ~ N(0, 1/W).
+    """Conv inputs of every segment, x ~ N(0, 1), and weights w ~ U(-1/sqrt(W),
+    1/sqrt(W)) (a depthwise convolution's usual initialisation, fan-in W), so
+    outputs stay within the range where a bf16 output's rounding error is
+    below the bf16 bar.
 
     Each segment draws from ``SeedSequence(seed, spawn_key=(request, key, 1))``
     -- a stream of its own, so the tensors of ``draw_inputs`` are unchanged
@@ -193,7 +196,7 @@ def draw_conv(tree: Tree, C: int, W: int, seed: int, dtype: str = "bf16",
         gen = np.random.Generator(np.random.PCG64(ss))
         vals.append(rnd(gen.standard_normal((s.length, C), dtype=np.float32)))
     wgen = np.random.Generator(np.random.PCG64(np.random.SeedSequence(int(seed), spawn_key=(2**30 + 1,))))
-    w = to_f32(wgen.standard_normal((C, W)) / np.sqrt(W))
+    w = to_f32(wgen.uniform(-1.0, 1.0, (C, W)) / np.sqrt(W))
     store = np.uint16 if dtype == "bf16" else np.float32
     live = [vals[i] for i in tree.order]
     cached_ids = [i for i, s in enumerate(tree.segs) if s.cached]
