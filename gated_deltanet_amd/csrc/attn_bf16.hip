@@ -13,8 +13,14 @@
 // Per block and wave, with v_mfma_f32_32x32x16_bf16 (fp32 accumulate):
 //   S^T[64 keys x 32 rows] = K_blk[64 x 128] . Q^T[128 x 32]      16 MFMAs
 //   online softmax on S^T in registers (row = lane % 32; the two halves of
-//   the wave hold disjoint keys of the same row; max via one lane swap)
+//   the wave hold disjoint keys of the same row; max via one permlane32 swap)
 //   O^T[128 x 32] += V^T[128 x 64] . P^T[64 x 32]                 16 MFMAs
+// The two 32-key MFMA chains (and the four 32-dim output chains) are
+// interleaved, with LDS operand reads issued LOOKAHEAD instructions ahead.
+// A row's reference maximum moves only when a block exceeds it by more than
+// 2^RESCALE_LOG2 (the exponentials stay bounded by that factor), so most
+// blocks skip the rescale of the output accumulators; the decision is per
+// row, and a row that does not move multiplies by exactly 1.
 // The accumulator layout of S^T is reused directly as the P^T operand: the
 // K rows are loaded under a fixed permutation (bits 2 and 3 of the row index
 // swapped) so that each lane's accumulator registers hold 8 consecutive keys
@@ -41,6 +47,23 @@ constexpr int K_LDS = BN * K_STRIDE;
 constexpr int V_LDS = D * V_STRIDE;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// max / sum of a lane's value and that of lane (lane ^ 32): one permlane32
+// swap gives every lane both values (the two halves of a wave hold disjoint
+// keys of the same rows); the sum is commutative, so both halves agree
+__device__ __forceinline__ float pair_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+constexpr float RESCALE_LOG2 = 8.f;
+constexpr int LOOKAHEAD = 6;   // LDS operand reads issued ahead of the MFMAs
 
 __device__ __forceinline__ uint4 pack8(const float *x)
 {
@@ -180,41 +203,59 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
         const bool own = cur.own;
         const uint16_t *kl = k_lds[buf], *vl = v_lds[buf];
         // S^T = K . Q^T
-        f32x16 sacc[2];
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+        {
+            const uint16_t *krow = kl + prow * K_STRIDE + half * 8;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            sacc[mt] = f32x16{};
-            const uint16_t *krow = kl + (mt * 32 + prow) * K_STRIDE + half * 8;
+            for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + ks * 16));
-                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
+                for (int mt = 0; mt < 2; ++mt) {
+                    const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + mt * 32 * K_STRIDE + ks * 16));
+                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
+                }
+            // keep LOOKAHEAD operand reads in flight ahead of the MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);
+#pragma unroll
+            for (int j = 0; j < 16 - LOOKAHEAD; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, LOOKAHEAD, 0);
         }
-        // mask: register r of tile mt holds key 32*mt + 16*(r/8) + 8*half + r%8.
-        // The row max is taken on raw scores (scale > 0), then one FMA per
-        // score gives the exponent in log2 units.
-        const bool full = own ? (key0 + BN - 1 <= row0) : (key0 + BN <= count);
-        float mloc = -INFINITY;
-        if (full) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[mt][r]);
-        } else {
+        // mask: register r of tile mt holds key 32*mt + 16*(r/8) + 8*half + r%8
+        // of the block.  Only blocks that cross the diagonal or the end of an
+        // ancestor's visible prefix are masked, in place.
+        // last visible key offset within the block, minus this half's 8 * half
+        const int lim = (own ? tok - key0 : count - 1 - key0) - half * 8;
+        if (!(own ? (key0 + BN - 1 <= row0) : (key0 + BN <= count))) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + mt * 32 + (r / 8) * 16 + half * 8 + (r % 8);
-                    const bool vis = own ? key <= tok : key < count;
-                    if (!vis) sacc[mt][r] = -INFINITY;
-                    mloc = fmaxf(mloc, sacc[mt][r]);
+                    sacc[mt][r] = (mt * 32 + (r / 8) * 16 + (r % 8)) <= lim ? sacc[mt][r] : -INFINITY;
                 }
         }
-        const float mrow = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * scale_log2e;
-        const float mnew = fmaxf(m, mrow);
-        float psum = 0.f;
+        // row max on raw scores (scale > 0); the two wave halves hold disjoint
+        // keys of the same row and swap maxima with one permlane
+        float mloc = sacc[0][0];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = (mt == 0 ? 1 : 0); r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[mt][r]);
+        const float mrow = pair_max(mloc) * scale_log2e;
+        // lazy rescale: a row moves its reference max only when the block's
+        // max exceeds it by more than RESCALE_LOG2 (the exponents then stay
+        // <= 2^RESCALE_LOG2); rows that do not move multiply by exactly 1
+        const bool need = mrow > m + RESCALE_LOG2;
+        if (__any(need)) {   // wave-uniform branch
+            const float mnew = need ? mrow : m;
+            const float corr = __builtin_amdgcn_exp2f(m - mnew);
+            l *= corr;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) o[i] *= corr;
+            m = mnew;
+        }
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
         bf16x8 pf[4];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -223,29 +264,22 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
                 float pv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][hh * 8 + e], scale_log2e, -mnew));
-                    psum += pv[e];
+                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][hh * 8 + e], scale_log2e, -m));
+                    ps[e & 3] += pv[e];
                 }
                 pf[mt * 2 + hh] = as_bf16x8(pack8(pv));
             }
-        // rescale only when some row's max moved (a factor of exactly 1 is a no-op)
-        if (__any(mnew != m)) {   // wave-uniform branch
-            const float corr = __builtin_amdgcn_exp2f(m - mnew);
-            l *= corr;
-#pragma unroll
-            for (int i = 0; i < D / 32; ++i) o[i] *= corr;
-        }
-        l += psum;
-        m = mnew;
+        l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
         // O^T += V^T . P^T ; k-step kk covers keys 16*kk + [0, 16)
+        {
+            const uint16_t *vrow = vl + n * V_STRIDE + half * 8;
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) {
-            const uint16_t *vrow = vl + (i * 32 + n) * V_STRIDE + half * 8;
+            for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + kk * 16));
-                o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[i], 0, 0, 0);
-            }
+                for (int i = 0; i < D / 32; ++i) {
+                    const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + i * 32 * V_STRIDE + kk * 16));
+                    o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[i], 0, 0, 0);
+                }
         }
         if (!more) break;
         store_block(k_lds[buf ^ 1], v_lds[buf ^ 1], R);
@@ -253,7 +287,7 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
         __syncthreads();   // next block staged; this buffer free for reuse
     }
     // epilogue: the row's sum is split over the two halves of the wave
-    const float lsum = l + __shfl_xor(l, 32, 64);
+    const float lsum = pair_sum(l);
     if (!row_valid) return;
     const float inv = 1.f / lsum;
     uint16_t *orow = out + (t_glob * Hq + h) * D;
