@@ -52,7 +52,7 @@ def lib(path: Optional[str] = None) -> ctypes.CDLL:
                                i32p, i32p, i32p, i32p, i32p, i32p]
         L.or_attention.argtypes = [ctypes.c_int, ctypes.c_int, i32p, i32p, i32p, i32p, i64p,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
-                                   f64p, f64p, f64p, f64p, f64p, ctypes.c_int, u8p, u8p, f64p, i64p]
+                                   ctypes.c_int, ctypes.c_int, f64p, f64p, f64p, f64p, f64p, ctypes.c_int, u8p, u8p, f64p, i64p]
         L.or_gdn.argtypes = [ctypes.c_int, ctypes.c_int, i32p, i32p, i32p, i32p,
                              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                              f64p, f64p, f64p, f64p, f64p, f64p, i32p, ctypes.c_int, u8p,
@@ -100,9 +100,16 @@ def index(tok_seg, seg_parent, seg_fork, seg_cached_len, libpath=None):
                 tok_pos=tok_pos[:T])
 
 
+RULE_CAUSAL, RULE_WINDOW, RULE_TWO_WAY = 0, 1, 2
+
+
 def attention(tok_seg, seg_parent, seg_fork, seg_cached_len, hist_off, q, k, v, hk, hv,
-              scale, mode=1, tok_sel=None, head_sel=None, libpath=None):
-    """Causal GQA softmax attention along every isolated path (fp64).
+              scale, mode=1, tok_sel=None, head_sel=None, libpath=None, rule=RULE_CAUSAL, window=0):
+    """GQA softmax attention along every isolated path (fp64).
+
+    ``rule``: RULE_CAUSAL (t_y <= t_x), RULE_WINDOW (also t_x - t_y <
+    ``window``), RULE_TWO_WAY (the whole own segment and each ancestor's
+    visible prefix; mode 1 only).
 
     q [T,Hq,d], k/v [T,Hkv,d] stream rows; hk/hv [Nh,Hkv,d] cached-history
     rows, ``hist_off[s]`` = first history row of cached segment s.  Returns
@@ -122,7 +129,7 @@ def attention(tok_seg, seg_parent, seg_fork, seg_cached_len, hist_off, q, k, v, 
     rc = lib(libpath).or_attention(T, len(seg_parent), _p(tok_seg, ctypes.c_int32),
                                    _p(seg_parent, ctypes.c_int32), _p(seg_fork, ctypes.c_int32),
                                    _p(seg_cached_len, ctypes.c_int32), _p(hist_off, ctypes.c_int64),
-                                   Hq, Hkv, d, float(scale), _p(q, ctypes.c_double),
+                                   Hq, Hkv, d, float(scale), int(rule), int(window), _p(q, ctypes.c_double),
                                    _p(k, ctypes.c_double), _p(v, ctypes.c_double),
                                    _p(hk, ctypes.c_double), _p(hv, ctypes.c_double), int(mode),
                                    _p(ts, ctypes.c_uint8), _p(hs, ctypes.c_uint8),

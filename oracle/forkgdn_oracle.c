@@ -21,6 +21,13 @@
  *    fp64.  This is Proposition 3.1 taken literally: each branch equals its
  *    own isolated forward pass.
  *
+ *    Two more visibility rules of the same section: a sliding-window layer
+ *    of width W also requires t_x - t_y < W (positions along P(s) are the
+ *    standalone positions, so the same keys are chosen); a two-way layer
+ *    (a model that reads each block both ways, Flide appendix H) drops
+ *    t_y <= t_x, so a row sees every token of its own segment and each
+ *    ancestor's visible prefix -- the state still never reads a question.
+ *
  *  - Gated DeltaNet (Flide, section 3.2.2, Eq. 4): along the same isolated
  *    sequence, token by token,
  *        S_t = a_t * S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  o_t = S_t q_t
@@ -186,15 +193,27 @@ static const double *row_ptr(const double *stream, const double *hist, int src, 
 /* Attention                                                                 */
 /* ------------------------------------------------------------------------ */
 
-/* causal softmax attention of row `r` of path P for q head h (kv head g). */
+#define OR_RULE_CAUSAL 0   /* t_y <= t_x                                   */
+#define OR_RULE_WINDOW 1   /* t_y <= t_x and t_x - t_y < window             */
+#define OR_RULE_TWO_WAY 2  /* every row of the own segment; ancestors' prefixes */
+
+/* softmax attention of row `r` of path P for q head h (kv head g) under the
+   visibility rule; the row index along P is the standalone position. */
 static void attend_row(const path_t *P, int r, int h, int g, int Hq, int Hkv, int d, double scale,
-                       const double *q, const double *k, const double *v,
+                       int rule, int window, const double *q, const double *k, const double *v,
                        const double *hk, const double *hv, double *o, double *sc)
 {
     const double *qr = row_ptr(q, NULL, P->src[r], Hq, d, h);
     double m = -INFINITY;
-    int last = r - MUT(1);                      /* keys 0..r are visible (t_y <= t_x) */
-    for (int j = 0; j <= last; ++j) {
+    int first = 0, last = r - MUT(1);           /* keys 0..r are visible (t_y <= t_x) */
+    if (rule == OR_RULE_WINDOW) {
+        first = r - window + 1 - MUT(11);       /* t_x - t_y < window */
+        if (first < 0) first = 0;
+    } else if (rule == OR_RULE_TWO_WAY) {
+        last = P->L - 1 - MUT(12);              /* the whole own segment (P ends with it) */
+    }
+    for (int j = 0; j < first; ++j) sc[j] = -INFINITY;
+    for (int j = first; j <= last; ++j) {
         const double *kj = row_ptr(k, hk, P->src[j], Hkv, d, g);
         double s = 0.0;
         for (int x = 0; x < d; ++x) s += qr[x] * kj[x];
@@ -204,7 +223,7 @@ static void attend_row(const path_t *P, int r, int h, int g, int Hq, int Hkv, in
     }
     double den = 0.0;
     for (int x = 0; x < d; ++x) o[x] = 0.0;
-    for (int j = 0; j <= last; ++j) {
+    for (int j = first; j <= last; ++j) {
         double p = exp(sc[j] - m);
         den += p;
         const double *vj = row_ptr(v, hv, P->src[j], Hkv, d, g);
@@ -215,11 +234,15 @@ static void attend_row(const path_t *P, int r, int h, int g, int Hq, int Hkv, in
 
 int or_attention(int T, int S, const int *tok_seg, const int *seg_parent, const int *seg_fork,
                  const int *seg_cached_len, const int64_t *hist_off, int Hq, int Hkv, int d,
-                 double scale, const double *q, const double *k, const double *v,
+                 double scale, int rule, int window, const double *q, const double *k, const double *v,
                  const double *hk, const double *hv, int mode, const uint8_t *tok_sel,
                  const uint8_t *head_sel, double *out, int64_t *n_mismatch)
 {
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0) return OR_E_ARG;
+    if (rule < OR_RULE_CAUSAL || rule > OR_RULE_TWO_WAY || (rule == OR_RULE_WINDOW && window < 1)) return OR_E_ARG;
+    /* under the two-way rule an ancestor's rows see their whole segment, which
+       a leaf path holds only up to the fork: rows are evaluated over P(s) */
+    if (rule == OR_RULE_TWO_WAY && mode == 0) return OR_E_ARG;
     int *seg_start = malloc(S * sizeof(int)), *seg_len = malloc(S * sizeof(int));
     int *seg_pos0 = malloc(S * sizeof(int)), *seg_depth = malloc(S * sizeof(int));
     int *seg_root = malloc(S * sizeof(int)), *tok_pos = malloc((T + 1) * sizeof(int));
@@ -263,10 +286,10 @@ int or_attention(int T, int S, const int *tok_seg, const int *seg_parent, const 
                     if (src < 0) continue;                       /* history row: no output */
                     if (head_sel && !head_sel[h]) continue;
                     if (mode == 1 && tok_sel && !tok_sel[src]) continue;
-                    double *sc = malloc((size_t)(r + 1) * sizeof(double));
+                    double *sc = malloc((size_t)P.L * sizeof(double));   /* keys 0 .. P.L-1 at most */
                     double *o = malloc((size_t)d * sizeof(double));
                     int g = MUT(3) ? h % Hkv : h / G;       /* contiguous GQA groups */
-                    attend_row(&P, r, h, g, Hq, Hkv, d, scale, q, k, v, hk, hv, o, sc);
+                    attend_row(&P, r, h, g, Hq, Hkv, d, scale, rule, window, q, k, v, hk, hv, o, sc);
                     double *dst = out + ((size_t)src * Hq + h) * d;
                     if (done_tok[src]) {
                         if (memcmp(dst, o, (size_t)d * sizeof(double)) != 0) local_mism++;

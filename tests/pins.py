@@ -486,6 +486,111 @@ def pin_chain_merge(libpath=None):
 
 
 # --------------------------------------------------------------------------
+# visibility variants (Flide section 3.2.1: a sliding-window layer adds
+# t_x - t_y < W; appendix H: models that read each block both ways fork
+# their state under the same rule without t_y <= t_x)
+# --------------------------------------------------------------------------
+
+def brute_positions(tree):
+    """pos0 of every segment by summing forks up the parent chain."""
+    pos0 = []
+    for i in range(tree.S):
+        acc, j = 0, i
+        while tree.segs[j].parent >= 0:
+            acc += tree.segs[j].fork
+            j = tree.segs[j].parent
+        pos0.append(acc)
+    return pos0
+
+
+def brute_visible_rule(tree, rule, window=0):
+    """Dense visibility (history rows first, then the stream) under a rule:
+    causal / causal and t_x - t_y < window / two-way (every token of the own
+    segment, each ancestor's first `fork` tokens)."""
+    segs = tree.segs
+    tok = token_table(tree)
+    pos0 = brute_positions(tree)
+    hist_rows = []
+    for i, sg in enumerate(segs):
+        if sg.cached:
+            hist_rows += [(i, j) for j in range(sg.length)]
+    keys = hist_rows + tok
+    M = np.zeros((len(tok), len(keys)), bool)
+    for x, (sx, ix) in enumerate(tok):
+        limit = {sx: segs[sx].length if rule == oracle.RULE_TWO_WAY else ix + 1}
+        c = sx
+        while segs[c].parent >= 0:
+            limit[segs[c].parent] = segs[c].fork
+            c = segs[c].parent
+        for y, (sy, iy) in enumerate(keys):
+            vis = sy in limit and iy < limit[sy]
+            if rule == oracle.RULE_WINDOW:
+                vis = vis and (pos0[sx] + ix) - (pos0[sy] + iy) < window
+            M[x, y] = vis
+    return M
+
+
+def _rule_run(inp, rule, window, libpath):
+    ts, par, fk, cl = inp.tree.arrays()
+    return oracle.attention(ts, par, fk, cl, inp.hist_off, inp.f64("aq"), inp.f64("ak"), inp.f64("av"),
+                            inp.f64("ak", True), inp.f64("av", True), 1 / np.sqrt(inp.shapes.d), mode=1,
+                            rule=rule, window=window, libpath=libpath)[0]
+
+
+def pin_window_masked_sdpa(libpath=None, n=8):
+    """Sliding window on random trees (cached roots, internal forks): SDPA
+    with the brute-force mask (ancestry, t_y <= t_x and t_x - t_y < W)."""
+    rng = np.random.default_rng(31)
+    for i in range(n):
+        t = random_tree(rng, p_cached_root=0.4, p_internal_fork=0.4).flatten()
+        inp = small_inputs(t, Hq=4, Hkv=2, d=16, seed=int(rng.integers(1 << 30)))
+        W = [1, 2, 5, 17, 40][i % 5]
+        o = _rule_run(inp, oracle.RULE_WINDOW, W, libpath)
+        M = brute_visible_rule(t, oracle.RULE_WINDOW, W)
+        keys = np.concatenate([inp.f64("ak", True), inp.f64("ak")], 0)
+        vals = np.concatenate([inp.f64("av", True), inp.f64("av")], 0)
+        ref = sdpa_masked(inp.f64("aq"), keys, vals, M, 1 / 4.0)
+        np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def pin_two_way_masked_sdpa(libpath=None, n=8):
+    """Two-way rule on random trees: SDPA with the brute-force block mask."""
+    rng = np.random.default_rng(37)
+    for _ in range(n):
+        t = random_tree(rng, p_cached_root=0.4, p_internal_fork=0.4).flatten()
+        inp = small_inputs(t, Hq=4, Hkv=2, d=16, seed=int(rng.integers(1 << 30)))
+        o = _rule_run(inp, oracle.RULE_TWO_WAY, 0, libpath)
+        M = brute_visible_rule(t, oracle.RULE_TWO_WAY)
+        keys = np.concatenate([inp.f64("ak", True), inp.f64("ak")], 0)
+        vals = np.concatenate([inp.f64("av", True), inp.f64("av")], 0)
+        ref = sdpa_masked(inp.f64("aq"), keys, vals, M, 1 / 4.0)
+        np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def pin_rule_special_cases(libpath=None):
+    """One segment read both ways is plain non-causal SDPA (no mask); a
+    window of 1 gives o = v of the token itself; a window longer than every
+    path is the causal rule, bit for bit."""
+    t = build_tree([[(-1, 0, 19)]]).flatten()
+    inp = small_inputs(t, Hq=4, Hkv=2, d=12)
+    o = _rule_run(inp, oracle.RULE_TWO_WAY, 0, libpath)
+    q, k, v = inp.f64("aq"), inp.f64("ak"), inp.f64("av")
+    qt = torch.from_numpy(q).permute(1, 0, 2)
+    kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(2, 0).contiguous()
+    vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(2, 0).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=1 / np.sqrt(12))
+    np.testing.assert_allclose(o, ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    t = _two_branch().flatten()
+    inp = small_inputs(t)
+    o1 = _rule_run(inp, oracle.RULE_WINDOW, 1, libpath)
+    v = inp.f64("av")
+    for h in range(inp.shapes.Hq):
+        np.testing.assert_allclose(o1[:, h], v[:, h // 2], rtol=0, atol=1e-15)
+    big = _rule_run(inp, oracle.RULE_WINDOW, 10_000, libpath)
+    assert np.array_equal(big, _rule_run(inp, oracle.RULE_CAUSAL, 0, libpath))
+
+
+# --------------------------------------------------------------------------
 # short causal convolution in front of the GDN rule (Flide section 3.2.2:
 # the conv reads each token's predecessors through the tree index, so a
 # question's first tokens see the last tokens of its state; section 3.4:

@@ -10,6 +10,8 @@ and check that the pin suite catches every one of them:
  8 positions off by one below a fork
  9 conv: rows before the segment's own first row not read (window lost at a fork)
 10 conv: predecessors taken one row too far back
+11 sliding window one key too wide (t_x - t_y <= W)
+12 two-way rule misses the last row of the own segment
 """
 import pytest
 
@@ -17,7 +19,7 @@ import oracle
 from tests import pins
 
 
-@pytest.mark.parametrize("mutant", range(1, 11))
+@pytest.mark.parametrize("mutant", range(1, 13))
 def test_mutant_is_caught(mutant):
     path = oracle.build(force=False, extra_flags=(f"-DORACLE_MUTANT={mutant}",))
     caught = []
