@@ -163,6 +163,22 @@ def fork_attn_forward(meta: TreeMeta, q, k, v, k_pool, v_pool, ws, scale=None, o
     return out
 
 
+def fork_attn_forward_rule(meta: TreeMeta, q, k, v, k_pool, v_pool, ws, rule, window=0, scale=None,
+                           out=None, stream=None) -> torch.Tensor:
+    """Attention under a visibility rule: _lib.FK_RULE_CAUSAL / FK_RULE_WINDOW
+    (with ``window``) / FK_RULE_TWO_WAY.  k = v = None: K/V already paged."""
+    T, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    scale = float(scale if scale is not None else d ** -0.5)
+    m = meta.c()
+    check("fork_attn_forward_rule", _lib.load().fork_attn_forward_rule(
+        ctypes.byref(m), _ptr(q), _ptr(k), _ptr(v), _DT[q.dtype], Hq, Hkv, d, scale, int(rule), int(window),
+        _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
 def gdn_fork_forward(meta: TreeMeta, q, k, v, a, b, ws, state_in=None, state_out=None, out=None,
                      stream=None) -> torch.Tensor:
     T, Hk, dk = q.shape

@@ -4,7 +4,9 @@
 // A query token x of segment s sees, in this fixed order:
 //   the first fork(a_{i+1}) tokens of every strict ancestor a_i on its chain
 //   (a cached history is simply a cached ancestor), then its own segment up
-//   to and including x.
+//   to and including x.  Under the sliding-window rule it also needs
+//   t_x - t_y < W; under the two-way rule it sees its whole own segment
+//   (Flide section 3.2.1 and appendix H).
 // Keys are visited in blocks anchored at the start of every range, so the
 // order of a row's reductions depends only on its own chain -- never on the
 // other segments of the round (Flide section 3.5).
@@ -21,8 +23,8 @@ int fk_launch_kv_append(const fk_tree_meta *meta, const void *k, const void *v, 
                         void *k_pool, void *v_pool, const void *ws, hipStream_t st);
 int fk_check_kv_args(const fk_tree_meta *meta, const void *k, const void *v, int dtype, int Hkv, int d,
                      void *k_pool, void *v_pool, const void *ws);
-int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv, float scale, const void *k_pool,
-                        const void *v_pool, void *out, const void *ws, hipStream_t st);
+int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv, float scale, int rule, int window,
+                        const void *k_pool, const void *v_pool, void *out, const void *ws, hipStream_t st);
 
 namespace fk {
 
@@ -41,6 +43,7 @@ __device__ __forceinline__ float wave_sum(float x)
 // grid: (tile capacity, Hq); block: one wave.  d <= 128: lane owns dims
 // lane and lane + 64.
 __global__ void __launch_bounds__(64) k_attn_f32(const float *__restrict__ q, int Hq, int Hkv, int d, float scale,
+                                                 int rule, int window, const int32_t *__restrict__ seg_pos0,
                                                  const float *__restrict__ kp, const float *__restrict__ vp,
                                                  float *__restrict__ out, const int32_t *__restrict__ header,
                                                  const int32_t *__restrict__ tile_seg,
@@ -68,12 +71,16 @@ __global__ void __launch_bounds__(64) k_attn_f32(const float *__restrict__ q, in
         float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
         for (int lvl = 0; lvl <= depth; ++lvl) {
             const int a = anc[lvl];
-            const int count = lvl < depth ? seg_fork[anc[lvl + 1]] : row0 + r + 1;
+            const int count = lvl < depth ? seg_fork[anc[lvl + 1]]
+                                          : (rule == FK_RULE_TWO_WAY ? seg_len[s] : row0 + r + 1);
+            // window: keys before klo are outside it; chunks stay anchored at 0
+            const int klo = rule == FK_RULE_WINDOW ? max(0, seg_pos0[s] + row0 + r - seg_pos0[a] - window + 1) : 0;
+            if (klo >= count) continue;
             const int *pl = pages + page_off[a];
-            for (int c0 = 0; c0 < count; c0 += 64) {
+            for (int c0 = (klo / 64) * 64; c0 < count; c0 += 64) {
                 const int key = c0 + lane;
                 float sc = -INFINITY;
-                if (key < count) {
+                if (key < count && key >= klo) {
                     const float *kr = kp + ((size_t)pl[key / FK_TILE_TOKENS] * Hkv + g) * page_elems +
                                       (size_t)(key % FK_TILE_TOKENS) * d;
                     float acc = 0.f;
@@ -83,7 +90,7 @@ __global__ void __launch_bounds__(64) k_attn_f32(const float *__restrict__ q, in
                 const float mc = wave_max(sc);
                 const float mn = fmaxf(m, mc);
                 const float corr = expf(m - mn);          // 0 on the first chunk (m = -inf)
-                const float p = key < count ? expf(sc - mn) : 0.f;
+                const float p = (key < count && key >= klo) ? expf(sc - mn) : 0.f;
                 l = l * corr + wave_sum(p);
                 o0 *= corr;
                 o1 *= corr;
@@ -109,10 +116,13 @@ __global__ void __launch_bounds__(64) k_attn_f32(const float *__restrict__ q, in
 
 using namespace fk;
 
-extern "C" int fork_attn_forward(const fk_tree_meta *meta, const void *q, const void *k, const void *v, int dtype,
-                                 int Hq, int Hkv, int d, float scale, void *k_pool, void *v_pool, void *out,
-                                 void *ws, size_t ws_bytes, fk_stream_t stream)
+extern "C" int fork_attn_forward_rule(const fk_tree_meta *meta, const void *q, const void *k, const void *v,
+                                      int dtype, int Hq, int Hkv, int d, float scale, int rule, int window,
+                                      void *k_pool, void *v_pool, void *out, void *ws, size_t ws_bytes,
+                                      fk_stream_t stream)
 {
+    if (rule != FK_RULE_CAUSAL && rule != FK_RULE_WINDOW && rule != FK_RULE_TWO_WAY) return FK_E_INVALID_ARG;
+    if (rule == FK_RULE_WINDOW && window < 1) return FK_E_INVALID_ARG;
     // k == v == NULL: this round's keys/values are already in the pool
     const bool append = k || v;
     int rc = fk_check_kv_args(meta, append ? k : q, append ? v : q, dtype, Hkv, d, k_pool, v_pool, ws);
@@ -129,13 +139,23 @@ extern "C" int fork_attn_forward(const fk_tree_meta *meta, const void *q, const 
         rc = fk_launch_kv_append(meta, k, v, dtype, Hkv, d, k_pool, v_pool, ws, st);
         if (rc) return rc;
     }
-    if (dtype == FK_BF16) return fk_launch_attn_bf16(meta, q, Hq, Hkv, scale, k_pool, v_pool, out, ws, st);
+    if (dtype == FK_BF16)
+        return fk_launch_attn_bf16(meta, q, Hq, Hkv, scale, rule, window, k_pool, v_pool, out, ws, st);
     dim3 grid((unsigned)L.tile_cap, (unsigned)Hq);
-    k_attn_f32<<<grid, 64, 0, st>>>((const float *)q, Hq, Hkv, d, scale, (const float *)k_pool,
+    k_attn_f32<<<grid, 64, 0, st>>>((const float *)q, Hq, Hkv, d, scale, rule, window, ws_at<int32_t>(ws, L.seg_pos0),
+                                    (const float *)k_pool,
                                     (const float *)v_pool, (float *)out, ws_at<int32_t>(ws, L.header),
                                     ws_at<int32_t>(ws, L.tile_seg), ws_at<int32_t>(ws, L.tile_row0),
                                     ws_at<int32_t>(ws, L.seg_start), ws_at<int32_t>(ws, L.seg_len),
                                     ws_at<int32_t>(ws, L.seg_depth), ws_at<int32_t>(ws, L.seg_anc), meta->seg_fork,
                                     meta->seg_page_off, meta->seg_pages);
     return launch_status();
+}
+
+extern "C" int fork_attn_forward(const fk_tree_meta *meta, const void *q, const void *k, const void *v, int dtype,
+                                 int Hq, int Hkv, int d, float scale, void *k_pool, void *v_pool, void *out,
+                                 void *ws, size_t ws_bytes, fk_stream_t stream)
+{
+    return fork_attn_forward_rule(meta, q, k, v, dtype, Hq, Hkv, d, scale, FK_RULE_CAUSAL, 0, k_pool, v_pool, out,
+                                  ws, ws_bytes, stream);
 }

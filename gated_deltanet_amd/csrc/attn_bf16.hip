@@ -109,39 +109,69 @@ __device__ __forceinline__ void store_block(uint16_t *__restrict__ ks, uint16_t 
     }
 }
 
+// Visibility rules (Flide section 3.2.1): causal (t_y <= t_x); a sliding
+// window of width W that also requires t_x - t_y < W; and two-way, where a row
+// sees every token of its own segment (models that read each block both
+// ways, Flide appendix H) -- ancestors always show their first `fork` tokens.
+enum Rule { CAUSAL = FK_RULE_CAUSAL, WINDOW = FK_RULE_WINDOW, TWO_WAY = FK_RULE_TWO_WAY };
+
+// What a tile's key walk needs to know about its chain.
+struct TileCtx {
+    int depth, row0, len, pos0, window;
+    const int *anc;
+    const int32_t *seg_fork, *seg_pos0, *page_off, *pages;
+};
+
 // Walks a tile's key blocks in order: each ancestor's visible prefix, then the
-// own segment; blocks are anchored at the start of every range.
+// own segment; blocks are anchored at the start of every range.  Under the
+// window rule a range starts at the first block that holds a key inside the
+// window of the tile's first row (earlier blocks are invisible to every row
+// of the tile and are skipped whole).
 struct BlockCursor {
-    int lvl, key0, count;
+    int lvl, key0, count, pdiff;   // pdiff = pos0(tile segment) - pos0(range segment)
     bool own;
     const int32_t *plist;
 };
 
-__device__ __forceinline__ void cursor_level(BlockCursor &c, int lvl, int depth, const int *anc,
-                                             const int32_t *seg_fork, const int32_t *page_off,
-                                             const int32_t *pages, int row0, int len)
+template <int RULE>
+__device__ __forceinline__ void cursor_level(BlockCursor &c, int lvl, const TileCtx &t)
 {
     c.lvl = lvl;
+    c.own = lvl == t.depth;
+    c.count = c.own ? (RULE == TWO_WAY ? t.len : min(t.row0 + FK_TILE_TOKENS, t.len)) : t.seg_fork[t.anc[lvl + 1]];
+    c.plist = t.pages + t.page_off[t.anc[lvl]];
+    c.pdiff = t.pos0 - t.seg_pos0[t.anc[lvl]];
     c.key0 = 0;
-    c.own = lvl == depth;
-    c.count = c.own ? min(row0 + FK_TILE_TOKENS, len) : seg_fork[anc[lvl + 1]];
-    c.plist = pages + page_off[anc[lvl]];
+    if (RULE == WINDOW) {
+        const int lo = c.pdiff + t.row0 - t.window + 1;   // first key the tile's first row sees
+        if (lo > 0) c.key0 = (lo / BN) * BN;
+    }
 }
 
-// move to the next non-empty block; returns false past the last one
-__device__ __forceinline__ bool cursor_next(BlockCursor &c, int depth, const int *anc, const int32_t *seg_fork,
-                                            const int32_t *page_off, const int32_t *pages, int row0, int len)
+// first block at or after level `lvl` (a range whose blocks all lie outside
+// the window, or an empty range, is passed over); the own range is never empty
+template <int RULE>
+__device__ __forceinline__ void cursor_settle(BlockCursor &c, const TileCtx &t)
+{
+    while (c.key0 >= c.count && c.lvl < t.depth) cursor_level<RULE>(c, c.lvl + 1, t);
+}
+
+// move to the next block; returns false past the last one
+template <int RULE>
+__device__ __forceinline__ bool cursor_next(BlockCursor &c, const TileCtx &t)
 {
     c.key0 += BN;
-    while (c.key0 >= c.count) {
-        if (c.lvl >= depth) return false;
-        cursor_level(c, c.lvl + 1, depth, anc, seg_fork, page_off, pages, row0, len);
-    }
+    if (c.key0 < c.count) return true;
+    if (c.lvl >= t.depth) return false;
+    cursor_level<RULE>(c, c.lvl + 1, t);
+    cursor_settle<RULE>(c, t);
     return true;
 }
 
+template <int RULE>
 __global__ void __launch_bounds__(THREADS, 2)
-k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, const uint16_t *__restrict__ kp,
+k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, int window,
+            const int32_t *__restrict__ seg_pos0, const uint16_t *__restrict__ kp,
             const uint16_t *__restrict__ vp, uint16_t *__restrict__ out, const int32_t *__restrict__ header,
             const int32_t *__restrict__ tile_seg, const int32_t *__restrict__ tile_row0,
             const int32_t *__restrict__ tile_order, const int32_t *__restrict__ seg_start,
@@ -177,29 +207,42 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     f32x16 o[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
-    float m = -INFINITY, l = 0.f;
+    // a finite floor for the reference max: under the window rule a row may
+    // meet a block with no visible key before its first visible one
+    float m = -1e30f, l = 0.f;
 
     const int depth = seg_depth[s];
     const int *anc = seg_anc + s * FK_MAX_DEPTH;
     // MFMA row m of a 32-key tile holds key perm(m): bits 2 and 3 swapped
     const int prow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
+    TileCtx tc;
+    tc.depth = depth;
+    tc.row0 = row0;
+    tc.len = len;
+    tc.pos0 = seg_pos0[s];
+    tc.window = window;
+    tc.anc = anc;
+    tc.seg_fork = seg_fork;
+    tc.seg_pos0 = seg_pos0;
+    tc.page_off = page_off;
+    tc.pages = pages;
     BlockCursor cur;
-    cursor_level(cur, 0, depth, anc, seg_fork, page_off, pages, row0, len);
-    while (cur.count == 0) cursor_level(cur, cur.lvl + 1, depth, anc, seg_fork, page_off, pages, row0, len);
+    cursor_level<RULE>(cur, 0, tc);
+    cursor_settle<RULE>(cur, tc);
     {
         BlockRegs R;
-        load_block(R, kp, vp, cur.plist, 0, cur.count, g, Hkv);
+        load_block(R, kp, vp, cur.plist, cur.key0, cur.count, g, Hkv);
         store_block(k_lds[0], v_lds[0], R);
     }
     __syncthreads();
     for (int buf = 0;; buf ^= 1) {
         // prefetch the next block into registers while this one is computed
         BlockCursor nxt = cur;
-        const bool more = cursor_next(nxt, depth, anc, seg_fork, page_off, pages, row0, len);
+        const bool more = cursor_next<RULE>(nxt, tc);
         BlockRegs R;
         if (more) load_block(R, kp, vp, nxt.plist, nxt.key0, nxt.count, g, Hkv);
-        const int key0 = cur.key0, count = cur.count;
+        const int key0 = cur.key0, count = cur.count, pdiff = cur.pdiff;
         const bool own = cur.own;
         const uint16_t *kl = k_lds[buf], *vl = v_lds[buf];
         // S^T = K . Q^T
@@ -223,16 +266,23 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             __builtin_amdgcn_sched_group_barrier(0x008, LOOKAHEAD, 0);
         }
         // mask: register r of tile mt holds key 32*mt + 16*(r/8) + 8*half + r%8
-        // of the block.  Only blocks that cross the diagonal or the end of an
-        // ancestor's visible prefix are masked, in place.
-        // last visible key offset within the block, minus this half's 8 * half
-        const int lim = (own ? tok - key0 : count - 1 - key0) - half * 8;
-        if (!(own ? (key0 + BN - 1 <= row0) : (key0 + BN <= count))) {
+        // of the block.  Only blocks that cross the diagonal, the end of a
+        // visible range or the window's edge are masked, in place.  hi / lo:
+        // last / first visible key offset within the block, minus 8 * half.
+        const bool causal_own = own && RULE != TWO_WAY;
+        const int hi = (causal_own ? tok - key0 : count - 1 - key0) - half * 8;
+        const int lo = (RULE == WINDOW ? pdiff + tok - window + 1 - key0 : 0) - half * 8;
+        const bool full = (causal_own ? (key0 + BN - 1 <= row0) : (key0 + BN <= count)) &&
+                          (RULE != WINDOW || key0 >= pdiff + row0 + FK_TILE_TOKENS - window);
+        if (!full) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    sacc[mt][r] = (mt * 32 + (r / 8) * 16 + (r % 8)) <= lim ? sacc[mt][r] : -INFINITY;
+                    const int koff = mt * 32 + (r / 8) * 16 + (r % 8);
+                    bool vis = koff <= hi;
+                    if (RULE == WINDOW) vis = vis && koff >= lo;
+                    sacc[mt][r] = vis ? sacc[mt][r] : -INFINITY;
                 }
         }
         // row max on raw scores (scale > 0); the two wave halves hold disjoint
@@ -311,17 +361,30 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
 
 using namespace fk;
 
-int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv, float scale, const void *k_pool,
-                        const void *v_pool, void *out, const void *ws, hipStream_t st)
+template <int RULE>
+static void launch_rule(const fk_tree_meta *meta, const WsLayout &L, const void *q, int Hq, int Hkv, float scale,
+                        int window, const void *k_pool, const void *v_pool, void *out, const void *ws, hipStream_t st)
 {
-    const WsLayout L = ws_layout(*meta, 0, 0, 0);
     dim3 grid((unsigned)(L.tile_cap * Hkv));
-    attn::k_attn_bf16<<<grid, attn::THREADS, 0, st>>>(
-        (const uint16_t *)q, Hq, Hkv, scale * 1.4426950408889634f, (const uint16_t *)k_pool,
+    attn::k_attn_bf16<RULE><<<grid, attn::THREADS, 0, st>>>(
+        (const uint16_t *)q, Hq, Hkv, scale * 1.4426950408889634f, window, ws_at<int32_t>(ws, L.seg_pos0),
+        (const uint16_t *)k_pool,
         (const uint16_t *)v_pool, (uint16_t *)out, ws_at<int32_t>(ws, L.header), ws_at<int32_t>(ws, L.tile_seg),
         ws_at<int32_t>(ws, L.tile_row0), ws_at<int32_t>(ws, L.tile_order), ws_at<int32_t>(ws, L.seg_start),
         ws_at<int32_t>(ws, L.seg_len),
         ws_at<int32_t>(ws, L.seg_depth), ws_at<int32_t>(ws, L.seg_anc), meta->seg_fork, meta->seg_page_off,
         meta->seg_pages);
+}
+
+int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv, float scale, int rule, int window,
+                        const void *k_pool, const void *v_pool, void *out, const void *ws, hipStream_t st)
+{
+    const WsLayout L = ws_layout(*meta, 0, 0, 0);
+    if (rule == FK_RULE_WINDOW)
+        launch_rule<attn::WINDOW>(meta, L, q, Hq, Hkv, scale, window, k_pool, v_pool, out, ws, st);
+    else if (rule == FK_RULE_TWO_WAY)
+        launch_rule<attn::TWO_WAY>(meta, L, q, Hq, Hkv, scale, window, k_pool, v_pool, out, ws, st);
+    else
+        launch_rule<attn::CAUSAL>(meta, L, q, Hq, Hkv, scale, window, k_pool, v_pool, out, ws, st);
     return launch_status();
 }

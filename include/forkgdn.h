@@ -193,6 +193,31 @@ int fork_attn_forward(const fk_tree_meta *meta, const void *q, const void *k, co
                       int dtype, int Hq, int Hkv, int d, float scale, void *k_pool, void *v_pool,
                       void *out, void *ws, size_t ws_bytes, fk_stream_t stream);
 
+/* Visibility rules of fork_attn_forward_rule (Flide section 3.2.1). */
+enum fk_attn_rule {
+    FK_RULE_CAUSAL = 0,  /* t_y <= t_x (fork_attn_forward)                          */
+    FK_RULE_WINDOW = 1,  /* t_y <= t_x and t_x - t_y < window (a sliding-window layer) */
+    FK_RULE_TWO_WAY = 2  /* every token of the own segment (models that read each
+                            block both ways, Flide appendix H)                       */
+};
+
+/*
+ * fork_attn_forward_rule -- fork_attn_forward under another visibility rule
+ * of the same section, on the same tile table.  FK_RULE_WINDOW: a
+ * sliding-window layer of width `window` (>= 1) also requires t_x - t_y <
+ * window, with positions continuing from the fork, so a branch selects the
+ * same keys as its standalone sequence; key blocks wholly outside every
+ * row's window are skipped.  FK_RULE_TWO_WAY: t_y <= t_x is dropped, so a
+ * row sees every token of its own segment and each ancestor's first `fork`
+ * tokens -- the state still never reads a question, so questions still fork
+ * it (Flide appendix H).  `window` is ignored unless rule == FK_RULE_WINDOW.
+ * Other arguments, layouts, support and errors as fork_attn_forward;
+ * FK_E_INVALID_ARG for an unknown rule or window < 1.
+ */
+int fork_attn_forward_rule(const fk_tree_meta *meta, const void *q, const void *k, const void *v, int dtype,
+                           int Hq, int Hkv, int d, float scale, int rule, int window, void *k_pool, void *v_pool,
+                           void *out, void *ws, size_t ws_bytes, fk_stream_t stream);
+
 /*
  * gdn_fork_forward -- forked Gated DeltaNet (Flide section 3.2.2, Eq. 4, and
  * its two-call scheme generalised to one launch per tree level).  A fresh

@@ -100,9 +100,12 @@ class GpuRound:
     def status(self):
         return fk.fk_read_status(self.ws)
 
-    def attention(self, scale=None):
-        return fk.fork_attn_forward(self.meta, self.x["aq"], self.x["ak"], self.x["av"], self.k_pool,
-                                    self.v_pool, self.ws, scale=scale)
+    def attention(self, scale=None, rule=None, window=0):
+        if rule is None:
+            return fk.fork_attn_forward(self.meta, self.x["aq"], self.x["ak"], self.x["av"], self.k_pool,
+                                        self.v_pool, self.ws, scale=scale)
+        return fk.fork_attn_forward_rule(self.meta, self.x["aq"], self.x["ak"], self.x["av"], self.k_pool,
+                                         self.v_pool, self.ws, rule, window, scale=scale)
 
     def gdn(self):
         return fk.gdn_fork_forward(self.meta, self.x["gq"], self.x["gk"], self.x["gv"], self.x["ga"],
@@ -110,12 +113,13 @@ class GpuRound:
                                    state_out=self.state_out if self.n_out else None)
 
 
-def oracle_attention(inp, mode=1, tok_sel=None, scale=None):
+def oracle_attention(inp, mode=1, tok_sel=None, scale=None, rule=0, window=0, head_sel=None):
     ts, par, fk_, cl = inp.tree.arrays()
     d = inp.shapes.d
     return oracle.attention(ts, par, fk_, cl, inp.hist_off, inp.f64("aq"), inp.f64("ak"), inp.f64("av"),
                             inp.f64("ak", True), inp.f64("av", True),
-                            scale if scale is not None else 1 / np.sqrt(d), mode=mode, tok_sel=tok_sel)[0]
+                            scale if scale is not None else 1 / np.sqrt(d), mode=mode, tok_sel=tok_sel,
+                            head_sel=head_sel, rule=rule, window=window)[0]
 
 
 def oracle_gdn(inp, state_in=None, mode=1, head_sel=None):
