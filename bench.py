@@ -335,6 +335,54 @@ def measure_conv(wl, steps: int, W: int = 4):
             "algorithmic_bytes": nbytes}
 
 
+def rule_pairs(tree, rule: int, window: int = 0) -> int:
+    """Visible (query, key) pairs per head under a visibility rule: a row at
+    position p sees min(p + 1, W) keys in a window of width W (its path holds
+    every earlier position), and pos0 + len keys when its segment is read
+    both ways."""
+    pos0 = np.zeros(tree.S, np.int64)
+    for i in range(tree.S):
+        acc, j = 0, i
+        while tree.segs[j].parent >= 0:
+            acc += tree.segs[j].fork
+            j = tree.segs[j].parent
+        pos0[i] = acc
+    tot = 0
+    for i, sg in enumerate(tree.segs):
+        if sg.cached:
+            continue
+        pos = pos0[i] + np.arange(sg.length, dtype=np.int64)
+        tot += int(np.minimum(pos + 1, window).sum()) if rule == 1 else int(sg.length * (pos0[i] + sg.length))
+    return tot
+
+
+def measure_rule(wl, steps: int, rule: int, window: int = 0):
+    """ForkAttention under another visibility rule (a row beyond the step),
+    over the same round with its keys/values already paged; MFMA roofline on
+    the rule's own visible pairs."""
+    torch, fk, sh = wl.torch, wl.fk, wl.sh
+    out = torch.empty_like(wl.attn_out)
+
+    def run():
+        fk.fork_attn_forward_rule(wl.meta, wl.x["aq"], None, None, wl.k_pool, wl.v_pool, wl.ws, rule, window,
+                                  scale=wl.scale, out=out)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 4.0 * sh.d * sh.Hq * rule_pairs(wl.tree, rule, window)
+    tf = flops / (ms * 1e-3) / 1e12
+    name = f"sliding-window attention (W={window})" if rule == 1 else "two-way attention"
+    return {"kernel": name + " (bf16 MFMA)", "ms": ms, "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "algorithmic_flops": flops}
+
+
 def cpu_baseline(index: int, n_req: int):
     """The fp64 oracle, as it stands, on the first ``n_req`` requests of the
     same workload: every root-to-leaf path as its own isolated sequence
@@ -485,7 +533,9 @@ def main():
                      "traffic": measured_traffic(args.config), "algorithmic_flops": flops,
                      "visible_pairs_per_head": nvis},
     }
-    line["next_rows"] = {"conv": measure_conv(wl, args.steps)}
+    line["next_rows"] = {"conv": measure_conv(wl, args.steps),
+                         "window_attention": measure_rule(wl, args.steps, 1, 1024),
+                         "two_way_attention": measure_rule(wl, args.steps, 2)}
     if not getattr(wl, "gdn_ok", True):
         line["incomplete"] = "gdn_fork_forward unsupported for this dtype in this build: step lacks GDN"
         line["phases_ms"]["gdn"] = None

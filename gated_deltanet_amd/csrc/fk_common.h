@@ -49,6 +49,7 @@ struct WsLayout {
     size_t seg_tile0;     // int32[S]  first tile of each segment (non-decreasing)
     size_t seg_coff;      // int32[S]  first chunk of each segment (non-decreasing)
     size_t lvl_seg;       // int32[FK_MAX_DEPTH*level_cap]
+    size_t lvl_sorted;    // int32[FK_MAX_DEPTH*level_cap] each level by decreasing chunk count
     size_t chunk_seg;     // int32[chunk_cap] segment of each GDN chunk
     size_t chunk_row0;    // int32[chunk_cap] first local token of each chunk
     size_t seg_chunk0;    // int32[S] index of a live segment's first chunk
@@ -111,6 +112,7 @@ inline WsLayout ws_layout(const fk_tree_meta &m, int64_t Hv, int64_t dk, int64_t
     L.seg_tile0 = take(S * 4);
     L.seg_coff = take(S * 4);
     L.lvl_seg = take((size_t)FK_MAX_DEPTH * (size_t)(m.level_cap > 0 ? m.level_cap : 1) * 4);
+    L.lvl_sorted = take((size_t)FK_MAX_DEPTH * (size_t)(m.level_cap > 0 ? m.level_cap : 1) * 4);
     L.chunk_seg = take((size_t)L.chunk_cap * 4);
     L.chunk_row0 = take((size_t)L.chunk_cap * 4);
     L.seg_chunk0 = take(S * 4);

@@ -309,10 +309,11 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
 }
 
 // ---------------------------------------------------------------------------
-// Chunk walk of one tree level, persistent: work-group b runs the items
-// b, b + G, b + 2G, ... (G = grid size), item = (segment, v-head, 64-wide dv
-// slice), and within an item its chunks in order -- one flat sequence of
-// steps.  Waves 0-3 (consumers) own the state slice and run the
+// Chunk walk of one tree level, persistent: item = (segment, v-head, 64-wide
+// dv slice), segments taken by decreasing chunk count; work-group b runs the
+// items b, 2G-1-b, 2G+b, 4G-1-b, ... (G = grid size: forward and backward in
+// turn, so the longest items pair with the shortest), and within an item its
+// chunks in order -- one flat sequence of steps.  Waves 0-3 (consumers) own the state slice and run the
 // state-dependent products of step j; waves 4-7 (producers) meanwhile write
 // step j+1 (already in their registers) into the other LDS buffer, issue the
 // global loads of step j+2, and store the output of step j-1 that the
@@ -327,7 +328,7 @@ struct ChunkArgs {
     const float *a, *b;
     uint16_t *out;
     int T, Hk, Hv, level, level_cap;
-    const int32_t *header, *lvl_seg, *seg_start, *seg_len, *seg_src, *seg_chunk0, *emit_off, *emit_pos,
+    const int32_t *header, *lvl_sorted, *seg_start, *seg_len, *seg_src, *seg_chunk0, *emit_off, *emit_pos,
         *seg_state_out;
     const uint16_t *tmat, *pmat;
     const float *state_in;
@@ -368,11 +369,15 @@ struct Item {
     int s, h, g, dv0, len, nch, chunk0, t0, src;
 };
 
+// the k-th item of work-group b among G: forward in even rounds, backward in
+// odd ones.  Once an id reaches n_items every later one does too.
+__device__ __forceinline__ int item_id(int b, int k, int G) { return k * G + ((k & 1) ? G - 1 - b : b); }
+
 __device__ __forceinline__ Item item_at(const ChunkArgs &A, int it)
 {
     Item I;
     const int rank = it / (A.Hv * NSL);
-    I.s = ldc(A.lvl_seg, A.level * A.level_cap + rank);
+    I.s = ldc(A.lvl_sorted, A.level * A.level_cap + rank);
     I.h = (it / NSL) % A.Hv;
     I.g = I.h / (A.Hv / A.Hk);
     I.dv0 = (it % NSL) * DVS;
@@ -602,11 +607,12 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
         Item cur = item_at(A, blockIdx.x);
         // the item after the last one handed to a step, looked up one item
         // ahead so its (dependent) scalar loads are long done when it is used
-        int la_it = blockIdx.x + stride;
+        int la_k = 1;
+        int la_it = item_id(blockIdx.x, la_k, stride);
         Item la = la_it < n_items ? item_at(A, la_it) : cur;
         auto take = [&](Item &I) {
             I = la;
-            la_it += stride;
+            la_it = item_id(blockIdx.x, ++la_k, stride);
             if (la_it < n_items) la = item_at(A, la_it);
         };
         load_step(R, A, cur, 0, lane, part);
@@ -661,8 +667,8 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
 
     const int wv = w;   // consumer wave: dv columns [16 w, 16 w + 16) of the slice
     f32x4 st[DK / 16];
-    int it = blockIdx.x, c = 0;
-    Item cur = item_at(A, it);
+    int ik = 0, c = 0;
+    Item cur = item_at(A, blockIdx.x);
     Emits E = item_emits(A, cur);
     const size_t SZ = (size_t)DV * DK;
     __syncthreads();
@@ -671,11 +677,12 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
         const int dvc = cur.dv0 + wv * 16 + c16;   // this lane's state column (dv index)
         const bool last = c + 1 == cur.nch;
         // the next item's metadata, fetched while this step computes
-        const bool more = !last || it + stride < n_items;
+        const int next_it = item_id(blockIdx.x, ik + 1, stride);
+        const bool more = !last || next_it < n_items;
         Item nxt = cur;
         Emits nE = E;
         if (last && more) {
-            nxt = item_at(A, it + stride);
+            nxt = item_at(A, next_it);
             nE = item_emits(A, nxt);
         }
         if (c == 0) {
@@ -800,7 +807,7 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
         if (!last) {
             ++c;
         } else {
-            it += stride;
+            ++ik;
             cur = nxt;
             E = nE;
             c = 0;
@@ -846,7 +853,7 @@ int fk_launch_gdn_bf16(const fk_tree_meta *meta, int level, const void *q, const
     A.level = level;
     A.level_cap = meta->level_cap;
     A.header = ws_at<int32_t>(ws, L.header);
-    A.lvl_seg = ws_at<int32_t>(ws, L.lvl_seg);
+    A.lvl_sorted = ws_at<int32_t>(ws, L.lvl_sorted);
     A.seg_start = ws_at<int32_t>(ws, L.seg_start);
     A.seg_len = ws_at<int32_t>(ws, L.seg_len);
     A.seg_src = ws_at<int32_t>(ws, L.seg_src);

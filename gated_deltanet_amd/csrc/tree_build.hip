@@ -313,6 +313,39 @@ k_tile_order(const int32_t *__restrict__ header, const int32_t *__restrict__ til
     for (int t = threadIdx.x; t < n; t += blockDim.x) tile_order[atomicAdd(&cnt[bucket(t)], 1)] = t;
 }
 
+// Each level's live segments by decreasing number of GDN chunks (one block
+// per level; a bucket sort, order within a bucket is whatever the atomics
+// give).  Only the schedule of a level's launch depends on it: the chunk walk
+// deals the longest items out first, in a back-and-forth order, so the
+// level ends evenly; every item computes the same way in any order.
+__global__ void __launch_bounds__(BUILD_THREADS)
+k_level_order(const int32_t *__restrict__ header, const int32_t *__restrict__ lvl_seg,
+              const int32_t *__restrict__ seg_len, int level_cap, int32_t *__restrict__ lvl_sorted)
+{
+    __shared__ int cnt[ORDER_BUCKETS];
+    __shared__ int lds[32];
+    if (header[H_STATUS] != FK_OK) return;
+    const int lvl = blockIdx.x;
+    const int n = header[H_LEVEL0 + lvl];
+    if (n == 0) return;
+    const int32_t *src = lvl_seg + (size_t)lvl * level_cap;
+    int32_t *dst = lvl_sorted + (size_t)lvl * level_cap;
+    for (int b = threadIdx.x; b < ORDER_BUCKETS; b += blockDim.x) cnt[b] = 0;
+    __syncthreads();
+    auto bucket = [&](int i) { return min((seg_len[src[i]] + FK_GDN_CHUNK - 1) / FK_GDN_CHUNK, ORDER_BUCKETS - 1); };
+    for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&cnt[bucket(i)], 1);
+    __syncthreads();
+    const int b0 = ORDER_BUCKETS - 1 - 2 * threadIdx.x, b1 = b0 - 1;
+    int tot;
+    const int before = block_scan(cnt[b0] + cnt[b1], lds, &tot);
+    const int c0 = cnt[b0];
+    __syncthreads();
+    cnt[b0] = before;
+    cnt[b1] = before + c0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) dst[atomicAdd(&cnt[bucket(i)], 1)] = src[i];
+}
+
 // Phase 3 (pages): one block per segment checks the page ids the segment
 // uses, in parallel.  Runs only when the tree passed every other check.
 __global__ void k_check_pages(int S, const int32_t *__restrict__ seg_len, const int32_t *__restrict__ page_off,
@@ -411,6 +444,9 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
         if ((rc = launch_status())) return rc;
         k_tile_order<<<1, BUILD_THREADS, 0, st>>>(A.header, A.tile_seg, A.tile_row0, A.seg_pos0, A.seg_len,
                                                  ws_at<int32_t>(ws, L.tile_order));
+        if ((rc = launch_status())) return rc;
+        k_level_order<<<(unsigned)meta->max_depth, BUILD_THREADS, 0, st>>>(
+            A.header, A.lvl_seg, A.seg_len, meta->level_cap, ws_at<int32_t>(ws, L.lvl_sorted));
         if ((rc = launch_status())) return rc;
     }
     if (meta->seg_page_off) {
