@@ -383,6 +383,50 @@ def measure_rule(wl, steps: int, rule: int, window: int = 0):
             "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "algorithmic_flops": flops}
 
 
+def measure_readout(wl, steps: int):
+    """Selective readout (a row beyond the step): attention at the last token
+    of every question only, the round's keys/values already paged.  Bound by
+    streaming those rows' keys/values: algorithmic bytes = every key/value
+    token visible to some selected row, read once, plus their queries and
+    outputs."""
+    torch, fk, sh, tree = wl.torch, wl.fk, wl.sh, wl.tree
+    starts, acc = {}, 0
+    for sid in tree.order:
+        starts[sid] = acc
+        acc += tree.segs[sid].length
+    leaves = [i for i, sg in enumerate(tree.segs) if not sg.cached and not tree.children(i)]
+    rows = np.array([starts[i] + tree.segs[i].length - 1 for i in leaves], np.int32)
+    seen = {}                       # segment -> keys of it visible to some selected row
+    for i in leaves:
+        seen[i] = tree.segs[i].length
+        c = i
+        while tree.segs[c].parent >= 0:
+            p = tree.segs[c].parent
+            seen[p] = max(seen.get(p, 0), tree.segs[c].fork)
+            c = p
+    kv_tokens = sum(seen.values())
+    rows_t = torch.from_numpy(rows).cuda()
+    q_rows = wl.x["aq"][rows_t.long()].contiguous()
+    out = torch.empty_like(q_rows)
+
+    def run():
+        fk.fork_attn_readout(wl.meta, q_rows, rows_t, wl.k_pool, wl.v_pool, wl.ws, scale=wl.scale, out=out)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = float(kv_tokens * sh.Hkv * sh.d * 2 * 2 + 2 * len(rows) * sh.Hq * sh.d * 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "selective readout (bf16)", "rows": len(rows), "ms": ms, "bound": "hbm", "achieved": gbs,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": nbytes}
+
+
 def cpu_baseline(index: int, n_req: int):
     """The fp64 oracle, as it stands, on the first ``n_req`` requests of the
     same workload: every root-to-leaf path as its own isolated sequence
@@ -535,7 +579,8 @@ def main():
     }
     line["next_rows"] = {"conv": measure_conv(wl, args.steps),
                          "window_attention": measure_rule(wl, args.steps, 1, 1024),
-                         "two_way_attention": measure_rule(wl, args.steps, 2)}
+                         "two_way_attention": measure_rule(wl, args.steps, 2),
+                         "readout": measure_readout(wl, args.steps)}
     if not getattr(wl, "gdn_ok", True):
         line["incomplete"] = "gdn_fork_forward unsupported for this dtype in this build: step lacks GDN"
         line["phases_ms"]["gdn"] = None

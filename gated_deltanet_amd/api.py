@@ -179,6 +179,23 @@ def fork_attn_forward_rule(meta: TreeMeta, q, k, v, k_pool, v_pool, ws, rule, wi
     return out
 
 
+def fork_attn_readout(meta: TreeMeta, q_rows, rows, k_pool, v_pool, ws, rule=_lib.FK_RULE_CAUSAL, window=0,
+                      scale=None, out=None, stream=None) -> torch.Tensor:
+    """Attention at the stream tokens ``rows`` (int32 device tensor, -1 =
+    unused) only; q_rows / out [n_rows, Hq, d].  K/V must already be paged."""
+    n, Hq, d = q_rows.shape
+    assert rows.dtype == torch.int32 and rows.numel() == n
+    Hkv = k_pool.shape[1]
+    if out is None:
+        out = torch.zeros_like(q_rows)
+    scale = float(scale if scale is not None else d ** -0.5)
+    m = meta.c()
+    check("fork_attn_readout", _lib.load().fork_attn_readout(
+        ctypes.byref(m), _ptr(q_rows), _ptr(rows), n, _DT[q_rows.dtype], Hq, Hkv, d, scale, int(rule), int(window),
+        _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
 def gdn_fork_forward(meta: TreeMeta, q, k, v, a, b, ws, state_in=None, state_out=None, out=None,
                      stream=None) -> torch.Tensor:
     T, Hk, dk = q.shape

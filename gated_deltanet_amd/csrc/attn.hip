@@ -24,7 +24,8 @@ int fk_launch_kv_append(const fk_tree_meta *meta, const void *k, const void *v, 
 int fk_check_kv_args(const fk_tree_meta *meta, const void *k, const void *v, int dtype, int Hkv, int d,
                      void *k_pool, void *v_pool, const void *ws);
 int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv, float scale, int rule, int window,
-                        const void *k_pool, const void *v_pool, void *out, const void *ws, hipStream_t st);
+                        const int32_t *rows, int n_rows, const void *k_pool, const void *v_pool, void *out,
+                        const void *ws, hipStream_t st);
 
 namespace fk {
 
@@ -41,9 +42,12 @@ __device__ __forceinline__ float wave_sum(float x)
 }
 
 // grid: (tile capacity, Hq); block: one wave.  d <= 128: lane owns dims
-// lane and lane + 64.
+// lane and lane + 64.  Readout (sel_rows != NULL): grid (rows, Hq), the one
+// selected token, its query and output at the row buffer's entry.
 __global__ void __launch_bounds__(64) k_attn_f32(const float *__restrict__ q, int Hq, int Hkv, int d, float scale,
-                                                 int rule, int window, const int32_t *__restrict__ seg_pos0,
+                                                 int rule, int window, const int32_t *__restrict__ sel_rows,
+                                                 const int32_t *__restrict__ tok_seg, int T,
+                                                 const int32_t *__restrict__ seg_pos0,
                                                  const float *__restrict__ kp, const float *__restrict__ vp,
                                                  float *__restrict__ out, const int32_t *__restrict__ header,
                                                  const int32_t *__restrict__ tile_seg,
@@ -58,16 +62,27 @@ __global__ void __launch_bounds__(64) k_attn_f32(const float *__restrict__ q, in
 {
     if (header[H_STATUS] != FK_OK) return;
     const int tile = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-    if (tile >= header[H_NTILES]) return;
-    const int s = tile_seg[tile], row0 = tile_row0[tile];
+    int s, row0, nrows;
+    if (sel_rows) {
+        const int t = sel_rows[tile];
+        if (t < 0 || t >= T) return;   // an unused entry of the row buffer
+        s = tok_seg[t];
+        row0 = t - seg_start[s];
+        nrows = 1;
+    } else {
+        if (tile >= header[H_NTILES]) return;
+        s = tile_seg[tile];
+        row0 = tile_row0[tile];
+        nrows = min(FK_TILE_TOKENS, seg_len[s] - row0);
+    }
     const int g = h / (Hq / Hkv);
     const int depth = seg_depth[s];
     const int *anc = seg_anc + s * FK_MAX_DEPTH;
-    const int nrows = min(FK_TILE_TOKENS, seg_len[s] - row0);
     const size_t page_elems = (size_t)FK_TILE_TOKENS * d;
     for (int r = 0; r < nrows; ++r) {
         const int t = seg_start[s] + row0 + r;
-        const float *qr = q + ((size_t)t * Hq + h) * d;
+        const size_t qrow = sel_rows ? (size_t)tile * Hq + h : (size_t)t * Hq + h;
+        const float *qr = q + qrow * d;
         float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
         for (int lvl = 0; lvl <= depth; ++lvl) {
             const int a = anc[lvl];
@@ -106,7 +121,7 @@ __global__ void __launch_bounds__(64) k_attn_f32(const float *__restrict__ q, in
                 m = mn;
             }
         }
-        float *orow = out + ((size_t)t * Hq + h) * d;
+        float *orow = out + qrow * d;
         if (lane < d) orow[lane] = o0 / l;
         if (lane + 64 < d) orow[lane + 64] = o1 / l;
     }
@@ -116,10 +131,10 @@ __global__ void __launch_bounds__(64) k_attn_f32(const float *__restrict__ q, in
 
 using namespace fk;
 
-extern "C" int fork_attn_forward_rule(const fk_tree_meta *meta, const void *q, const void *k, const void *v,
-                                      int dtype, int Hq, int Hkv, int d, float scale, int rule, int window,
-                                      void *k_pool, void *v_pool, void *out, void *ws, size_t ws_bytes,
-                                      fk_stream_t stream)
+// The full launch (rows == NULL) or the readout of `rows`.
+static int attn_entry(const fk_tree_meta *meta, const void *q, const void *k, const void *v, int dtype, int Hq,
+                      int Hkv, int d, float scale, int rule, int window, const int32_t *rows, int n_rows,
+                      void *k_pool, void *v_pool, void *out, void *ws, size_t ws_bytes, hipStream_t st)
 {
     if (rule != FK_RULE_CAUSAL && rule != FK_RULE_WINDOW && rule != FK_RULE_TWO_WAY) return FK_E_INVALID_ARG;
     if (rule == FK_RULE_WINDOW && window < 1) return FK_E_INVALID_ARG;
@@ -128,22 +143,23 @@ extern "C" int fork_attn_forward_rule(const fk_tree_meta *meta, const void *q, c
     int rc = fk_check_kv_args(meta, append ? k : q, append ? v : q, dtype, Hkv, d, k_pool, v_pool, ws);
     if (rc) return rc;
     if (Hq < 1 || Hq % Hkv) return FK_E_UNSUPPORTED;
-    if (meta->T > 0 && (!q || !out)) return FK_E_INVALID_ARG;
+    const bool any = rows ? n_rows > 0 : meta->T > 0;
+    if (any && (!q || !out)) return FK_E_INVALID_ARG;
     if (!(scale > 0.f) || !isfinite(scale)) return FK_E_INVALID_ARG;
     const WsLayout L = ws_layout(*meta, 0, 0, 0);
     if (ws_bytes < L.total) return FK_E_WORKSPACE;
     if (dtype == FK_BF16 && (d != 128 || Hq / Hkv != 8)) return FK_E_UNSUPPORTED;
     if (meta->T == 0) return FK_OK;
-    hipStream_t st = (hipStream_t)stream;
     if (append) {
         rc = fk_launch_kv_append(meta, k, v, dtype, Hkv, d, k_pool, v_pool, ws, st);
         if (rc) return rc;
     }
+    if (!any) return FK_OK;
     if (dtype == FK_BF16)
-        return fk_launch_attn_bf16(meta, q, Hq, Hkv, scale, rule, window, k_pool, v_pool, out, ws, st);
-    dim3 grid((unsigned)L.tile_cap, (unsigned)Hq);
-    k_attn_f32<<<grid, 64, 0, st>>>((const float *)q, Hq, Hkv, d, scale, rule, window, ws_at<int32_t>(ws, L.seg_pos0),
-                                    (const float *)k_pool,
+        return fk_launch_attn_bf16(meta, q, Hq, Hkv, scale, rule, window, rows, n_rows, k_pool, v_pool, out, ws, st);
+    dim3 grid((unsigned)(rows ? (int64_t)n_rows : L.tile_cap), (unsigned)Hq);
+    k_attn_f32<<<grid, 64, 0, st>>>((const float *)q, Hq, Hkv, d, scale, rule, window, rows, meta->tok_seg, meta->T,
+                                    ws_at<int32_t>(ws, L.seg_pos0), (const float *)k_pool,
                                     (const float *)v_pool, (float *)out, ws_at<int32_t>(ws, L.header),
                                     ws_at<int32_t>(ws, L.tile_seg), ws_at<int32_t>(ws, L.tile_row0),
                                     ws_at<int32_t>(ws, L.seg_start), ws_at<int32_t>(ws, L.seg_len),
@@ -152,10 +168,31 @@ extern "C" int fork_attn_forward_rule(const fk_tree_meta *meta, const void *q, c
     return launch_status();
 }
 
+extern "C" int fork_attn_forward_rule(const fk_tree_meta *meta, const void *q, const void *k, const void *v,
+                                      int dtype, int Hq, int Hkv, int d, float scale, int rule, int window,
+                                      void *k_pool, void *v_pool, void *out, void *ws, size_t ws_bytes,
+                                      fk_stream_t stream)
+{
+    return attn_entry(meta, q, k, v, dtype, Hq, Hkv, d, scale, rule, window, nullptr, 0, k_pool, v_pool, out, ws,
+                      ws_bytes, (hipStream_t)stream);
+}
+
 extern "C" int fork_attn_forward(const fk_tree_meta *meta, const void *q, const void *k, const void *v, int dtype,
                                  int Hq, int Hkv, int d, float scale, void *k_pool, void *v_pool, void *out,
                                  void *ws, size_t ws_bytes, fk_stream_t stream)
 {
-    return fork_attn_forward_rule(meta, q, k, v, dtype, Hq, Hkv, d, scale, FK_RULE_CAUSAL, 0, k_pool, v_pool, out,
-                                  ws, ws_bytes, stream);
+    return attn_entry(meta, q, k, v, dtype, Hq, Hkv, d, scale, FK_RULE_CAUSAL, 0, nullptr, 0, k_pool, v_pool, out,
+                      ws, ws_bytes, (hipStream_t)stream);
+}
+
+extern "C" int fork_attn_readout(const fk_tree_meta *meta, const void *q_rows, const int32_t *rows, int32_t n_rows,
+                                 int dtype, int Hq, int Hkv, int d, float scale, int rule, int window,
+                                 const void *k_pool, const void *v_pool, void *out_rows, void *ws, size_t ws_bytes,
+                                 fk_stream_t stream)
+{
+    if (n_rows < 0 || (n_rows > 0 && !rows)) return FK_E_INVALID_ARG;
+    if (n_rows == 0) return FK_OK;
+    return attn_entry(meta, q_rows, nullptr, nullptr, dtype, Hq, Hkv, d, scale, rule, window, rows, n_rows,
+                      const_cast<void *>(k_pool), const_cast<void *>(v_pool), out_rows, ws, ws_bytes,
+                      (hipStream_t)stream);
 }

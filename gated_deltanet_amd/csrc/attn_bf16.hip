@@ -168,9 +168,16 @@ __device__ __forceinline__ bool cursor_next(BlockCursor &c, const TileCtx &t)
     return true;
 }
 
-template <int RULE>
+// READOUT (selective readout, Flide section 3.3.3): work item = (selected
+// row, kv head) instead of (tile, kv head).
+// The work-group runs the tile that holds the selected token exactly as the
+// full launch does, but only the wave that owns the token computes, its
+// other rows read zero queries, and only the token's 8 rows are stored --
+// so a readout row has the same bits as the same row of the full launch.
+template <int RULE, bool READOUT>
 __global__ void __launch_bounds__(THREADS, 2)
 k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, int window,
+            const int32_t *__restrict__ sel_rows, const int32_t *__restrict__ tok_seg, int T,
             const int32_t *__restrict__ seg_pos0, const uint16_t *__restrict__ kp,
             const uint16_t *__restrict__ vp, uint16_t *__restrict__ out, const int32_t *__restrict__ header,
             const int32_t *__restrict__ tile_seg, const int32_t *__restrict__ tile_row0,
@@ -185,23 +192,37 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     // heaviest tiles first (both kv heads of a tile side by side), so the
     // launch does not end on a long tile started late
     const int rank = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
-    if (rank >= header[H_NTILES]) return;
-    const int tile = tile_order[rank];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int half = lane >> 5, n = lane & 31;
-    const int s = tile_seg[tile], row0 = tile_row0[tile];
+    int s, row0, sel_local = 0;
+    if (READOUT) {
+        const int t = sel_rows[rank];
+        if (t < 0 || t >= T) return;   // an unused entry of the row buffer
+        s = tok_seg[t];
+        sel_local = t - seg_start[s];
+        row0 = sel_local & ~(FK_TILE_TOKENS - 1);
+    } else {
+        if (rank >= header[H_NTILES]) return;
+        const int tile = tile_order[rank];
+        s = tile_seg[tile];
+        row0 = tile_row0[tile];
+    }
     const int len = seg_len[s];
     const int tok = row0 + w * 4 + n / 8;          // local token of this lane's row
     const int h = g * G + (n % 8);
-    const bool row_valid = tok < len;
+    const bool row_valid = READOUT ? tok == sel_local : tok < len;
+    // the wave that owns the selected token (all waves in a full launch)
+    const bool active = !READOUT || w == ((sel_local - row0) >> 2);
     const size_t t_glob = (size_t)seg_start[s] + tok;
+    // query / output row: the stream token, or the row buffer's entry
+    const size_t qrow = READOUT ? (size_t)rank * Hq + h : t_glob * Hq + h;
 
     // Q^T as the B operand: lane holds its row's dims 16*ks + 8*half + [0, 8)
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
         uint4 u = make_uint4(0, 0, 0, 0);
-        if (row_valid) u = *reinterpret_cast<const uint4 *>(q + (t_glob * Hq + h) * D + ks * 16 + half * 8);
+        if (row_valid) u = *reinterpret_cast<const uint4 *>(q + qrow * D + ks * 16 + half * 8);
         qf[ks] = as_bf16x8(u);
     }
     f32x16 o[D / 32];
@@ -242,94 +263,96 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
         const bool more = cursor_next<RULE>(nxt, tc);
         BlockRegs R;
         if (more) load_block(R, kp, vp, nxt.plist, nxt.key0, nxt.count, g, Hkv);
-        const int key0 = cur.key0, count = cur.count, pdiff = cur.pdiff;
-        const bool own = cur.own;
-        const uint16_t *kl = k_lds[buf], *vl = v_lds[buf];
-        // S^T = K . Q^T
-        f32x16 sacc[2] = {f32x16{}, f32x16{}};
-        {
-            const uint16_t *krow = kl + prow * K_STRIDE + half * 8;
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + mt * 32 * K_STRIDE + ks * 16));
-                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
+        if (active) {   // wave-uniform
+            const int key0 = cur.key0, count = cur.count, pdiff = cur.pdiff;
+            const bool own = cur.own;
+            const uint16_t *kl = k_lds[buf], *vl = v_lds[buf];
+            // S^T = K . Q^T
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+            {
+                const uint16_t *krow = kl + prow * K_STRIDE + half * 8;
+    #pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks)
+    #pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + mt * 32 * K_STRIDE + ks * 16));
+                        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
+                    }
+                // keep LOOKAHEAD operand reads in flight ahead of the MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);
+    #pragma unroll
+                for (int j = 0; j < 16 - LOOKAHEAD; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
-            // keep LOOKAHEAD operand reads in flight ahead of the MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);
-#pragma unroll
-            for (int j = 0; j < 16 - LOOKAHEAD; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, LOOKAHEAD, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, LOOKAHEAD, 0);
-        }
-        // mask: register r of tile mt holds key 32*mt + 16*(r/8) + 8*half + r%8
-        // of the block.  Only blocks that cross the diagonal, the end of a
-        // visible range or the window's edge are masked, in place.  hi / lo:
-        // last / first visible key offset within the block, minus 8 * half.
-        const bool causal_own = own && RULE != TWO_WAY;
-        const int hi = (causal_own ? tok - key0 : count - 1 - key0) - half * 8;
-        const int lo = (RULE == WINDOW ? pdiff + tok - window + 1 - key0 : 0) - half * 8;
-        const bool full = (causal_own ? (key0 + BN - 1 <= row0) : (key0 + BN <= count)) &&
-                          (RULE != WINDOW || key0 >= pdiff + row0 + FK_TILE_TOKENS - window);
-        if (!full) {
-#pragma unroll
+            // mask: register r of tile mt holds key 32*mt + 16*(r/8) + 8*half + r%8
+            // of the block.  Only blocks that cross the diagonal, the end of a
+            // visible range or the window's edge are masked, in place.  hi / lo:
+            // last / first visible key offset within the block, minus 8 * half.
+            const bool causal_own = own && RULE != TWO_WAY;
+            const int hi = (causal_own ? tok - key0 : count - 1 - key0) - half * 8;
+            const int lo = (RULE == WINDOW ? pdiff + tok - window + 1 - key0 : 0) - half * 8;
+            const bool full = (causal_own ? (key0 + BN - 1 <= row0) : (key0 + BN <= count)) &&
+                              (RULE != WINDOW || key0 >= pdiff + row0 + FK_TILE_TOKENS - window);
+            if (!full) {
+    #pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int koff = mt * 32 + (r / 8) * 16 + (r % 8);
+                        bool vis = koff <= hi;
+                        if (RULE == WINDOW) vis = vis && koff >= lo;
+                        sacc[mt][r] = vis ? sacc[mt][r] : -INFINITY;
+                    }
+            }
+            // row max on raw scores (scale > 0); the two wave halves hold disjoint
+            // keys of the same row and swap maxima with one permlane
+            float mloc = sacc[0][0];
+    #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int koff = mt * 32 + (r / 8) * 16 + (r % 8);
-                    bool vis = koff <= hi;
-                    if (RULE == WINDOW) vis = vis && koff >= lo;
-                    sacc[mt][r] = vis ? sacc[mt][r] : -INFINITY;
-                }
-        }
-        // row max on raw scores (scale > 0); the two wave halves hold disjoint
-        // keys of the same row and swap maxima with one permlane
-        float mloc = sacc[0][0];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = (mt == 0 ? 1 : 0); r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[mt][r]);
-        const float mrow = pair_max(mloc) * scale_log2e;
-        // lazy rescale: a row moves its reference max only when the block's
-        // max exceeds it by more than RESCALE_LOG2 (the exponents then stay
-        // <= 2^RESCALE_LOG2); rows that do not move multiply by exactly 1
-        const bool need = mrow > m + RESCALE_LOG2;
-        if (__any(need)) {   // wave-uniform branch
-            const float mnew = need ? mrow : m;
-            const float corr = __builtin_amdgcn_exp2f(m - mnew);
-            l *= corr;
-#pragma unroll
-            for (int i = 0; i < D / 32; ++i) o[i] *= corr;
-            m = mnew;
-        }
-        float ps[4] = {0.f, 0.f, 0.f, 0.f};
-        bf16x8 pf[4];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                float pv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][hh * 8 + e], scale_log2e, -m));
-                    ps[e & 3] += pv[e];
-                }
-                pf[mt * 2 + hh] = as_bf16x8(pack8(pv));
+    #pragma unroll
+                for (int r = (mt == 0 ? 1 : 0); r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[mt][r]);
+            const float mrow = pair_max(mloc) * scale_log2e;
+            // lazy rescale: a row moves its reference max only when the block's
+            // max exceeds it by more than RESCALE_LOG2 (the exponents then stay
+            // <= 2^RESCALE_LOG2); rows that do not move multiply by exactly 1
+            const bool need = mrow > m + RESCALE_LOG2;
+            if (__any(need)) {   // wave-uniform branch
+                const float mnew = need ? mrow : m;
+                const float corr = __builtin_amdgcn_exp2f(m - mnew);
+                l *= corr;
+    #pragma unroll
+                for (int i = 0; i < D / 32; ++i) o[i] *= corr;
+                m = mnew;
             }
-        l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        // O^T += V^T . P^T ; k-step kk covers keys 16*kk + [0, 16)
-        {
-            const uint16_t *vrow = vl + n * V_STRIDE + half * 8;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int i = 0; i < D / 32; ++i) {
-                    const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + i * 32 * V_STRIDE + kk * 16));
-                    o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[i], 0, 0, 0);
+            float ps[4] = {0.f, 0.f, 0.f, 0.f};
+            bf16x8 pf[4];
+    #pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+    #pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    float pv[8];
+    #pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][hh * 8 + e], scale_log2e, -m));
+                        ps[e & 3] += pv[e];
+                    }
+                    pf[mt * 2 + hh] = as_bf16x8(pack8(pv));
                 }
+            l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            // O^T += V^T . P^T ; k-step kk covers keys 16*kk + [0, 16)
+            {
+                const uint16_t *vrow = vl + n * V_STRIDE + half * 8;
+    #pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+    #pragma unroll
+                    for (int i = 0; i < D / 32; ++i) {
+                        const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + i * 32 * V_STRIDE + kk * 16));
+                        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[i], 0, 0, 0);
+                    }
+            }
         }
         if (!more) break;
         store_block(k_lds[buf ^ 1], v_lds[buf ^ 1], R);
@@ -340,7 +363,7 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     const float lsum = pair_sum(l);
     if (!row_valid) return;
     const float inv = 1.f / lsum;
-    uint16_t *orow = out + (t_glob * Hq + h) * D;
+    uint16_t *orow = out + qrow * D;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
@@ -361,13 +384,15 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
 
 using namespace fk;
 
-template <int RULE>
+template <int RULE, bool READOUT>
 static void launch_rule(const fk_tree_meta *meta, const WsLayout &L, const void *q, int Hq, int Hkv, float scale,
-                        int window, const void *k_pool, const void *v_pool, void *out, const void *ws, hipStream_t st)
+                        int window, const int32_t *rows, int n_rows, const void *k_pool, const void *v_pool,
+                        void *out, const void *ws, hipStream_t st)
 {
-    dim3 grid((unsigned)(L.tile_cap * Hkv));
-    attn::k_attn_bf16<RULE><<<grid, attn::THREADS, 0, st>>>(
-        (const uint16_t *)q, Hq, Hkv, scale * 1.4426950408889634f, window, ws_at<int32_t>(ws, L.seg_pos0),
+    dim3 grid((unsigned)((READOUT ? (int64_t)n_rows : L.tile_cap) * Hkv));
+    attn::k_attn_bf16<RULE, READOUT><<<grid, attn::THREADS, 0, st>>>(
+        (const uint16_t *)q, Hq, Hkv, scale * 1.4426950408889634f, window, rows, meta->tok_seg, meta->T,
+        ws_at<int32_t>(ws, L.seg_pos0),
         (const uint16_t *)k_pool,
         (const uint16_t *)v_pool, (uint16_t *)out, ws_at<int32_t>(ws, L.header), ws_at<int32_t>(ws, L.tile_seg),
         ws_at<int32_t>(ws, L.tile_row0), ws_at<int32_t>(ws, L.tile_order), ws_at<int32_t>(ws, L.seg_start),
@@ -376,15 +401,26 @@ static void launch_rule(const fk_tree_meta *meta, const WsLayout &L, const void 
         meta->seg_pages);
 }
 
+// rows == NULL: the full launch over the round's tiles; otherwise readout of
+// the n_rows entries of `rows` (q and out then hold one row per entry)
 int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv, float scale, int rule, int window,
-                        const void *k_pool, const void *v_pool, void *out, const void *ws, hipStream_t st)
+                        const int32_t *rows, int n_rows, const void *k_pool, const void *v_pool, void *out,
+                        const void *ws, hipStream_t st)
 {
     const WsLayout L = ws_layout(*meta, 0, 0, 0);
+#define FK_ATTN_LAUNCH(R)                                                                                   \
+    do {                                                                                                   \
+        if (rows)                                                                                          \
+            launch_rule<R, true>(meta, L, q, Hq, Hkv, scale, window, rows, n_rows, k_pool, v_pool, out, ws, st); \
+        else                                                                                               \
+            launch_rule<R, false>(meta, L, q, Hq, Hkv, scale, window, rows, n_rows, k_pool, v_pool, out, ws, st); \
+    } while (0)
     if (rule == FK_RULE_WINDOW)
-        launch_rule<attn::WINDOW>(meta, L, q, Hq, Hkv, scale, window, k_pool, v_pool, out, ws, st);
+        FK_ATTN_LAUNCH(attn::WINDOW);
     else if (rule == FK_RULE_TWO_WAY)
-        launch_rule<attn::TWO_WAY>(meta, L, q, Hq, Hkv, scale, window, k_pool, v_pool, out, ws, st);
+        FK_ATTN_LAUNCH(attn::TWO_WAY);
     else
-        launch_rule<attn::CAUSAL>(meta, L, q, Hq, Hkv, scale, window, k_pool, v_pool, out, ws, st);
+        FK_ATTN_LAUNCH(attn::CAUSAL);
+#undef FK_ATTN_LAUNCH
     return launch_status();
 }

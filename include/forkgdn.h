@@ -219,6 +219,24 @@ int fork_attn_forward_rule(const fk_tree_meta *meta, const void *q, const void *
                            void *out, void *ws, size_t ws_bytes, fk_stream_t stream);
 
 /*
+ * fork_attn_readout -- attention at selected rows only (Flide section 3.3.3:
+ * the output head reads only the last token of every question, so in the
+ * final layer every token still contributes its keys and values while the
+ * rest of the layer runs only at these rows, listed in an index buffer of
+ * fixed size).  rows: int32 [n_rows] (device), stream token index of each
+ * entry, or -1 for an unused entry (its output row is left untouched).
+ * q_rows, out_rows: [n_rows, Hq, d] -- the queries and outputs of the entries.
+ * The round's keys/values must already be in the pool (kv_append or a full
+ * fork_attn_forward of the round).  Each entry's output has the same bits as
+ * that token's row of fork_attn_forward_rule with the same rule: the work of
+ * an entry is the tile that holds its token, run the same way.  Other
+ * arguments, support and errors as fork_attn_forward_rule.
+ */
+int fork_attn_readout(const fk_tree_meta *meta, const void *q_rows, const int32_t *rows, int32_t n_rows, int dtype,
+                      int Hq, int Hkv, int d, float scale, int rule, int window, const void *k_pool,
+                      const void *v_pool, void *out_rows, void *ws, size_t ws_bytes, fk_stream_t stream);
+
+/*
  * gdn_fork_forward -- forked Gated DeltaNet (Flide section 3.2.2, Eq. 4, and
  * its two-call scheme generalised to one launch per tree level).  A fresh
  * root starts from the zero state; a child of a cached segment from
