@@ -16,6 +16,8 @@
 // before the tile (the halo) and the tile's rows into registers once, and
 // writes each output row once -- an HBM-bound stream, read once and written
 // once, halo rows aside (neighbouring tiles of one XCD share them in L2).
+// The tile's own rows are read and the outputs written with non-temporal
+// accesses (streamed, not kept in the caches).
 // Halo rows before a segment's first token come from the ancestor chain the
 // builder derived: a live ancestor's token, or, below a cached history, the
 // history's saved window (window_in of its state slot).  The tile holding a
@@ -31,6 +33,8 @@ namespace convk {
 constexpr int TILE = FK_TILE_TOKENS;   // 16 rows per work item
 constexpr int THREADS = 256;
 constexpr int XCDS = 8;                // work-groups are dealt to the 8 XCDs round-robin
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 struct ConvArgs {
     const void *x;          // [T, C]
@@ -160,7 +164,10 @@ __global__ void __launch_bounds__(THREADS) k_conv(ConvArgs A)
 #pragma unroll
     for (int r = 0; r < TILE; ++r) {
         rows[H + r] = make_uint4(0, 0, 0, 0);
-        if (r < count) rows[H + r] = *reinterpret_cast<const uint4 *>(x + (size_t)(t0 + r) * C + c0);
+        if (r < count) {
+            const u32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + (size_t)(t0 + r) * C + c0));
+            rows[H + r] = make_uint4(vv.x, vv.y, vv.z, vv.w);
+        }
     }
 
     float wt[W][NV];
@@ -183,7 +190,8 @@ __global__ void __launch_bounds__(THREADS) k_conv(ConvArgs A)
 #pragma unroll
                 for (int j = 0; j < NV; ++j) acc[j] = fmaf(wt[i][j], xv[j], acc[j]);
             }
-            *reinterpret_cast<uint4 *>(y + (size_t)(t0 + r) * C + c0) = V::from_f32(acc);
+            const uint4 vv = V::from_f32(acc);
+            __builtin_nontemporal_store(u32x4{vv.x, vv.y, vv.z, vv.w}, reinterpret_cast<u32x4 *>(y + (size_t)(t0 + r) * C + c0));
         }
     }
 
