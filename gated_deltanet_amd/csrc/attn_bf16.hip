@@ -7,16 +7,18 @@
 // waves owns 32 rows (4 tokens x 8 heads), so a key/value block staged once in
 // LDS feeds the whole group.  Keys are visited range by range along the
 // tile's ancestor chain (each ancestor's first `fork` tokens, then the own
-// segment causally), in 64-key blocks anchored at every range start; a row's
+// segment causally), in 32-key blocks anchored at every range start; a row's
 // reduction order therefore depends only on its own chain (Flide 3.5).
+// A block pair of LDS buffers takes 38 KB, and the kernel 161 VGPRs, so three
+// work-groups (12 waves) share a compute unit.
 //
 // Per block and wave, with v_mfma_f32_32x32x16_bf16 (fp32 accumulate):
-//   S^T[64 keys x 32 rows] = K_blk[64 x 128] . Q^T[128 x 32]      16 MFMAs
+//   S^T[32 keys x 32 rows] = K_blk[32 x 128] . Q^T[128 x 32]       8 MFMAs
 //   online softmax on S^T in registers (row = lane % 32; the two halves of
 //   the wave hold disjoint keys of the same row; max via one permlane32 swap)
-//   O^T[128 x 32] += V^T[128 x 64] . P^T[64 x 32]                 16 MFMAs
-// The two 32-key MFMA chains (and the four 32-dim output chains) are
-// interleaved, with LDS operand reads issued LOOKAHEAD instructions ahead.
+//   O^T[128 x 32] += V^T[128 x 32] . P^T[32 x 32]                  8 MFMAs
+// The four 32-dim output chains are interleaved, and LDS operand reads are
+// issued LOOKAHEAD instructions ahead of their MFMAs.
 // A row's reference maximum moves only when a block exceeds it by more than
 // 2^RESCALE_LOG2 (the exponentials stay bounded by that factor), so most
 // blocks skip the rescale of the output accumulators; the decision is per
@@ -38,7 +40,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int D = 128;           // head dim
 constexpr int G = 8;             // q heads per kv head
-constexpr int BN = 64;           // keys per block
+constexpr int BN = 32;           // keys per block
+constexpr int MT = BN / 32;      // 32-key MFMA tiles per block
 constexpr int WAVES = 4;
 constexpr int THREADS = WAVES * 64;
 constexpr int K_STRIDE = D + 8;  // LDS row stride (bf16) of the key tile, padded
@@ -63,7 +66,7 @@ __device__ __forceinline__ float pair_sum(float x)
 }
 
 constexpr float RESCALE_LOG2 = 8.f;
-constexpr int LOOKAHEAD = 6;   // LDS operand reads issued ahead of the MFMAs
+constexpr int LOOKAHEAD = 4;   // LDS operand reads issued ahead of the MFMAs
 
 __device__ __forceinline__ uint4 pack8(const float *x)
 {
@@ -73,7 +76,7 @@ __device__ __forceinline__ uint4 pack8(const float *x)
     return __builtin_bit_cast(uint4, v);
 }
 
-// One 64-key block of a range = 4 pages of 16 keys.  Keys [BN][D] and
+// One block of a range = BN / 16 pages of 16 keys.  Keys [BN][D] and
 // transposed values [D][BN] of a block are loaded into registers (two 16-byte
 // pieces per page and thread) and later written into one of two LDS buffers.
 // Pages past the range's valid keys are zero, so no page-list entry beyond
@@ -175,7 +178,7 @@ __device__ __forceinline__ bool cursor_next(BlockCursor &c, const TileCtx &t)
 // other rows read zero queries, and only the token's 8 rows are stored --
 // so a readout row has the same bits as the same row of the full launch.
 template <int RULE, bool READOUT>
-__global__ void __launch_bounds__(THREADS, 2)
+__global__ void __launch_bounds__(THREADS, 3)
 k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, int window,
             const int32_t *__restrict__ sel_rows, const int32_t *__restrict__ tok_seg, int T,
             const int32_t *__restrict__ seg_pos0, const uint16_t *__restrict__ kp,
@@ -268,20 +271,22 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             const bool own = cur.own;
             const uint16_t *kl = k_lds[buf], *vl = v_lds[buf];
             // S^T = K . Q^T
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+            f32x16 sacc[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
             {
                 const uint16_t *krow = kl + prow * K_STRIDE + half * 8;
     #pragma unroll
                 for (int ks = 0; ks < D / 16; ++ks)
     #pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) {
+                    for (int mt = 0; mt < MT; ++mt) {
                         const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + mt * 32 * K_STRIDE + ks * 16));
                         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
                     }
                 // keep LOOKAHEAD operand reads in flight ahead of the MFMAs
                 __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);
     #pragma unroll
-                for (int j = 0; j < 16 - LOOKAHEAD; ++j) {
+                for (int j = 0; j < 8 * MT - LOOKAHEAD; ++j) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
@@ -298,7 +303,7 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
                               (RULE != WINDOW || key0 >= pdiff + row0 + FK_TILE_TOKENS - window);
             if (!full) {
     #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
     #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int koff = mt * 32 + (r / 8) * 16 + (r % 8);
@@ -311,7 +316,7 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             // keys of the same row and swap maxima with one permlane
             float mloc = sacc[0][0];
     #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
     #pragma unroll
                 for (int r = (mt == 0 ? 1 : 0); r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[mt][r]);
             const float mrow = pair_max(mloc) * scale_log2e;
@@ -328,9 +333,9 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
                 m = mnew;
             }
             float ps[4] = {0.f, 0.f, 0.f, 0.f};
-            bf16x8 pf[4];
+            bf16x8 pf[2 * MT];
     #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
     #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     float pv[8];
@@ -346,7 +351,7 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             {
                 const uint16_t *vrow = vl + n * V_STRIDE + half * 8;
     #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
+                for (int kk = 0; kk < 2 * MT; ++kk)
     #pragma unroll
                     for (int i = 0; i < D / 32; ++i) {
                         const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + i * 32 * V_STRIDE + kk * 16));
