@@ -66,7 +66,7 @@ __device__ __forceinline__ float pair_sum(float x)
 }
 
 constexpr float RESCALE_LOG2 = 8.f;
-constexpr int LOOKAHEAD = 4;   // LDS operand reads issued ahead of the MFMAs
+constexpr int LOOKAHEAD = 2;   // LDS operand reads issued ahead of the MFMAs
 
 __device__ __forceinline__ uint4 pack8(const float *x)
 {
