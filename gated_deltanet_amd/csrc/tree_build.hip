@@ -4,11 +4,15 @@
 // table is built on the GPU; section 3.3.2: launch sizes come from host-known
 // capacities, so the host never reads the tree).
 //
-// Kernels:
+// Kernels (five launches):
+//   k_init     grid over S   zero the header and per-segment counters
 //   k_tokens   grid over T   token runs of every segment (start, end, run count)
 //   k_build    one block     validation, lengths, first positions, ancestor
-//                            chains, attention tiles, level lists, fork points
-//   k_positions grid over T  per-token positions
+//                            chains, tile / chunk / level offsets, fork points
+//   k_post     grid          tile and chunk lists, page-id checks (a block per
+//                            segment), per-token positions
+//   k_orders   1 + levels    tile order (heaviest first), each level's
+//                            segments by decreasing chunk count
 // No dense T x T mask is ever formed: a tile's key ranges follow from its
 // segment's ancestor chain and the forks along it.
 #include <hip/hip_runtime.h>
@@ -157,7 +161,7 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
         const int coff = chunk_base + block_scan(nchunk, lds, &tot);
         chunk_base += tot;
         if (in) {
-            // the tile and chunk lists themselves are written by k_lists
+            // the tile and chunk lists themselves are written by k_post
             A.seg_tile0[s] = toff;
             A.seg_coff[s] = coff;
             A.seg_chunk0[s] = live ? coff : -1;
@@ -259,13 +263,11 @@ __device__ __forceinline__ int owner_of(const int32_t *__restrict__ first, int S
 }
 
 // Attention tiles and GDN chunks of every live segment, one thread per entry.
-__global__ void k_lists(int S, const int32_t *__restrict__ header, const int32_t *__restrict__ seg_tile0,
-                        const int32_t *__restrict__ seg_coff, int32_t *__restrict__ tile_seg,
-                        int32_t *__restrict__ tile_row0, int32_t *__restrict__ chunk_seg,
-                        int32_t *__restrict__ chunk_row0)
+__device__ void lists_thread(int i, int S, const int32_t *__restrict__ header, const int32_t *__restrict__ seg_tile0,
+                             const int32_t *__restrict__ seg_coff, int32_t *__restrict__ tile_seg,
+                             int32_t *__restrict__ tile_row0, int32_t *__restrict__ chunk_seg,
+                             int32_t *__restrict__ chunk_row0)
 {
-    if (header[H_STATUS] != FK_OK) return;
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < header[H_NTILES]) {
         const int s = owner_of(seg_tile0, S, i);
         tile_seg[i] = s;
@@ -283,14 +285,11 @@ __global__ void k_lists(int S, const int32_t *__restrict__ header, const int32_t
 // attention launch depends on it -- every tile computes the same way in any
 // order -- so the heaviest tiles start first and the launch ends evenly.
 constexpr int ORDER_BUCKETS = 2 * BUILD_THREADS;
-__global__ void __launch_bounds__(BUILD_THREADS)
-k_tile_order(const int32_t *__restrict__ header, const int32_t *__restrict__ tile_seg,
-             const int32_t *__restrict__ tile_row0, const int32_t *__restrict__ seg_pos0,
-             const int32_t *__restrict__ seg_len, int32_t *__restrict__ tile_order)
+__device__ void tile_order_block(const int32_t *__restrict__ header, const int32_t *__restrict__ tile_seg,
+                                 const int32_t *__restrict__ tile_row0, const int32_t *__restrict__ seg_pos0,
+                                 const int32_t *__restrict__ seg_len, int32_t *__restrict__ tile_order, int *cnt,
+                                 int *lds)
 {
-    __shared__ int cnt[ORDER_BUCKETS];
-    __shared__ int lds[32];
-    if (header[H_STATUS] != FK_OK) return;
     const int n = header[H_NTILES];
     for (int b = threadIdx.x; b < ORDER_BUCKETS; b += blockDim.x) cnt[b] = 0;
     __syncthreads();
@@ -318,14 +317,10 @@ k_tile_order(const int32_t *__restrict__ header, const int32_t *__restrict__ til
 // give).  Only the schedule of a level's launch depends on it: the chunk walk
 // deals the longest items out first, in a back-and-forth order, so the
 // level ends evenly; every item computes the same way in any order.
-__global__ void __launch_bounds__(BUILD_THREADS)
-k_level_order(const int32_t *__restrict__ header, const int32_t *__restrict__ lvl_seg,
-              const int32_t *__restrict__ seg_len, int level_cap, int32_t *__restrict__ lvl_sorted)
+__device__ void level_order_block(int lvl, const int32_t *__restrict__ header, const int32_t *__restrict__ lvl_seg,
+                                  const int32_t *__restrict__ seg_len, int level_cap, int32_t *__restrict__ lvl_sorted,
+                                  int *cnt, int *lds)
 {
-    __shared__ int cnt[ORDER_BUCKETS];
-    __shared__ int lds[32];
-    if (header[H_STATUS] != FK_OK) return;
-    const int lvl = blockIdx.x;
     const int n = header[H_LEVEL0 + lvl];
     if (n == 0) return;
     const int32_t *src = lvl_seg + (size_t)lvl * level_cap;
@@ -346,26 +341,60 @@ k_level_order(const int32_t *__restrict__ header, const int32_t *__restrict__ lv
     for (int i = threadIdx.x; i < n; i += blockDim.x) dst[atomicAdd(&cnt[bucket(i)], 1)] = src[i];
 }
 
+// Both orders in one launch: block 0 orders the tiles, block 1 + l level l.
+__global__ void __launch_bounds__(BUILD_THREADS)
+k_orders(const int32_t *__restrict__ header, const int32_t *__restrict__ tile_seg,
+         const int32_t *__restrict__ tile_row0, const int32_t *__restrict__ seg_pos0,
+         const int32_t *__restrict__ seg_len, int32_t *__restrict__ tile_order, const int32_t *__restrict__ lvl_seg,
+         int level_cap, int32_t *__restrict__ lvl_sorted)
+{
+    __shared__ int cnt[ORDER_BUCKETS];
+    __shared__ int lds[32];
+    if (header[H_STATUS] != FK_OK) return;
+    if (blockIdx.x == 0)
+        tile_order_block(header, tile_seg, tile_row0, seg_pos0, seg_len, tile_order, cnt, lds);
+    else
+        level_order_block(blockIdx.x - 1, header, lvl_seg, seg_len, level_cap, lvl_sorted, cnt, lds);
+}
+
 // Phase 3 (pages): one block per segment checks the page ids the segment
 // uses, in parallel.  Runs only when the tree passed every other check.
-__global__ void k_check_pages(int S, const int32_t *__restrict__ seg_len, const int32_t *__restrict__ page_off,
-                              const int32_t *__restrict__ pages, int page_size, int n_pages, int32_t *header)
+__device__ void check_pages_block(int s, const int32_t *__restrict__ seg_len, const int32_t *__restrict__ page_off,
+                                  const int32_t *__restrict__ pages, int page_size, int n_pages, int32_t *header)
 {
-    if (header[H_STATUS] != FK_OK) return;
-    const int s = blockIdx.x;
-    if (s >= S) return;
     const int need = (seg_len[s] + page_size - 1) / page_size, a = page_off[s];
     for (int j = threadIdx.x; j < need; j += blockDim.x)
         if (!rule_page_id(pages[a + j], n_pages)) set_error(header, FK_E_PAGES);
 }
 
-__global__ void k_positions(const int32_t *__restrict__ tok_seg, int T, const int32_t *header,
-                            const int32_t *seg_start, const int32_t *seg_pos0, int32_t *tok_pos)
+__device__ void positions_thread(int t, const int32_t *__restrict__ tok_seg, int T, const int32_t *seg_start,
+                                 const int32_t *seg_pos0, int32_t *tok_pos)
 {
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= T || header[H_STATUS] != FK_OK) return;
+    if (t >= T) return;
     const int s = tok_seg[t];
     tok_pos[t] = seg_pos0[s] + (t - seg_start[s]);
+}
+
+// After k_build, in one launch of 256-thread blocks: the tile and chunk lists
+// (blocks [0, nl)), the page checks (one block per segment, [nl, nl + np)),
+// the token positions (the rest).
+__global__ void __launch_bounds__(256)
+k_post(int nl, int np, int S, int T, int32_t *header, const int32_t *__restrict__ seg_tile0,
+       const int32_t *__restrict__ seg_coff, int32_t *__restrict__ tile_seg, int32_t *__restrict__ tile_row0,
+       int32_t *__restrict__ chunk_seg, int32_t *__restrict__ chunk_row0, const int32_t *__restrict__ seg_len,
+       const int32_t *__restrict__ page_off, const int32_t *__restrict__ pages, int page_size, int n_pages,
+       const int32_t *__restrict__ tok_seg, const int32_t *__restrict__ seg_start,
+       const int32_t *__restrict__ seg_pos0, int32_t *__restrict__ tok_pos)
+{
+    if (header[H_STATUS] != FK_OK) return;
+    const int b = blockIdx.x;
+    if (b < nl)
+        lists_thread(b * 256 + threadIdx.x, S, header, seg_tile0, seg_coff, tile_seg, tile_row0, chunk_seg,
+                     chunk_row0);
+    else if (b < nl + np)
+        check_pages_block(b - nl, seg_len, page_off, pages, page_size, n_pages, header);
+    else
+        positions_thread((b - nl - np) * 256 + threadIdx.x, tok_seg, T, seg_start, seg_pos0, tok_pos);
 }
 
 int check_meta_scalars(const fk_tree_meta *m)
@@ -439,24 +468,15 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
     if ((rc = launch_status())) return rc;
     {
         const int64_t n = L.tile_cap > L.chunk_cap ? L.tile_cap : L.chunk_cap;
-        k_lists<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(S, A.header, A.seg_tile0, A.seg_coff, A.tile_seg,
-                                                           A.tile_row0, A.chunk_seg, A.chunk_row0);
+        const int nl = (int)((n + 255) / 256), np = meta->seg_page_off ? S : 0, nt = (T + 255) / 256;
+        k_post<<<(unsigned)(nl + np + nt), 256, 0, st>>>(
+            nl, np, S, T, A.header, A.seg_tile0, A.seg_coff, A.tile_seg, A.tile_row0, A.chunk_seg, A.chunk_row0,
+            A.seg_len, meta->seg_page_off, meta->seg_pages, meta->page_size, meta->n_pages, meta->tok_seg,
+            A.seg_start, A.seg_pos0, ws_at<int32_t>(ws, L.tok_pos));
         if ((rc = launch_status())) return rc;
-        k_tile_order<<<1, BUILD_THREADS, 0, st>>>(A.header, A.tile_seg, A.tile_row0, A.seg_pos0, A.seg_len,
-                                                 ws_at<int32_t>(ws, L.tile_order));
-        if ((rc = launch_status())) return rc;
-        k_level_order<<<(unsigned)meta->max_depth, BUILD_THREADS, 0, st>>>(
-            A.header, A.lvl_seg, A.seg_len, meta->level_cap, ws_at<int32_t>(ws, L.lvl_sorted));
-        if ((rc = launch_status())) return rc;
-    }
-    if (meta->seg_page_off) {
-        k_check_pages<<<S, 256, 0, st>>>(S, A.seg_len, meta->seg_page_off, meta->seg_pages, meta->page_size,
-                                         meta->n_pages, A.header);
-        if ((rc = launch_status())) return rc;
-    }
-    if (T > 0) {
-        k_positions<<<(T + 255) / 256, 256, 0, st>>>(meta->tok_seg, T, A.header, A.seg_start, A.seg_pos0,
-                                                    ws_at<int32_t>(ws, L.tok_pos));
+        k_orders<<<(unsigned)(1 + meta->max_depth), BUILD_THREADS, 0, st>>>(
+            A.header, A.tile_seg, A.tile_row0, A.seg_pos0, A.seg_len, ws_at<int32_t>(ws, L.tile_order), A.lvl_seg,
+            meta->level_cap, ws_at<int32_t>(ws, L.lvl_sorted));
         if ((rc = launch_status())) return rc;
     }
     return FK_OK;
