@@ -369,18 +369,34 @@ struct Item {
     int s, h, g, dv0, len, nch, chunk0, t0, src;
 };
 
-// the k-th item of work-group b among G: forward in even rounds, backward in
-// odd ones.  Once an id reaches n_items every later one does too.
-__device__ __forceinline__ int item_id(int b, int k, int G) { return k * G + ((k & 1) ? G - 1 - b : b); }
+// How a level's items are dealt to the G work-groups.  Items are numbered
+// (v-head, dv slice) major, segment rank minor, so consecutive items of a
+// group are sibling segments on the same head and slice -- they enter from
+// the same fork-point state.  A level with at least 4 G items is dealt in
+// contiguous runs (work-group b takes items [b per, b per + per)), so a run of
+// siblings stages their common entering state once; a smaller level is dealt
+// forward and backward in turn (items b, 2G-1-b, 2G+b, ...), pairing its long
+// items with its short ones.  Once an id reaches n_items every later id of
+// the same work-group does too.
+struct Walk {
+    int n_items, nseg, G, per;
+    bool runs;
+};
 
-__device__ __forceinline__ Item item_at(const ChunkArgs &A, int it)
+__device__ __forceinline__ int item_id(const Walk &W, int b, int k)
+{
+    if (W.runs) return k < W.per ? b * W.per + k : 0x7fffffff;
+    return k * W.G + ((k & 1) ? W.G - 1 - b : b);
+}
+
+__device__ __forceinline__ Item item_at(const ChunkArgs &A, const Walk &W, int it)
 {
     Item I;
-    const int rank = it / (A.Hv * NSL);
+    const int rank = it % W.nseg, hs = it / W.nseg;
     I.s = ldc(A.lvl_sorted, A.level * A.level_cap + rank);
-    I.h = (it / NSL) % A.Hv;
+    I.h = hs / NSL;
     I.g = I.h / (A.Hv / A.Hk);
-    I.dv0 = (it % NSL) * DVS;
+    I.dv0 = (hs % NSL) * DVS;
     I.len = ldc(A.seg_len, I.s);
     I.nch = (I.len + C - 1) / C;
     I.chunk0 = ldc(A.seg_chunk0, I.s);
@@ -481,12 +497,16 @@ struct StepRegs {
     uint4 kv[4], qv[4], tv[2], pv[2], vv[2];
     f32x4 s0[8];
     float a_raw, b_raw;
+    bool s0_write;   // this step starts an item whose entering state is not staged yet
 };
 
-// issue the loads of chunk c of item I (and, when c == 0, of its entering
+// issue the loads of chunk c of item I (and, when `stage_s0`, of its entering
 // state); rows [16 part, 16 part + 16) of the chunk, dv rows of the state
 // likewise.  Coalesced: consecutive lanes read consecutive 16 B of a row.
-__device__ __forceinline__ void load_step(StepRegs &R, const ChunkArgs &A, const Item &I, int c, int lane, int part)
+// Rows past the chunk's last token are not read (zero): nothing uses them --
+// T and P are lower triangular, and zero key rows keep them out of the state.
+__device__ __forceinline__ void load_step(StepRegs &R, const ChunkArgs &A, const Item &I, int c, int lane, int part,
+                                          bool stage_s0)
 {
     const int n = min(C, I.len - c * C);
     const size_t t0 = (size_t)I.t0 + (size_t)c * C;
@@ -505,15 +525,21 @@ __device__ __forceinline__ void load_step(StepRegs &R, const ChunkArgs &A, const
 #pragma unroll
     for (int j = 0; j < 4; ++j) {               // 4 rows x 16 lanes per instruction
         const int idx = j * 64 + lane, row = rb + (idx >> 4), c8 = idx & 15;
-        R.kv[j] = buf_load(rk, row * kq_row + c8 * 16);
-        R.qv[j] = buf_load(rq, row * kq_row + c8 * 16);
+        R.kv[j] = R.qv[j] = make_uint4(0, 0, 0, 0);
+        if (row < n) {
+            R.kv[j] = buf_load(rk, row * kq_row + c8 * 16);
+            R.qv[j] = buf_load(rq, row * kq_row + c8 * 16);
+        }
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {               // 8 rows x 8 lanes per instruction
         const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
-        R.tv[j] = buf_load(rt, row * C * 2 + c8 * 16);
-        R.pv[j] = buf_load(rp, row * C * 2 + c8 * 16);
-        R.vv[j] = buf_load(rv, row * v_row + c8 * 16);
+        R.tv[j] = R.pv[j] = R.vv[j] = make_uint4(0, 0, 0, 0);
+        if (row < n) {
+            R.tv[j] = buf_load(rt, row * C * 2 + c8 * 16);
+            R.pv[j] = buf_load(rp, row * C * 2 + c8 * 16);
+            R.vv[j] = buf_load(rv, row * v_row + c8 * 16);
+        }
     }
     R.a_raw = 1.f;
     R.b_raw = 0.f;
@@ -522,7 +548,8 @@ __device__ __forceinline__ void load_step(StepRegs &R, const ChunkArgs &A, const
         R.a_raw = A.a[(t0 + rr) * A.Hv + I.h];
         R.b_raw = A.b[(t0 + rr) * A.Hv + I.h];
     }
-    if (c == 0) {
+    R.s0_write = c == 0 && stage_s0;
+    if (R.s0_write) {
         // dv rows [16 part, +16) of the slice, 32 lanes x 16 B per row
         const float *S0 = item_s0(A, I);
 #pragma unroll
@@ -573,7 +600,7 @@ __device__ __forceinline__ void write_step(ChunkBuf &B, float *s0, StepRegs &R, 
         B.gsh[lane] = __expf(la);
         B.dsh[lane] = __expf(last - la);
     }
-    if (c == 0) {
+    if (c == 0 && R.s0_write) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int idx = j * 64 + lane, row = part * 16 + (idx >> 5), c4 = idx & 31;
@@ -589,9 +616,15 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
     float *s0buf = reinterpret_cast<float *>(smem + 2 * sizeof(ChunkBuf));
     if (ldc(A.header, H_STATUS) != FK_OK) return;
     // item ids: (segment rank, v-head, dv slice), slice fastest
-    const int n_items = ldc(A.header, H_LEVEL0 + A.level) * A.Hv * NSL;
-    const int stride = gridDim.x;
-    if ((int)blockIdx.x >= n_items) return;
+    Walk W;
+    W.nseg = ldc(A.header, H_LEVEL0 + A.level);
+    W.n_items = W.nseg * A.Hv * NSL;
+    W.G = gridDim.x;
+    W.runs = W.n_items >= 4 * W.G;
+    W.per = (W.n_items + W.G - 1) / W.G;
+    const int n_items = W.n_items;
+    const int b0 = item_id(W, blockIdx.x, 0);
+    if (b0 >= n_items) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int G = lane >> 4, c16 = lane & 15;
 
@@ -604,18 +637,29 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
         const int part = w - CONSUMERS;
         StepRegs R;
         int c = 0;
-        Item cur = item_at(A, blockIdx.x);
+        Item cur = item_at(A, W, b0);
         // the item after the last one handed to a step, looked up one item
         // ahead so its (dependent) scalar loads are long done when it is used
         int la_k = 1;
-        int la_it = item_id(blockIdx.x, la_k, stride);
-        Item la = la_it < n_items ? item_at(A, la_it) : cur;
+        int la_it = item_id(W, blockIdx.x, la_k);
+        Item la = la_it < n_items ? item_at(A, W, la_it) : cur;
         auto take = [&](Item &I) {
             I = la;
-            la_it = item_id(blockIdx.x, ++la_k, stride);
-            if (la_it < n_items) la = item_at(A, la_it);
+            la_it = item_id(W, blockIdx.x, ++la_k);
+            if (la_it < n_items) la = item_at(A, W, la_it);
         };
-        load_step(R, A, cur, 0, lane, part);
+        // the entering state staged last (in item order): a sibling entering
+        // from the same state on the same head and slice finds it in LDS
+        int ls_src = 0, ls_h = -1, ls_dv0 = -1;
+        auto stage = [&](const Item &I, int cc) {
+            if (cc != 0) return false;
+            const bool same = I.src == ls_src && I.h == ls_h && I.dv0 == ls_dv0;
+            ls_src = I.src;
+            ls_h = I.h;
+            ls_dv0 = I.dv0;
+            return !same;
+        };
+        load_step(R, A, cur, 0, lane, part, stage(cur, 0));
         write_step(buf[0], s0buf, R, cur, 0, lane, part);
         // step 1 into registers
         int c1 = 1;
@@ -626,7 +670,7 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
             has1 = la_it < n_items;
             if (has1) take(nx1);
         }
-        if (has1) load_step(R, A, nx1, c1, lane, part);
+        if (has1) load_step(R, A, nx1, c1, lane, part, stage(nx1, c1));
         __syncthreads();
         Item prev = cur;
         int pc = -1;
@@ -647,7 +691,7 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
                 if (pc >= 0) flush_out(Bn, A, prev, pc, lane, part);
                 write_step(Bn, s0buf, R, nx1, c1, lane, part);
             }
-            if (has2) load_step(R, A, nx2, c2, lane, part);
+            if (has2) load_step(R, A, nx2, c2, lane, part, stage(nx2, c2));
             __syncthreads();   // step j consumed, step j+1 staged
             if (!has1) {
                 // outputs of steps j-1 and j are still in LDS
@@ -668,7 +712,7 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
     const int wv = w;   // consumer wave: dv columns [16 w, 16 w + 16) of the slice
     f32x4 st[DK / 16];
     int ik = 0, c = 0;
-    Item cur = item_at(A, blockIdx.x);
+    Item cur = item_at(A, W, b0);
     Emits E = item_emits(A, cur);
     const size_t SZ = (size_t)DV * DK;
     __syncthreads();
@@ -677,12 +721,12 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
         const int dvc = cur.dv0 + wv * 16 + c16;   // this lane's state column (dv index)
         const bool last = c + 1 == cur.nch;
         // the next item's metadata, fetched while this step computes
-        const int next_it = item_id(blockIdx.x, ik + 1, stride);
+        const int next_it = item_id(W, blockIdx.x, ik + 1);
         const bool more = !last || next_it < n_items;
         Item nxt = cur;
         Emits nE = E;
         if (last && more) {
-            nxt = item_at(A, next_it);
+            nxt = item_at(A, W, next_it);
             nE = item_emits(A, nxt);
         }
         if (c == 0) {

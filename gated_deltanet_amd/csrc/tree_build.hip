@@ -312,14 +312,17 @@ __device__ void tile_order_block(const int32_t *__restrict__ header, const int32
     for (int t = threadIdx.x; t < n; t += blockDim.x) tile_order[atomicAdd(&cnt[bucket(t)], 1)] = t;
 }
 
-// Each level's live segments by decreasing number of GDN chunks (one block
-// per level; a bucket sort, order within a bucket is whatever the atomics
-// give).  Only the schedule of a level's launch depends on it: the chunk walk
-// deals the longest items out first, in a back-and-forth order, so the
-// level ends evenly; every item computes the same way in any order.
+// Each level's live segments in the order the GDN chunk walk deals them out
+// (one block per level; a bucket sort, order within a bucket is whatever the
+// atomics give).  Level 0 (roots): by decreasing number of chunks, so the
+// longest items start first.  Deeper levels: grouped by entering state
+// (fork point, or the cached history's state slot), so siblings that start
+// from the same state are adjacent and a work-group stages it once.  Only
+// the schedule of a level's launch depends on it; every item computes the
+// same way in any order.
 __device__ void level_order_block(int lvl, const int32_t *__restrict__ header, const int32_t *__restrict__ lvl_seg,
-                                  const int32_t *__restrict__ seg_len, int level_cap, int32_t *__restrict__ lvl_sorted,
-                                  int *cnt, int *lds)
+                                  const int32_t *__restrict__ seg_len, const int32_t *__restrict__ seg_src,
+                                  int level_cap, int32_t *__restrict__ lvl_sorted, int *cnt, int *lds)
 {
     const int n = header[H_LEVEL0 + lvl];
     if (n == 0) return;
@@ -327,7 +330,11 @@ __device__ void level_order_block(int lvl, const int32_t *__restrict__ header, c
     int32_t *dst = lvl_sorted + (size_t)lvl * level_cap;
     for (int b = threadIdx.x; b < ORDER_BUCKETS; b += blockDim.x) cnt[b] = 0;
     __syncthreads();
-    auto bucket = [&](int i) { return min((seg_len[src[i]] + FK_GDN_CHUNK - 1) / FK_GDN_CHUNK, ORDER_BUCKETS - 1); };
+    auto bucket = [&](int i) {
+        if (lvl == 0) return min((seg_len[src[i]] + FK_GDN_CHUNK - 1) / FK_GDN_CHUNK, ORDER_BUCKETS - 1);
+        const int e = seg_src[src[i]];   // >= 0 fork slot, <= -2 state_in slot
+        return (e >= 0 ? e : -2 - e) % ORDER_BUCKETS;
+    };
     for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&cnt[bucket(i)], 1);
     __syncthreads();
     const int b0 = ORDER_BUCKETS - 1 - 2 * threadIdx.x, b1 = b0 - 1;
@@ -346,7 +353,7 @@ __global__ void __launch_bounds__(BUILD_THREADS)
 k_orders(const int32_t *__restrict__ header, const int32_t *__restrict__ tile_seg,
          const int32_t *__restrict__ tile_row0, const int32_t *__restrict__ seg_pos0,
          const int32_t *__restrict__ seg_len, int32_t *__restrict__ tile_order, const int32_t *__restrict__ lvl_seg,
-         int level_cap, int32_t *__restrict__ lvl_sorted)
+         const int32_t *__restrict__ seg_src, int level_cap, int32_t *__restrict__ lvl_sorted)
 {
     __shared__ int cnt[ORDER_BUCKETS];
     __shared__ int lds[32];
@@ -354,7 +361,7 @@ k_orders(const int32_t *__restrict__ header, const int32_t *__restrict__ tile_se
     if (blockIdx.x == 0)
         tile_order_block(header, tile_seg, tile_row0, seg_pos0, seg_len, tile_order, cnt, lds);
     else
-        level_order_block(blockIdx.x - 1, header, lvl_seg, seg_len, level_cap, lvl_sorted, cnt, lds);
+        level_order_block(blockIdx.x - 1, header, lvl_seg, seg_len, seg_src, level_cap, lvl_sorted, cnt, lds);
 }
 
 // Phase 3 (pages): one block per segment checks the page ids the segment
@@ -476,7 +483,7 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
         if ((rc = launch_status())) return rc;
         k_orders<<<(unsigned)(1 + meta->max_depth), BUILD_THREADS, 0, st>>>(
             A.header, A.tile_seg, A.tile_row0, A.seg_pos0, A.seg_len, ws_at<int32_t>(ws, L.tile_order), A.lvl_seg,
-            meta->level_cap, ws_at<int32_t>(ws, L.lvl_sorted));
+            ws_at<int32_t>(ws, L.seg_src), meta->level_cap, ws_at<int32_t>(ws, L.lvl_sorted));
         if ((rc = launch_status())) return rc;
     }
     return FK_OK;
