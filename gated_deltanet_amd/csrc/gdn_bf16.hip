@@ -192,7 +192,7 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
             __bf16 p4[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) p4[r] = (__bf16)acc[r];
-            if (valid)
+            if (valid && i < n)   // rows past the chunk's last token are never read
                 *reinterpret_cast<uint2 *>(pdst + i * C + perm_off(jt * 16 + G * 4)) = __builtin_bit_cast(uint2, p4);
         }
     }
@@ -291,7 +291,7 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     put(3, 1, t31);
     put(3, 0, t30);
     __syncthreads();
-    if (!valid) return;
+    if (!valid || lane >= n) return;   // rows past the chunk's last token are never read
     // row `lane` of T, stored permuted (both T and P serve as A operands)
     uint16_t *dst = tmat + (((size_t)c * Hv + h) * C + lane) * C;
 #pragma unroll
@@ -310,10 +310,9 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
 
 // ---------------------------------------------------------------------------
 // Chunk walk of one tree level, persistent: item = (segment, v-head, 64-wide
-// dv slice), segments taken by decreasing chunk count; work-group b runs the
-// items b, 2G-1-b, 2G+b, 4G-1-b, ... (G = grid size: forward and backward in
-// turn, so the longest items pair with the shortest), and within an item its
-// chunks in order -- one flat sequence of steps.  Waves 0-3 (consumers) own the state slice and run the
+// dv slice), dealt to the work-groups as `Walk` describes; a work-group runs
+// its items, and within an item its chunks, in order -- one flat sequence of
+// steps.  Waves 0-3 (consumers) own the state slice and run the
 // state-dependent products of step j; waves 4-7 (producers) meanwhile write
 // step j+1 (already in their registers) into the other LDS buffer, issue the
 // global loads of step j+2, and store the output of step j-1 that the
