@@ -171,16 +171,124 @@ __device__ __forceinline__ bool cursor_next(BlockCursor &c, const TileCtx &t)
     return true;
 }
 
-// READOUT (selective readout, Flide section 3.3.3): work item = (selected
-// row, kv head) instead of (tile, kv head).
-// The work-group runs the tile that holds the selected token exactly as the
-// full launch does, but only the wave that owns the token computes, its
-// other rows read zero queries, and only the token's 8 rows are stored --
-// so a readout row has the same bits as the same row of the full launch.
-template <int RULE, bool READOUT>
+// Epilogue: the row's sum is split over the two halves of the wave; a valid
+// row stores O / l as bf16 (registers 4*rq .. 4*rq+3 of tile i hold dims
+// 32*i + 8*rq + 4*half + [0, 4)).
+__device__ __forceinline__ void store_rows(const f32x16 (&o)[D / 32], float l, bool row_valid, uint16_t *orow,
+                                           int half)
+{
+    const float lsum = pair_sum(l);
+    if (!row_valid) return;
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            uint2 packed;
+            __bf16 b4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b4[e] = (__bf16)(o[i][rq * 4 + e] * inv);
+            packed.x = (uint32_t)__builtin_bit_cast(uint16_t, b4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, b4[1]) << 16);
+            packed.y = (uint32_t)__builtin_bit_cast(uint16_t, b4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, b4[3]) << 16);
+            *reinterpret_cast<uint2 *>(orow + i * 32 + rq * 8 + half * 4) = packed;
+        }
+}
+
+// One key block for one wave's 32 rows: S^T = K . Q^T on MFMA, masking (only
+// when the block is not `full` for every row of the wave: hi / lo = last /
+// first visible key offset of the lane's row within the block, minus
+// 8 * half), online softmax with the per-row lazy rescale, O^T += V^T . P^T.
+template <int RULE>
+__device__ __forceinline__ void block_compute(const uint16_t *kl, const uint16_t *vl, const bf16x8 (&qf)[D / 16],
+                                              f32x16 (&o)[D / 32], float &m, float &l, bool full, int hi, int lo,
+                                              int prow, int half, int n, float scale_log2e)
+{
+    // S^T = K . Q^T
+    f32x16 sacc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+    {
+        const uint16_t *krow = kl + prow * K_STRIDE + half * 8;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + mt * 32 * K_STRIDE + ks * 16));
+                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
+            }
+        // keep LOOKAHEAD operand reads in flight ahead of the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);
+#pragma unroll
+        for (int j = 0; j < 8 * MT - LOOKAHEAD; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, LOOKAHEAD, 0);
+    }
+    // mask: register r of tile mt holds key 32*mt + 16*(r/8) + 8*half + r%8
+    // of the block; masked in place unless the block is `full`
+    if (!full) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int koff = mt * 32 + (r / 8) * 16 + (r % 8);
+                bool vis = koff <= hi;
+                if (RULE == WINDOW) vis = vis && koff >= lo;
+                sacc[mt][r] = vis ? sacc[mt][r] : -INFINITY;
+            }
+    }
+    // row max on raw scores (scale > 0); the two wave halves hold disjoint
+    // keys of the same row and swap maxima with one permlane
+    float mloc = sacc[0][0];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = (mt == 0 ? 1 : 0); r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[mt][r]);
+    const float mrow = pair_max(mloc) * scale_log2e;
+    // lazy rescale: a row moves its reference max only when the block's
+    // max exceeds it by more than RESCALE_LOG2 (the exponents then stay
+    // <= 2^RESCALE_LOG2); rows that do not move multiply by exactly 1
+    const bool need = mrow > m + RESCALE_LOG2;
+    if (__any(need)) {   // wave-uniform branch
+        const float mnew = need ? mrow : m;
+        const float corr = __builtin_amdgcn_exp2f(m - mnew);
+        l *= corr;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) o[i] *= corr;
+        m = mnew;
+    }
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 pf[2 * MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][hh * 8 + e], scale_log2e, -m));
+                ps[e & 3] += pv[e];
+            }
+            pf[mt * 2 + hh] = as_bf16x8(pack8(pv));
+        }
+    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    // O^T += V^T . P^T ; k-step kk covers keys 16*kk + [0, 16)
+    {
+        const uint16_t *vrow = vl + n * V_STRIDE + half * 8;
+#pragma unroll
+        for (int kk = 0; kk < 2 * MT; ++kk)
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) {
+                const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + i * 32 * V_STRIDE + kk * 16));
+                o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[i], 0, 0, 0);
+            }
+    }
+}
+
+template <int RULE>
 __global__ void __launch_bounds__(THREADS, 3)
 k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, int window,
-            const int32_t *__restrict__ sel_rows, const int32_t *__restrict__ tok_seg, int T,
             const int32_t *__restrict__ seg_pos0, const uint16_t *__restrict__ kp,
             const uint16_t *__restrict__ vp, uint16_t *__restrict__ out, const int32_t *__restrict__ header,
             const int32_t *__restrict__ tile_seg, const int32_t *__restrict__ tile_row0,
@@ -197,28 +305,15 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     const int rank = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int half = lane >> 5, n = lane & 31;
-    int s, row0, sel_local = 0;
-    if (READOUT) {
-        const int t = sel_rows[rank];
-        if (t < 0 || t >= T) return;   // an unused entry of the row buffer
-        s = tok_seg[t];
-        sel_local = t - seg_start[s];
-        row0 = sel_local & ~(FK_TILE_TOKENS - 1);
-    } else {
-        if (rank >= header[H_NTILES]) return;
-        const int tile = tile_order[rank];
-        s = tile_seg[tile];
-        row0 = tile_row0[tile];
-    }
+    if (rank >= header[H_NTILES]) return;
+    const int tile = tile_order[rank];
+    const int s = tile_seg[tile], row0 = tile_row0[tile];
     const int len = seg_len[s];
     const int tok = row0 + w * 4 + n / 8;          // local token of this lane's row
     const int h = g * G + (n % 8);
-    const bool row_valid = READOUT ? tok == sel_local : tok < len;
-    // the wave that owns the selected token (all waves in a full launch)
-    const bool active = !READOUT || w == ((sel_local - row0) >> 2);
+    const bool row_valid = tok < len;
     const size_t t_glob = (size_t)seg_start[s] + tok;
-    // query / output row: the stream token, or the row buffer's entry
-    const size_t qrow = READOUT ? (size_t)rank * Hq + h : t_glob * Hq + h;
+    const size_t qrow = t_glob * Hq + h;
 
     // Q^T as the B operand: lane holds its row's dims 16*ks + 8*half + [0, 8)
     bf16x8 qf[D / 16];
@@ -266,122 +361,179 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
         const bool more = cursor_next<RULE>(nxt, tc);
         BlockRegs R;
         if (more) load_block(R, kp, vp, nxt.plist, nxt.key0, nxt.count, g, Hkv);
-        if (active) {   // wave-uniform
+        {
             const int key0 = cur.key0, count = cur.count, pdiff = cur.pdiff;
             const bool own = cur.own;
-            const uint16_t *kl = k_lds[buf], *vl = v_lds[buf];
-            // S^T = K . Q^T
-            f32x16 sacc[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
-            {
-                const uint16_t *krow = kl + prow * K_STRIDE + half * 8;
-    #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks)
-    #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + mt * 32 * K_STRIDE + ks * 16));
-                        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
-                    }
-                // keep LOOKAHEAD operand reads in flight ahead of the MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, LOOKAHEAD, 0);
-    #pragma unroll
-                for (int j = 0; j < 8 * MT - LOOKAHEAD; ++j) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, LOOKAHEAD, 0);
-            }
-            // mask: register r of tile mt holds key 32*mt + 16*(r/8) + 8*half + r%8
-            // of the block.  Only blocks that cross the diagonal, the end of a
-            // visible range or the window's edge are masked, in place.  hi / lo:
-            // last / first visible key offset within the block, minus 8 * half.
+            // Only blocks that cross the diagonal, the end of a visible range or
+            // the window's edge are masked.
             const bool causal_own = own && RULE != TWO_WAY;
             const int hi = (causal_own ? tok - key0 : count - 1 - key0) - half * 8;
             const int lo = (RULE == WINDOW ? pdiff + tok - window + 1 - key0 : 0) - half * 8;
             const bool full = (causal_own ? (key0 + BN - 1 <= row0) : (key0 + BN <= count)) &&
                               (RULE != WINDOW || key0 >= pdiff + row0 + FK_TILE_TOKENS - window);
-            if (!full) {
-    #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-    #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int koff = mt * 32 + (r / 8) * 16 + (r % 8);
-                        bool vis = koff <= hi;
-                        if (RULE == WINDOW) vis = vis && koff >= lo;
-                        sacc[mt][r] = vis ? sacc[mt][r] : -INFINITY;
-                    }
-            }
-            // row max on raw scores (scale > 0); the two wave halves hold disjoint
-            // keys of the same row and swap maxima with one permlane
-            float mloc = sacc[0][0];
-    #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-    #pragma unroll
-                for (int r = (mt == 0 ? 1 : 0); r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[mt][r]);
-            const float mrow = pair_max(mloc) * scale_log2e;
-            // lazy rescale: a row moves its reference max only when the block's
-            // max exceeds it by more than RESCALE_LOG2 (the exponents then stay
-            // <= 2^RESCALE_LOG2); rows that do not move multiply by exactly 1
-            const bool need = mrow > m + RESCALE_LOG2;
-            if (__any(need)) {   // wave-uniform branch
-                const float mnew = need ? mrow : m;
-                const float corr = __builtin_amdgcn_exp2f(m - mnew);
-                l *= corr;
-    #pragma unroll
-                for (int i = 0; i < D / 32; ++i) o[i] *= corr;
-                m = mnew;
-            }
-            float ps[4] = {0.f, 0.f, 0.f, 0.f};
-            bf16x8 pf[2 * MT];
-    #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-    #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    float pv[8];
-    #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][hh * 8 + e], scale_log2e, -m));
-                        ps[e & 3] += pv[e];
-                    }
-                    pf[mt * 2 + hh] = as_bf16x8(pack8(pv));
-                }
-            l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-            // O^T += V^T . P^T ; k-step kk covers keys 16*kk + [0, 16)
-            {
-                const uint16_t *vrow = vl + n * V_STRIDE + half * 8;
-    #pragma unroll
-                for (int kk = 0; kk < 2 * MT; ++kk)
-    #pragma unroll
-                    for (int i = 0; i < D / 32; ++i) {
-                        const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + i * 32 * V_STRIDE + kk * 16));
-                        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[i], 0, 0, 0);
-                    }
-            }
+            block_compute<RULE>(k_lds[buf], v_lds[buf], qf, o, m, l, full, hi, lo, prow, half, n, scale_log2e);
         }
         if (!more) break;
         store_block(k_lds[buf ^ 1], v_lds[buf ^ 1], R);
         cur = nxt;
         __syncthreads();   // next block staged; this buffer free for reuse
     }
-    // epilogue: the row's sum is split over the two halves of the wave
-    const float lsum = pair_sum(l);
-    if (!row_valid) return;
-    const float inv = 1.f / lsum;
-    uint16_t *orow = out + qrow * D;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            // registers 4*rq .. 4*rq+3 hold dims 32*i + 8*rq + 4*half + [0, 4)
-            uint2 packed;
-            __bf16 b4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) b4[e] = (__bf16)(o[i][rq * 4 + e] * inv);
-            packed.x = (uint32_t)__builtin_bit_cast(uint16_t, b4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, b4[1]) << 16);
-            packed.y = (uint32_t)__builtin_bit_cast(uint16_t, b4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, b4[3]) << 16);
-            *reinterpret_cast<uint2 *>(orow + i * 32 + rq * 8 + half * 4) = packed;
+    store_rows(o, l, row_valid, out + qrow * D, half);
+}
+
+// Selective readout (Flide section 3.3.3): work item = (group of up to 16
+// entries of the row buffer, kv head).  The group's entries take the 16 token
+// slots of a tile (wave w: slots 4w .. 4w+3, 8 q heads each), and the key walk
+// covers the union of their chains: depth by depth, every distinct segment
+// met at that depth, up to the largest count any entry sees of it.  A row
+// masks what its own chain does not show -- blocks off its chain or past its
+// limit contribute exactly nothing (no key, no max change, zero weights), so
+// each row meets its own chain's blocks in chain order, anchored as in the
+// full launch, and its output has the same bits as that token's row of the
+// full launch, whatever its group.  Grouping only fills the tile's rows: one
+// pass over a shared trunk serves up to 16 questions.
+constexpr int RO_CAND = FK_TILE_TOKENS * FK_MAX_DEPTH;   // (slot, depth) candidates
+
+template <int RULE>
+__global__ void __launch_bounds__(THREADS, 3)
+k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restrict__ sel_rows, int n_rows,
+                    int group, int Hq, int Hkv, float scale_log2e, int window, const int32_t *__restrict__ tok_seg,
+                    int T, const int32_t *__restrict__ seg_pos0, const uint16_t *__restrict__ kp,
+                    const uint16_t *__restrict__ vp, uint16_t *__restrict__ out_rows,
+                    const int32_t *__restrict__ header, const int32_t *__restrict__ seg_start,
+                    const int32_t *__restrict__ seg_len, const int32_t *__restrict__ seg_depth,
+                    const int32_t *__restrict__ seg_anc, const int32_t *__restrict__ seg_fork,
+                    const int32_t *__restrict__ page_off, const int32_t *__restrict__ pages)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][K_LDS];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][V_LDS];
+    __shared__ int c_seg[RO_CAND], c_lim[RO_CAND], c_lo[RO_CAND];   // per (slot, depth)
+    __shared__ int r_seg[RO_CAND], r_depth[RO_CAND], r_count[RO_CAND], r_key0[RO_CAND];
+    __shared__ int n_ranges;
+    if (header[H_STATUS] != FK_OK) return;
+    const int grp = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int half = lane >> 5, n = lane & 31;
+
+    // candidate (slot ci / FK_MAX_DEPTH, depth ci % FK_MAX_DEPTH): the segment
+    // that slot's entry meets at that depth, how many of its keys the entry
+    // sees, and (window) the first one inside the entry's window
+    if (threadIdx.x < RO_CAND) {
+        const int ci = threadIdx.x, slot = ci / FK_MAX_DEPTH, cd = ci % FK_MAX_DEPTH;
+        const int e = grp * group + slot;
+        int cseg = -1, clim = 0, clo = 0;
+        const int t = (slot < group && e < n_rows) ? sel_rows[e] : -1;
+        if (t >= 0 && t < T) {
+            const int cs = tok_seg[t], cdep = seg_depth[cs];
+            if (cd <= cdep) {
+                const int32_t *ca = seg_anc + (size_t)cs * FK_MAX_DEPTH;
+                const int cloc = t - seg_start[cs];
+                cseg = ca[cd];
+                clim = cd == cdep ? (RULE == TWO_WAY ? seg_len[cs] : cloc + 1) : seg_fork[ca[cd + 1]];
+                if (RULE == WINDOW) clo = max(0, seg_pos0[cs] + cloc - seg_pos0[cseg] - window + 1);
+            }
         }
+        c_seg[ci] = cseg;
+        c_lim[ci] = clim;
+        c_lo[ci] = clo;
+    }
+    __syncthreads();
+    // one range per distinct segment of a depth, in (depth, first slot) order
+    if (threadIdx.x == 0) {
+        int nr = 0;
+        for (int cd = 0; cd < FK_MAX_DEPTH; ++cd)
+            for (int slot = 0; slot < FK_TILE_TOKENS; ++slot) {
+                const int a = c_seg[slot * FK_MAX_DEPTH + cd];
+                if (a < 0) continue;
+                bool seen = false;
+                int cnt = 0, lo = 0x7fffffff;
+                for (int o2 = 0; o2 < FK_TILE_TOKENS; ++o2) {
+                    if (c_seg[o2 * FK_MAX_DEPTH + cd] != a) continue;
+                    if (o2 < slot) seen = true;
+                    cnt = max(cnt, c_lim[o2 * FK_MAX_DEPTH + cd]);
+                    lo = min(lo, c_lo[o2 * FK_MAX_DEPTH + cd]);
+                }
+                const int key0 = RULE == WINDOW ? (lo / BN) * BN : 0;
+                if (seen || key0 >= cnt) continue;
+                r_seg[nr] = a;
+                r_depth[nr] = cd;
+                r_count[nr] = cnt;
+                r_key0[nr] = key0;
+                ++nr;
+            }
+        n_ranges = nr;
+    }
+    __syncthreads();
+    const int nr = n_ranges;
+    if (nr == 0) return;   // no used entry in this group
+
+    // this lane's row: entry of slot w*4 + n/8, q head g*G + n%8
+    const int slot = w * 4 + n / 8, e = grp * group + slot;
+    const int t = (slot < group && e < n_rows) ? sel_rows[e] : -1;
+    const bool row_valid = t >= 0 && t < T;
+    const int s = row_valid ? tok_seg[t] : 0;
+    const int local = row_valid ? t - seg_start[s] : 0, depth = row_valid ? seg_depth[s] : -1;
+    const int own_lim = RULE == TWO_WAY ? seg_len[s] : local + 1;
+    const int32_t *anc = seg_anc + (size_t)s * FK_MAX_DEPTH;
+    const int pos0 = seg_pos0[s];
+    const int h = g * G + (n % 8);
+    const size_t qrow = (size_t)e * Hq + h;
+    const bool wave_has_rows = __any(row_valid);
+
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (row_valid) u = *reinterpret_cast<const uint4 *>(q_rows + qrow * D + ks * 16 + half * 8);
+        qf[ks] = as_bf16x8(u);
+    }
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+    float m = -1e30f, l = 0.f;
+    const int prow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+
+    // the lane's visible keys [lo_r, lim_r) of range ri (none off its chain)
+    int lim_r = 0, lo_r = 0;
+    auto lane_range = [&](int ri) {
+        const int a = r_seg[ri], dd = r_depth[ri];
+        const bool on = row_valid && dd <= depth && anc[dd] == a;
+        lim_r = on ? (dd == depth ? own_lim : seg_fork[anc[dd + 1]]) : 0;
+        lo_r = (RULE == WINDOW && on) ? pos0 + local - seg_pos0[a] - window + 1 : 0;
+    };
+    int ri = 0, key0 = r_key0[0];
+    lane_range(0);
+    {
+        BlockRegs R;
+        load_block(R, kp, vp, pages + page_off[r_seg[0]], key0, r_count[0], g, Hkv);
+        store_block(k_lds[0], v_lds[0], R);
+    }
+    __syncthreads();
+    for (int buf = 0;; buf ^= 1) {
+        int nri = ri, nkey0 = key0 + BN;
+        bool more = true;
+        if (nkey0 >= r_count[ri]) {
+            nri = ri + 1;
+            more = nri < nr;
+            if (more) nkey0 = r_key0[nri];
+        }
+        BlockRegs R;
+        if (more) load_block(R, kp, vp, pages + page_off[r_seg[nri]], nkey0, r_count[nri], g, Hkv);
+        if (wave_has_rows) {   // wave-uniform
+            const bool lane_full = !row_valid || (key0 + BN <= lim_r && (RULE != WINDOW || key0 >= lo_r));
+            const bool full = __all(lane_full);
+            const int hi = lim_r - 1 - key0 - half * 8;
+            const int lo = (RULE == WINDOW ? lo_r - key0 : 0) - half * 8;
+            block_compute<RULE>(k_lds[buf], v_lds[buf], qf, o, m, l, full, hi, lo, prow, half, n, scale_log2e);
+        }
+        if (!more) break;
+        store_block(k_lds[buf ^ 1], v_lds[buf ^ 1], R);
+        if (nri != ri) lane_range(nri);
+        ri = nri;
+        key0 = nkey0;
+        __syncthreads();   // next block staged; this buffer free for reuse
+    }
+    store_rows(o, l, row_valid, out_rows + qrow * D, half);
 }
 
 }  // namespace attn
@@ -389,43 +541,54 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
 
 using namespace fk;
 
-template <int RULE, bool READOUT>
+template <int RULE>
 static void launch_rule(const fk_tree_meta *meta, const WsLayout &L, const void *q, int Hq, int Hkv, float scale,
-                        int window, const int32_t *rows, int n_rows, const void *k_pool, const void *v_pool,
-                        void *out, const void *ws, hipStream_t st)
+                        int window, const int32_t *rows, int n_rows, int group, const void *k_pool,
+                        const void *v_pool, void *out, const void *ws, hipStream_t st)
 {
-    dim3 grid((unsigned)((READOUT ? (int64_t)n_rows : L.tile_cap) * Hkv));
-    attn::k_attn_bf16<RULE, READOUT><<<grid, attn::THREADS, 0, st>>>(
-        (const uint16_t *)q, Hq, Hkv, scale * 1.4426950408889634f, window, rows, meta->tok_seg, meta->T,
-        ws_at<int32_t>(ws, L.seg_pos0),
-        (const uint16_t *)k_pool,
+    const float sl = scale * 1.4426950408889634f;
+    if (rows) {
+        const int64_t groups = (n_rows + group - 1) / group;
+        attn::k_attn_readout_bf16<RULE><<<dim3((unsigned)(groups * Hkv)), attn::THREADS, 0, st>>>(
+            (const uint16_t *)q, rows, n_rows, group, Hq, Hkv, sl, window, meta->tok_seg, meta->T,
+            ws_at<int32_t>(ws, L.seg_pos0), (const uint16_t *)k_pool, (const uint16_t *)v_pool, (uint16_t *)out,
+            ws_at<int32_t>(ws, L.header), ws_at<int32_t>(ws, L.seg_start), ws_at<int32_t>(ws, L.seg_len),
+            ws_at<int32_t>(ws, L.seg_depth), ws_at<int32_t>(ws, L.seg_anc), meta->seg_fork, meta->seg_page_off,
+            meta->seg_pages);
+        return;
+    }
+    attn::k_attn_bf16<RULE><<<dim3((unsigned)(L.tile_cap * Hkv)), attn::THREADS, 0, st>>>(
+        (const uint16_t *)q, Hq, Hkv, sl, window, ws_at<int32_t>(ws, L.seg_pos0), (const uint16_t *)k_pool,
         (const uint16_t *)v_pool, (uint16_t *)out, ws_at<int32_t>(ws, L.header), ws_at<int32_t>(ws, L.tile_seg),
         ws_at<int32_t>(ws, L.tile_row0), ws_at<int32_t>(ws, L.tile_order), ws_at<int32_t>(ws, L.seg_start),
-        ws_at<int32_t>(ws, L.seg_len),
-        ws_at<int32_t>(ws, L.seg_depth), ws_at<int32_t>(ws, L.seg_anc), meta->seg_fork, meta->seg_page_off,
-        meta->seg_pages);
+        ws_at<int32_t>(ws, L.seg_len), ws_at<int32_t>(ws, L.seg_depth), ws_at<int32_t>(ws, L.seg_anc),
+        meta->seg_fork, meta->seg_page_off, meta->seg_pages);
 }
 
 // rows == NULL: the full launch over the round's tiles; otherwise readout of
-// the n_rows entries of `rows` (q and out then hold one row per entry)
+// the n_rows entries of `rows` (q and out then hold one row per entry),
+// grouped so that the launch fills about three work-groups per compute unit
 int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv, float scale, int rule, int window,
                         const int32_t *rows, int n_rows, const void *k_pool, const void *v_pool, void *out,
                         const void *ws, hipStream_t st)
 {
     const WsLayout L = ws_layout(*meta, 0, 0, 0);
-#define FK_ATTN_LAUNCH(R)                                                                                   \
-    do {                                                                                                   \
-        if (rows)                                                                                          \
-            launch_rule<R, true>(meta, L, q, Hq, Hkv, scale, window, rows, n_rows, k_pool, v_pool, out, ws, st); \
-        else                                                                                               \
-            launch_rule<R, false>(meta, L, q, Hq, Hkv, scale, window, rows, n_rows, k_pool, v_pool, out, ws, st); \
-    } while (0)
+    int group = 1;
+    if (rows) {
+        int dev = 0;
+        FK_HIP(hipGetDevice(&dev));
+        static int n_cu[64] = {0};
+        if (dev < 0 || dev >= 64) return FK_E_HIP;
+        if (!n_cu[dev]) FK_HIP(hipDeviceGetAttribute(&n_cu[dev], hipDeviceAttributeMultiprocessorCount, dev));
+        const int64_t g = (int64_t)n_rows * Hkv / (3 * (int64_t)n_cu[dev]);
+        group = (int)(g < 1 ? 1 : g > FK_TILE_TOKENS ? FK_TILE_TOKENS : g);
+    }
     if (rule == FK_RULE_WINDOW)
-        FK_ATTN_LAUNCH(attn::WINDOW);
+        launch_rule<attn::WINDOW>(meta, L, q, Hq, Hkv, scale, window, rows, n_rows, group, k_pool, v_pool, out, ws, st);
     else if (rule == FK_RULE_TWO_WAY)
-        FK_ATTN_LAUNCH(attn::TWO_WAY);
+        launch_rule<attn::TWO_WAY>(meta, L, q, Hq, Hkv, scale, window, rows, n_rows, group, k_pool, v_pool, out, ws,
+                                   st);
     else
-        FK_ATTN_LAUNCH(attn::CAUSAL);
-#undef FK_ATTN_LAUNCH
+        launch_rule<attn::CAUSAL>(meta, L, q, Hq, Hkv, scale, window, rows, n_rows, group, k_pool, v_pool, out, ws, st);
     return launch_status();
 }

@@ -92,3 +92,24 @@ def test_readout_config3_leaves():
     ref = oracle_attention(inp, tok_sel=sel, head_sel=hsel)
     d = np.abs(o[used][:, ::4] - ref[rows[used]][:, ::4])
     assert d.max() <= 2e-2 and d.mean() <= 2e-3, (d.max(), d.mean())
+
+
+@pytest.mark.parametrize("rule,W", [(FK_RULE_CAUSAL, 0), (FK_RULE_WINDOW, 45), (FK_RULE_TWO_WAY, 0)])
+def test_readout_grouped_mixed_entries(rule, W):
+    """A buffer large enough that entries are grouped 16 to a work-group, in
+    shuffled order (each group mixes tokens of different segments, requests
+    and depths, cached histories included): every entry still equals its row
+    of the full launch bit for bit."""
+    rng = np.random.default_rng(6400)
+    t = random_tree(rng, n_requests=4, p_cached_root=0.4, p_internal_fork=0.4, max_len=100, max_depth=4).flatten()
+    inp = draw_inputs(t, SH["bf16"], 77, "bf16")
+    r = GpuRound(inp).build()
+    full = to_f64(r.attention(rule=rule, window=W))
+    rows = np.concatenate([rng.permutation(t.T) for _ in range(8)]).astype(np.int32)
+    rows[rng.integers(0, len(rows), 50)] = -1
+    print(f"[readout grouped] rule {rule} T={t.T} entries={len(rows)}", flush=True)
+    o = _readout(r, rows, rule, W)
+    assert r.status() == 0
+    used = rows >= 0
+    assert np.isnan(o[~used]).all()
+    assert np.array_equal(o[used], full[rows[used]])
