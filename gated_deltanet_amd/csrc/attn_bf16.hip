@@ -408,6 +408,7 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][K_LDS];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][V_LDS];
     __shared__ int c_seg[RO_CAND], c_lim[RO_CAND], c_lo[RO_CAND];   // per (slot, depth)
+    __shared__ int c_rep[RO_CAND], c_cnt[RO_CAND], c_key0[RO_CAND];
     __shared__ int r_seg[RO_CAND], r_depth[RO_CAND], r_count[RO_CAND], r_key0[RO_CAND];
     __shared__ int n_ranges;
     if (header[H_STATUS] != FK_OK) return;
@@ -415,19 +416,34 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int half = lane >> 5, n = lane & 31;
 
+    // this lane's row: entry of slot w*4 + n/8, q head g*G + n%8; its query
+    // loads are issued first and land while the walk is planned
+    const int slot = w * 4 + n / 8, e = grp * group + slot;
+    const int t = (slot < group && e < n_rows) ? sel_rows[e] : -1;
+    const bool row_valid = t >= 0 && t < T;
+    const int h = g * G + (n % 8);
+    const size_t qrow = (size_t)e * Hq + h;
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (row_valid) u = *reinterpret_cast<const uint4 *>(q_rows + qrow * D + ks * 16 + half * 8);
+        qf[ks] = as_bf16x8(u);
+    }
+
     // candidate (slot ci / FK_MAX_DEPTH, depth ci % FK_MAX_DEPTH): the segment
     // that slot's entry meets at that depth, how many of its keys the entry
     // sees, and (window) the first one inside the entry's window
     if (threadIdx.x < RO_CAND) {
-        const int ci = threadIdx.x, slot = ci / FK_MAX_DEPTH, cd = ci % FK_MAX_DEPTH;
-        const int e = grp * group + slot;
+        const int ci = threadIdx.x, cslot = ci / FK_MAX_DEPTH, cd = ci % FK_MAX_DEPTH;
+        const int ce = grp * group + cslot;
         int cseg = -1, clim = 0, clo = 0;
-        const int t = (slot < group && e < n_rows) ? sel_rows[e] : -1;
-        if (t >= 0 && t < T) {
-            const int cs = tok_seg[t], cdep = seg_depth[cs];
+        const int ct = (cslot < group && ce < n_rows) ? sel_rows[ce] : -1;
+        if (ct >= 0 && ct < T) {
+            const int cs = tok_seg[ct], cdep = seg_depth[cs];
+            const int cloc = ct - seg_start[cs];
             if (cd <= cdep) {
                 const int32_t *ca = seg_anc + (size_t)cs * FK_MAX_DEPTH;
-                const int cloc = t - seg_start[cs];
                 cseg = ca[cd];
                 clim = cd == cdep ? (RULE == TWO_WAY ? seg_len[cs] : cloc + 1) : seg_fork[ca[cd + 1]];
                 if (RULE == WINDOW) clo = max(0, seg_pos0[cs] + cloc - seg_pos0[cseg] - window + 1);
@@ -438,87 +454,97 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
         c_lo[ci] = clo;
     }
     __syncthreads();
-    // one range per distinct segment of a depth, in (depth, first slot) order
+    // a candidate is a range when no earlier slot meets its segment at that
+    // depth; its count / start cover every slot that does
+    int rep = 0, cnt = 0, key0c = 0;
+    if (threadIdx.x < RO_CAND) {
+        const int ci = threadIdx.x, cslot = ci / FK_MAX_DEPTH, cd = ci % FK_MAX_DEPTH;
+        const int a = c_seg[ci];
+        int lo = 0x7fffffff;
+        rep = a >= 0;
+        if (a >= 0)
+            for (int o2 = 0; o2 < FK_TILE_TOKENS; ++o2) {
+                const int oi = o2 * FK_MAX_DEPTH + cd;
+                if (c_seg[oi] != a) continue;
+                if (o2 < cslot) rep = 0;
+                cnt = max(cnt, c_lim[oi]);
+                lo = min(lo, c_lo[oi]);
+            }
+        key0c = RULE == WINDOW ? (lo / BN) * BN : 0;
+        if (rep && key0c >= cnt) rep = 0;
+    }
+    if (threadIdx.x < RO_CAND) {
+        c_rep[threadIdx.x] = rep;
+        c_cnt[threadIdx.x] = cnt;
+        c_key0[threadIdx.x] = key0c;
+    }
+    __syncthreads();
+    // ranges in (depth, first slot) order
     if (threadIdx.x == 0) {
         int nr = 0;
         for (int cd = 0; cd < FK_MAX_DEPTH; ++cd)
-            for (int slot = 0; slot < FK_TILE_TOKENS; ++slot) {
-                const int a = c_seg[slot * FK_MAX_DEPTH + cd];
-                if (a < 0) continue;
-                bool seen = false;
-                int cnt = 0, lo = 0x7fffffff;
-                for (int o2 = 0; o2 < FK_TILE_TOKENS; ++o2) {
-                    if (c_seg[o2 * FK_MAX_DEPTH + cd] != a) continue;
-                    if (o2 < slot) seen = true;
-                    cnt = max(cnt, c_lim[o2 * FK_MAX_DEPTH + cd]);
-                    lo = min(lo, c_lo[o2 * FK_MAX_DEPTH + cd]);
-                }
-                const int key0 = RULE == WINDOW ? (lo / BN) * BN : 0;
-                if (seen || key0 >= cnt) continue;
-                r_seg[nr] = a;
+            for (int cslot = 0; cslot < FK_TILE_TOKENS; ++cslot) {
+                const int ci = cslot * FK_MAX_DEPTH + cd;
+                if (!c_rep[ci]) continue;
+                r_seg[nr] = c_seg[ci];
                 r_depth[nr] = cd;
-                r_count[nr] = cnt;
-                r_key0[nr] = key0;
+                r_count[nr] = c_cnt[ci];
+                r_key0[nr] = c_key0[ci];
                 ++nr;
             }
         n_ranges = nr;
     }
     __syncthreads();
-    const int nr = n_ranges;
+    // walk values are the same in every lane: keep them scalar, so page ids
+    // are read with scalar loads as in the full launch
+    auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    const int nr = uni(n_ranges);
     if (nr == 0) return;   // no used entry in this group
 
-    // this lane's row: entry of slot w*4 + n/8, q head g*G + n%8
-    const int slot = w * 4 + n / 8, e = grp * group + slot;
-    const int t = (slot < group && e < n_rows) ? sel_rows[e] : -1;
-    const bool row_valid = t >= 0 && t < T;
-    const int s = row_valid ? tok_seg[t] : 0;
-    const int local = row_valid ? t - seg_start[s] : 0, depth = row_valid ? seg_depth[s] : -1;
-    const int own_lim = RULE == TWO_WAY ? seg_len[s] : local + 1;
-    const int32_t *anc = seg_anc + (size_t)s * FK_MAX_DEPTH;
-    const int pos0 = seg_pos0[s];
-    const int h = g * G + (n % 8);
-    const size_t qrow = (size_t)e * Hq + h;
     const bool wave_has_rows = __any(row_valid);
 
-    bf16x8 qf[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (row_valid) u = *reinterpret_cast<const uint4 *>(q_rows + qrow * D + ks * 16 + half * 8);
-        qf[ks] = as_bf16x8(u);
-    }
     f32x16 o[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
     float m = -1e30f, l = 0.f;
     const int prow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
-    // the lane's visible keys [lo_r, lim_r) of range ri (none off its chain)
+    // the lane's visible keys [lo_r, lim_r) of range ri (none off its chain),
+    // from the planning tables in LDS (no global load in the walk)
     int lim_r = 0, lo_r = 0;
     auto lane_range = [&](int ri) {
-        const int a = r_seg[ri], dd = r_depth[ri];
-        const bool on = row_valid && dd <= depth && anc[dd] == a;
-        lim_r = on ? (dd == depth ? own_lim : seg_fork[anc[dd + 1]]) : 0;
-        lo_r = (RULE == WINDOW && on) ? pos0 + local - seg_pos0[a] - window + 1 : 0;
+        const int a = uni(r_seg[ri]), dd = uni(r_depth[ri]);
+        const int ci = slot * FK_MAX_DEPTH + dd;
+        const bool on = row_valid && c_seg[ci] == a;
+        lim_r = on ? c_lim[ci] : 0;
+        lo_r = (RULE == WINDOW && on) ? c_lo[ci] : 0;
     };
-    int ri = 0, key0 = r_key0[0];
+    // the walk position: range ri (its page list and key count held in
+    // registers), block key0; the next block's are looked up one block ahead
+    int ri = 0, key0 = uni(r_key0[0]), count = uni(r_count[0]);
+    const int32_t *plist = pages + uni(page_off[uni(r_seg[0])]);
     lane_range(0);
     {
         BlockRegs R;
-        load_block(R, kp, vp, pages + page_off[r_seg[0]], key0, r_count[0], g, Hkv);
+        load_block(R, kp, vp, plist, key0, count, g, Hkv);
         store_block(k_lds[0], v_lds[0], R);
     }
     __syncthreads();
     for (int buf = 0;; buf ^= 1) {
-        int nri = ri, nkey0 = key0 + BN;
+        int nri = ri, nkey0 = key0 + BN, ncount = count;
+        const int32_t *nplist = plist;
         bool more = true;
-        if (nkey0 >= r_count[ri]) {
+        if (nkey0 >= count) {
             nri = ri + 1;
             more = nri < nr;
-            if (more) nkey0 = r_key0[nri];
+            if (more) {
+                nkey0 = uni(r_key0[nri]);
+                ncount = uni(r_count[nri]);
+                nplist = pages + uni(page_off[uni(r_seg[nri])]);
+            }
         }
         BlockRegs R;
-        if (more) load_block(R, kp, vp, pages + page_off[r_seg[nri]], nkey0, r_count[nri], g, Hkv);
+        if (more) load_block(R, kp, vp, nplist, nkey0, ncount, g, Hkv);
         if (wave_has_rows) {   // wave-uniform
             const bool lane_full = !row_valid || (key0 + BN <= lim_r && (RULE != WINDOW || key0 >= lo_r));
             const bool full = __all(lane_full);
@@ -531,6 +557,8 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
         if (nri != ri) lane_range(nri);
         ri = nri;
         key0 = nkey0;
+        count = ncount;
+        plist = nplist;
         __syncthreads();   // next block staged; this buffer free for reuse
     }
     store_rows(o, l, row_valid, out_rows + qrow * D, half);
