@@ -40,7 +40,7 @@ constexpr int C = FK_GDN_CHUNK;   // 64 tokens
 constexpr int DK = 128, DV = 128;
 constexpr int DVS = 64;           // dv columns of one work-group (4 waves x 16)
 constexpr int KS = DK;            // LDS stride (bf16) of key/query rows (swizzled, unpadded)
-constexpr int TS = C + 8;         // LDS stride (bf16) of 64-wide rows written 16 B at a time (T, P)
+constexpr int RS = C;             // LDS stride (bf16) of 64-wide rows (T, P, values / output), swizzled
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -72,17 +72,28 @@ __device__ __forceinline__ int perm4(int q) { return 8 * (q & 3) + 4 * (q >> 2);
 // element offset, within a row, of the group of four positions starting at p (p % 4 == 0)
 __device__ __forceinline__ int perm_off(int p) { return (p & ~31) + perm4((p >> 2) & 7); }
 
-__device__ __forceinline__ bf16x8 load_perm(const uint16_t *row, int ks, int G)
+// 64-wide rows in LDS (T, P, and the value / output slice): 128 B per row, no
+// padding, the eight 16-byte units of row r XOR-swizzled by r mod 8.  Every
+// access to them -- 16-byte operand reads of 16 rows, 16-byte row writes,
+// transpose reads of 4 rows x 4 columns, 4-byte output writes -- is then free
+// of LDS bank conflicts on gfx950 (measured, not only by bank arithmetic).
+__device__ __forceinline__ int r64_off(int row, int e) { return row * RS + ((((e >> 3) ^ (row & 7)) << 3) | (e & 7)); }
+
+__device__ __forceinline__ bf16x8 load_perm(const uint16_t *buf, int row, int ks, int G)
 {
-    return as_bf16x8(*reinterpret_cast<const uint4 *>(row + ks * 32 + 8 * G));
+    return as_bf16x8(*reinterpret_cast<const uint4 *>(buf + r64_off(row, ks * 32 + 8 * G)));
 }
 
-// Key and query rows in LDS: 256 B per row, no padding; the 16-byte units of
-// row r are XOR-swizzled by the two 2-bit halves of r's low nibble swapped.
-// Both readers are then free of bank conflicts: the operand read (16 rows,
-// one unit each) sees 16 different units, and the transpose read (4 rows x
-// 4 units of one block) sees 16 different units as well.
-__device__ __forceinline__ int kq_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// Key and query rows in LDS: 256 B per row, no padding; the sixteen 16-byte
+// units of row r are XOR-swizzled by r's low nibble with its bits reordered
+// (unit bits 0..3 take row bits 0, 3, 1, 2).  Of the orders that keep the
+// operand read (16 rows, one unit each), the transpose read (4 rows x 4 units
+// of one block) and the producers' 8-byte row writes free of bank conflicts,
+// this is one that gfx950 also serves at full rate (measured).
+__device__ __forceinline__ int kq_swz(int row)
+{
+    return (row & 1) | (((row >> 3) & 1) << 1) | (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 3);
+}
 
 // element offset of element `e` (a multiple of 4) of row `row`
 __device__ __forceinline__ int kq_off(int row, int e) { return row * KS + ((((e >> 3) ^ kq_swz(row)) << 3) | (e & 7)); }
@@ -337,16 +348,15 @@ struct ChunkArgs {
 constexpr int CONSUMERS = DVS / 16;           // 4 waves, 16 dv columns each
 constexpr int PRODUCERS = 4;
 constexpr int CHUNK_THREADS = (CONSUMERS + PRODUCERS) * 64;
-constexpr int VS = DVS + 8;                   // LDS stride (bf16) of the value / output slice
 constexpr int S0S = DK + 4;                   // LDS stride (fp32) of the staged entering state
 constexpr int NSL = DV / DVS;                 // dv slices per v-head
 
 struct ChunkBuf {
     uint16_t kr[C * KS];     // key rows
     uint16_t qr[C * KS];     // query rows
-    uint16_t tm[C * TS];     // T = (I + A)^-1
-    uint16_t pm[C * TS];     // P = Gamma o Q K^T
-    uint16_t vs[C * VS];     // values of this dv slice, then the chunk's output
+    uint16_t tm[C * RS];     // T = (I + A)^-1
+    uint16_t pm[C * RS];     // P = Gamma o Q K^T
+    uint16_t vs[C * RS];     // values of this dv slice, then the chunk's output
     float lsh[C];            // log-decay prefix l_i
     float esh[C];            // write strength b_i
     float gsh[C];            // e^{l_i}
@@ -455,7 +465,7 @@ __device__ __forceinline__ void flush_out(const ChunkBuf &B, const ChunkArgs &A,
         const int idx = j * 64 + lane, row = part * (C / PRODUCERS) + (idx >> 3), c8 = idx & 7;
         if (row < n)
             *reinterpret_cast<uint4 *>(A.out + ((t0 + row) * A.Hv + I.h) * DV + I.dv0 + c8 * 8) =
-                *reinterpret_cast<const uint4 *>(B.vs + row * VS + c8 * 8);
+                *reinterpret_cast<const uint4 *>(B.vs + r64_off(row, c8 * 8));
     }
 }
 
@@ -570,20 +580,23 @@ __device__ __forceinline__ void write_step(ChunkBuf &B, float *s0, StepRegs &R, 
     for (int j = 0; j < 4; ++j) {
         const int idx = j * 64 + lane, row = rb + (idx >> 4), c8 = idx & 15;
         if (row >= n) R.kv[j] = R.qv[j] = make_uint4(0, 0, 0, 0);
-        // key dims 8 c8 .. 8 c8 + 7 = position groups 2 c8 and 2 c8 + 1
-        const int o0 = kq_off(row, perm_off(c8 * 8)), o1 = kq_off(row, perm_off(c8 * 8 + 4));
-        *reinterpret_cast<uint2 *>(B.kr + o0) = make_uint2(R.kv[j].x, R.kv[j].y);
-        *reinterpret_cast<uint2 *>(B.kr + o1) = make_uint2(R.kv[j].z, R.kv[j].w);
-        *reinterpret_cast<uint2 *>(B.qr + o0) = make_uint2(R.qv[j].x, R.qv[j].y);
-        *reinterpret_cast<uint2 *>(B.qr + o1) = make_uint2(R.qv[j].z, R.qv[j].w);
+        // key dims 8 c8 .. 8 c8 + 7 = position groups 2 c8 and 2 c8 + 1; lanes
+        // of the upper 64 dims write their second group first, so each
+        // instruction's 16 lanes cover 128 distinct bytes of the bank space
+        const bool sw = c8 >= 8;
+        const int o0 = kq_off(row, perm_off(c8 * 8 + (sw ? 4 : 0))), o1 = kq_off(row, perm_off(c8 * 8 + (sw ? 0 : 4)));
+        *reinterpret_cast<uint2 *>(B.kr + o0) = sw ? make_uint2(R.kv[j].z, R.kv[j].w) : make_uint2(R.kv[j].x, R.kv[j].y);
+        *reinterpret_cast<uint2 *>(B.kr + o1) = sw ? make_uint2(R.kv[j].x, R.kv[j].y) : make_uint2(R.kv[j].z, R.kv[j].w);
+        *reinterpret_cast<uint2 *>(B.qr + o0) = sw ? make_uint2(R.qv[j].z, R.qv[j].w) : make_uint2(R.qv[j].x, R.qv[j].y);
+        *reinterpret_cast<uint2 *>(B.qr + o1) = sw ? make_uint2(R.qv[j].x, R.qv[j].y) : make_uint2(R.qv[j].z, R.qv[j].w);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
         if (row >= n) R.vv[j] = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(B.tm + row * TS + c8 * 8) = R.tv[j];
-        *reinterpret_cast<uint4 *>(B.pm + row * TS + c8 * 8) = R.pv[j];
-        *reinterpret_cast<uint4 *>(B.vs + row * VS + c8 * 8) = R.vv[j];
+        *reinterpret_cast<uint4 *>(B.tm + r64_off(row, c8 * 8)) = R.tv[j];
+        *reinterpret_cast<uint4 *>(B.pm + r64_off(row, c8 * 8)) = R.pv[j];
+        *reinterpret_cast<uint4 *>(B.vs + r64_off(row, c8 * 8)) = R.vv[j];
     }
     if (part == 0) {
         const bool live = lane < n;
@@ -758,7 +771,7 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
 #pragma unroll
         for (int mt = 0; mt < C / 16; ++mt) {
             const int i0 = mt * 16 + G * 4;
-            const v4s vq = load_tr(B.vs + (i0 + (c16 >> 2)) * VS + wv * 16 + 4 * (c16 & 3));
+            const v4s vq = load_tr(B.vs + r64_off(i0 + (c16 >> 2), wv * 16 + 4 * (c16 & 3)));
             const f32x4 eb = *reinterpret_cast<const f32x4 *>(B.esh + i0);
             const f32x4 gb = *reinterpret_cast<const f32x4 *>(B.gsh + i0);
 #pragma unroll
@@ -769,8 +782,8 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
         f32x4 ua[C / 16];
 #pragma unroll
         for (int mt = 0; mt < C / 16; ++mt) {
-            ua[mt] = mfma(load_perm(B.tm + (mt * 16 + c16) * TS, 0, G), rb0, f32x4{0.f, 0.f, 0.f, 0.f});
-            ua[mt] = mfma(load_perm(B.tm + (mt * 16 + c16) * TS, 1, G), rb1, ua[mt]);
+            ua[mt] = mfma(load_perm(B.tm, mt * 16 + c16, 0, G), rb0, f32x4{0.f, 0.f, 0.f, 0.f});
+            ua[mt] = mfma(load_perm(B.tm, mt * 16 + c16, 1, G), rb1, ua[mt]);
         }
         __builtin_amdgcn_sched_barrier(0);
         // O = diag(e^l) Y + P U  -> left in the value buffer for the producers
@@ -783,8 +796,8 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
             f32x4 oa;
 #pragma unroll
             for (int r = 0; r < 4; ++r) oa[r] = gb[r] * ya[mt][r];
-            oa = mfma(load_perm(B.pm + (mt * 16 + c16) * TS, 0, G), ub0, oa);
-            if (mt >= 2) oa = mfma(load_perm(B.pm + (mt * 16 + c16) * TS, 1, G), ub1, oa);
+            oa = mfma(load_perm(B.pm, mt * 16 + c16, 0, G), ub0, oa);
+            if (mt >= 2) oa = mfma(load_perm(B.pm, mt * 16 + c16, 1, G), ub1, oa);
             // lanes c16 and c16^1 hold neighbouring dv columns of the same 4
             // rows: swap halves so each lane writes two rows x two columns
             const uint32_t lo = pack2(oa[0], oa[1]), hi = pack2(oa[2], oa[3]);   // (row0,row1), (row2,row3)
@@ -795,8 +808,8 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
             const int col = wv * 16 + (c16 & ~1), rr = i0 + (odd ? 2 : 0);
             const uint32_t w0 = odd ? ((got & 0xffffu) | (keep << 16)) : ((keep & 0xffffu) | (got << 16));
             const uint32_t w1 = odd ? ((got >> 16) | (keep & 0xffff0000u)) : ((keep >> 16) | (got & 0xffff0000u));
-            *reinterpret_cast<uint32_t *>(B.vs + rr * VS + col) = w0;
-            *reinterpret_cast<uint32_t *>(B.vs + (rr + 1) * VS + col) = w1;
+            *reinterpret_cast<uint32_t *>(B.vs + r64_off(rr, col)) = w0;
+            *reinterpret_cast<uint32_t *>(B.vs + r64_off(rr + 1, col)) = w1;
         }
         // fork points strictly inside this chunk: state after `off` tokens
         while (E.next < c * C + n) {
