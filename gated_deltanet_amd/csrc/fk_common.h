@@ -56,6 +56,7 @@ struct WsLayout {
     size_t fork_states;   // float[fork_cap * Hv * dv * dk]
     size_t tmat;          // bf16[chunk_cap * Hv * FK_GDN_CHUNK^2] per-chunk (I + A)^-1
     size_t pmat;          // bf16[chunk_cap * Hv * FK_GDN_CHUNK^2] per-chunk Gamma o Q K^T
+    size_t lvec;          // float[chunk_cap * Hv * FK_GDN_CHUNK] per-chunk log-decay prefix l_i
     size_t total;
     int64_t tile_cap;
     int64_t chunk_cap;
@@ -119,6 +120,7 @@ inline WsLayout ws_layout(const fk_tree_meta &m, int64_t Hv, int64_t dk, int64_t
     L.fork_states = take(fc * (size_t)(state_elems > 0 ? state_elems : 0) * 4);
     L.tmat = take((size_t)L.chunk_cap * (size_t)(Hv > 0 ? Hv : 0) * FK_GDN_CHUNK * FK_GDN_CHUNK * 2);
     L.pmat = take((size_t)L.chunk_cap * (size_t)(Hv > 0 ? Hv : 0) * FK_GDN_CHUNK * FK_GDN_CHUNK * 2);
+    L.lvec = take((size_t)L.chunk_cap * (size_t)(Hv > 0 ? Hv : 0) * FK_GDN_CHUNK * 4);
     L.total = off;
     return L;
 }

@@ -15,7 +15,8 @@
 //
 // k_gdn_prep  (all chunks of the round at once, before the level launches):
 //             T of every (chunk, v-head) in fp32 by forward substitution,
-//             stored as bf16.  It depends only on k, a, b -- never on a state.
+//             stored as bf16, with P and the chunk's log-decay prefix l.  It
+//             depends only on q, k, a, b -- never on a state.
 // k_gdn_chunk (one launch per tree level, persistent work-groups): each
 //             item (segment, v-head, 64-wide dv slice) walks its chunks in
 //             order.  Each wave keeps its 128 x 16 slice of S^T in fp32 MFMA
@@ -138,7 +139,7 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
            const float *__restrict__ b, int Hk, int Hv, const int32_t *__restrict__ header,
            const int32_t *__restrict__ chunk_seg, const int32_t *__restrict__ chunk_row0,
            const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_len,
-           uint16_t *__restrict__ tmat, uint16_t *__restrict__ pmat)
+           uint16_t *__restrict__ tmat, uint16_t *__restrict__ pmat, float *__restrict__ lvec)
 {
     // per wave: the fp32 diagonal blocks of A (then of T), later the finished
     // T as bf16 rows -- the two uses never overlap in time
@@ -180,6 +181,7 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     }
     lsh[lane] = la;
     esh[lane] = eta;
+    if (valid) lvec[((size_t)c * Hv + h) * C + lane] = la;   // read back by the chunk walk
     __syncthreads();
     // P^T tiles K_j Q_i^T: lane holds (row j = 16*jt + 4G + r, col i = 16*it + c16),
     // i.e. four consecutive j of one row i of P -> one 8-byte store per tile
@@ -335,19 +337,24 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
 // ---------------------------------------------------------------------------
 struct ChunkArgs {
     const uint16_t *q, *k, *v;
-    const float *a, *b;
+    const float *b;
     uint16_t *out;
     int T, Hk, Hv, level, level_cap;
     const int32_t *header, *lvl_sorted, *seg_start, *seg_len, *seg_src, *seg_chunk0, *emit_off, *emit_pos,
         *seg_state_out;
     const uint16_t *tmat, *pmat;
+    const float *lvec;
     const float *state_in;
     float *state_out, *fork_states;
 };
 
 constexpr int CONSUMERS = DVS / 16;           // 4 waves, 16 dv columns each
-constexpr int PRODUCERS = 4;
+constexpr int PRODUCERS = 8;
 constexpr int CHUNK_THREADS = (CONSUMERS + PRODUCERS) * 64;
+constexpr int PROWS = C / PRODUCERS;          // token rows (and state rows) a producer stages
+constexpr int KQ_LD = PROWS / 4;              // key / query loads: 4 rows x 16 lanes each
+constexpr int ROW_LD = PROWS / 8;             // 64-wide row loads: 8 rows x 8 lanes each
+constexpr int S0_LD = DVS / PRODUCERS / 2;    // entering-state loads: 2 rows x 32 lanes each
 constexpr int S0S = DK + 4;                   // LDS stride (fp32) of the staged entering state
 constexpr int NSL = DV / DVS;                 // dv slices per v-head
 
@@ -375,8 +382,10 @@ __device__ __forceinline__ int ldc(const int32_t *p, int i)
 }
 
 struct Item {
-    int s, h, g, dv0, len, nch, chunk0, t0, src;
+    int s, h, dv0, len, chunk0, t0, src;
 };
+
+__device__ __forceinline__ int item_nch(const Item &I) { return (I.len + C - 1) / C; }
 
 // How a level's items are dealt to the G work-groups.  Items are numbered
 // (v-head, dv slice) major, segment rank minor, so consecutive items of a
@@ -404,10 +413,8 @@ __device__ __forceinline__ Item item_at(const ChunkArgs &A, const Walk &W, int i
     const int rank = it % W.nseg, hs = it / W.nseg;
     I.s = ldc(A.lvl_sorted, A.level * A.level_cap + rank);
     I.h = hs / NSL;
-    I.g = I.h / (A.Hv / A.Hk);
     I.dv0 = (hs % NSL) * DVS;
     I.len = ldc(A.seg_len, I.s);
-    I.nch = (I.len + C - 1) / C;
     I.chunk0 = ldc(A.seg_chunk0, I.s);
     I.t0 = ldc(A.seg_start, I.s);
     I.src = ldc(A.seg_src, I.s);
@@ -453,7 +460,7 @@ __device__ __forceinline__ void store_state(float *base, int dvc, int G, const f
         *reinterpret_cast<f32x4 *>(base + (size_t)dvc * DK + i * 16 + G * 4) = st[i];
 }
 
-// producer `part`: store token rows [16 part, +16) of the output slice of
+// producer `part`: store token rows [PROWS part, +PROWS) of the output slice of
 // chunk `c` of item I (left in B.vs by the consumers), 8 lanes x 16 B per row
 __device__ __forceinline__ void flush_out(const ChunkBuf &B, const ChunkArgs &A, const Item &I, int c, int lane,
                                           int part)
@@ -461,8 +468,8 @@ __device__ __forceinline__ void flush_out(const ChunkBuf &B, const ChunkArgs &A,
     const int n = min(C, I.len - c * C);
     const size_t t0 = (size_t)I.t0 + (size_t)c * C;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int idx = j * 64 + lane, row = part * (C / PRODUCERS) + (idx >> 3), c8 = idx & 7;
+    for (int j = 0; j < ROW_LD; ++j) {
+        const int idx = j * 64 + lane, row = part * PROWS + (idx >> 3), c8 = idx & 7;
         if (row < n)
             *reinterpret_cast<uint4 *>(A.out + ((t0 + row) * A.Hv + I.h) * DV + I.dv0 + c8 * 8) =
                 *reinterpret_cast<const uint4 *>(B.vs + r64_off(row, c8 * 8));
@@ -503,14 +510,14 @@ __device__ __forceinline__ uint32_t pack2(float a, float b)
 // One step's worth of a producer's loads, held in registers between the
 // interval that issues them and the interval that writes them to LDS.
 struct StepRegs {
-    uint4 kv[4], qv[4], tv[2], pv[2], vv[2];
-    f32x4 s0[8];
-    float a_raw, b_raw;
+    uint4 kv[KQ_LD], qv[KQ_LD], tv[ROW_LD], pv[ROW_LD], vv[ROW_LD];
+    f32x4 s0[S0_LD];
+    float l_raw, b_raw;
     bool s0_write;   // this step starts an item whose entering state is not staged yet
 };
 
 // issue the loads of chunk c of item I (and, when `stage_s0`, of its entering
-// state); rows [16 part, 16 part + 16) of the chunk, dv rows of the state
+// state); rows [PROWS part, +PROWS) of the chunk, dv rows of the state
 // likewise.  Coalesced: consecutive lanes read consecutive 16 B of a row.
 // Rows past the chunk's last token are not read (zero): nothing uses them --
 // T and P are lower triangular, and zero key rows keep them out of the state.
@@ -520,10 +527,10 @@ __device__ __forceinline__ void load_step(StepRegs &R, const ChunkArgs &A, const
     const int n = min(C, I.len - c * C);
     const size_t t0 = (size_t)I.t0 + (size_t)c * C;
     const size_t mat = ((size_t)(I.chunk0 + c) * A.Hv + I.h) * C * C;
-    const int rb = part * (C / PRODUCERS);
+    const int rb = part * PROWS;
     // buffer resources based at this chunk's first row: 32-bit offsets, and
     // the hardware range check returns zeros past the end of each tensor
-    const size_t kq_base = (t0 * A.Hk + I.g) * DK, kq_end = (size_t)A.T * A.Hk * DK;
+    const size_t kq_base = (t0 * A.Hk + I.h / (A.Hv / A.Hk)) * DK, kq_end = (size_t)A.T * A.Hk * DK;
     const size_t v_base = (t0 * A.Hv + I.h) * DV + I.dv0, v_end = (size_t)A.T * A.Hv * DV;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(A.k + kq_base, (kq_end - kq_base) * 2);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(A.q + kq_base, (kq_end - kq_base) * 2);
@@ -532,7 +539,7 @@ __device__ __forceinline__ void load_step(StepRegs &R, const ChunkArgs &A, const
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(A.pmat + mat, (size_t)C * C * 2);
     const int kq_row = A.Hk * DK * 2, v_row = A.Hv * DV * 2;   // bytes between tokens
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {               // 4 rows x 16 lanes per instruction
+    for (int j = 0; j < KQ_LD; ++j) {           // 4 rows x 16 lanes per instruction
         const int idx = j * 64 + lane, row = rb + (idx >> 4), c8 = idx & 15;
         R.kv[j] = R.qv[j] = make_uint4(0, 0, 0, 0);
         if (row < n) {
@@ -541,7 +548,7 @@ __device__ __forceinline__ void load_step(StepRegs &R, const ChunkArgs &A, const
         }
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {               // 8 rows x 8 lanes per instruction
+    for (int j = 0; j < ROW_LD; ++j) {          // 8 rows x 8 lanes per instruction
         const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
         R.tv[j] = R.pv[j] = R.vv[j] = make_uint4(0, 0, 0, 0);
         if (row < n) {
@@ -550,20 +557,20 @@ __device__ __forceinline__ void load_step(StepRegs &R, const ChunkArgs &A, const
             R.vv[j] = buf_load(rv, row * v_row + c8 * 16);
         }
     }
-    R.a_raw = 1.f;
+    R.l_raw = 0.f;
     R.b_raw = 0.f;
     if (part == 0) {
         const int rr = lane < n ? lane : n - 1;
-        R.a_raw = A.a[(t0 + rr) * A.Hv + I.h];
+        R.l_raw = A.lvec[((size_t)(I.chunk0 + c) * A.Hv + I.h) * C + lane];
         R.b_raw = A.b[(t0 + rr) * A.Hv + I.h];
     }
     R.s0_write = c == 0 && stage_s0;
     if (R.s0_write) {
-        // dv rows [16 part, +16) of the slice, 32 lanes x 16 B per row
+        // dv rows [DVS / PRODUCERS part, +DVS / PRODUCERS) of the slice, 32 lanes x 16 B per row
         const float *S0 = item_s0(A, I);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int idx = j * 64 + lane, row = part * 16 + (idx >> 5), c4 = idx & 31;
+        for (int j = 0; j < S0_LD; ++j) {
+            const int idx = j * 64 + lane, row = part * (DVS / PRODUCERS) + (idx >> 5), c4 = idx & 31;
             R.s0[j] = S0 ? *reinterpret_cast<const f32x4 *>(S0 + (size_t)(I.dv0 + row) * DK + c4 * 4)
                          : f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -575,9 +582,9 @@ __device__ __forceinline__ void write_step(ChunkBuf &B, float *s0, StepRegs &R, 
                                            int part)
 {
     const int n = min(C, I.len - c * C);
-    const int rb = part * (C / PRODUCERS);
+    const int rb = part * PROWS;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < KQ_LD; ++j) {
         const int idx = j * 64 + lane, row = rb + (idx >> 4), c8 = idx & 15;
         if (row >= n) R.kv[j] = R.qv[j] = make_uint4(0, 0, 0, 0);
         // key dims 8 c8 .. 8 c8 + 7 = position groups 2 c8 and 2 c8 + 1; lanes
@@ -591,7 +598,7 @@ __device__ __forceinline__ void write_step(ChunkBuf &B, float *s0, StepRegs &R, 
         *reinterpret_cast<uint2 *>(B.qr + o1) = sw ? make_uint2(R.qv[j].x, R.qv[j].y) : make_uint2(R.qv[j].z, R.qv[j].w);
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < ROW_LD; ++j) {
         const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
         if (row >= n) R.vv[j] = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4 *>(B.tm + r64_off(row, c8 * 8)) = R.tv[j];
@@ -599,14 +606,11 @@ __device__ __forceinline__ void write_step(ChunkBuf &B, float *s0, StepRegs &R, 
         *reinterpret_cast<uint4 *>(B.vs + r64_off(row, c8 * 8)) = R.vv[j];
     }
     if (part == 0) {
+        // l as the prep kernel computed it (lanes past the chunk hold l_{n-1})
         const bool live = lane < n;
-        float la = live ? logf(R.a_raw) : 0.f;
+        const float la = R.l_raw;
         const float eta = live ? R.b_raw : 0.f;
-        for (int o = 1; o < 64; o <<= 1) {
-            const float y = __shfl_up(la, o, 64);
-            if (lane >= o) la += y;
-        }
-        const float last = __shfl(la, C - 1, 64);
+        const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(la), C - 1));
         B.lsh[lane] = la;
         B.esh[lane] = eta;
         B.gsh[lane] = __expf(la);
@@ -614,8 +618,8 @@ __device__ __forceinline__ void write_step(ChunkBuf &B, float *s0, StepRegs &R, 
     }
     if (c == 0 && R.s0_write) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int idx = j * 64 + lane, row = part * 16 + (idx >> 5), c4 = idx & 31;
+        for (int j = 0; j < S0_LD; ++j) {
+            const int idx = j * 64 + lane, row = part * (DVS / PRODUCERS) + (idx >> 5), c4 = idx & 31;
             *reinterpret_cast<f32x4 *>(s0 + row * S0S + c4 * 4) = R.s0[j];
         }
     }
@@ -677,7 +681,7 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
         int c1 = 1;
         bool has1 = true;
         Item nx1 = cur;
-        if (c1 == cur.nch) {
+        if (c1 == item_nch(cur)) {
             c1 = 0;
             has1 = la_it < n_items;
             if (has1) take(nx1);
@@ -693,7 +697,7 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
             int c2 = c1 + 1;
             bool has2 = has1;
             Item nx2 = nx1;
-            if (has1 && c2 == nx1.nch) {
+            if (has1 && c2 == item_nch(nx1)) {
                 c2 = 0;
                 has2 = la_it < n_items;
                 if (has2) take(nx2);
@@ -731,7 +735,7 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
     for (int j = 0;; ++j) {
         ChunkBuf &B = buf[j & 1];
         const int dvc = cur.dv0 + wv * 16 + c16;   // this lane's state column (dv index)
-        const bool last = c + 1 == cur.nch;
+        const bool last = c + 1 == item_nch(cur);
         // the next item's metadata, fetched while this step computes
         const int next_it = item_id(W, blockIdx.x, ik + 1);
         const bool more = !last || next_it < n_items;
@@ -887,7 +891,8 @@ int fk_launch_gdn_bf16_prep(const fk_tree_meta *meta, const void *q, const void 
                                           ws_at<int32_t>(ws, L.chunk_seg), ws_at<int32_t>(ws, L.chunk_row0),
                                           ws_at<int32_t>(ws, L.seg_start), ws_at<int32_t>(ws, L.seg_len),
                                           const_cast<uint16_t *>(ws_at<uint16_t>(ws, L.tmat)),
-                                          const_cast<uint16_t *>(ws_at<uint16_t>(ws, L.pmat)));
+                                          const_cast<uint16_t *>(ws_at<uint16_t>(ws, L.pmat)),
+                                          const_cast<float *>(ws_at<float>(ws, L.lvec)));
     return launch_status();
 }
 
@@ -900,7 +905,6 @@ int fk_launch_gdn_bf16(const fk_tree_meta *meta, int level, const void *q, const
     A.q = (const uint16_t *)q;
     A.k = (const uint16_t *)k;
     A.v = (const uint16_t *)v;
-    A.a = a;
     A.b = b;
     A.out = (uint16_t *)out;
     A.T = meta->T;
@@ -919,6 +923,7 @@ int fk_launch_gdn_bf16(const fk_tree_meta *meta, int level, const void *q, const
     A.seg_state_out = meta->seg_state_out;
     A.tmat = ws_at<uint16_t>(ws, L.tmat);
     A.pmat = ws_at<uint16_t>(ws, L.pmat);
+    A.lvec = ws_at<float>(ws, L.lvec);
     A.state_in = state_in;
     A.state_out = state_out;
     A.fork_states = fork_states;
