@@ -294,6 +294,28 @@ class ResumeWorkload:
             ev[4].record()
 
 
+def gdn_bytes(tree, sh, elem: int, resumed_save: bool = False) -> int:
+    """Algorithmic HBM bytes of one forked GDN pass: q and k (Hk heads) and v
+    read once, o written once, a and b read once (fp32); each fork-point
+    state written once and read once by every child entering from it; each
+    resumed root reads its state_in slot, and with ``resumed_save`` (the
+    resume workload's step) also writes its state_out slot, which the
+    checkpoint save then reads and copies out."""
+    per_tok = 2 * sh.Hk * sh.dk * elem + 2 * sh.Hv * sh.dv * elem + 2 * sh.Hv * 4
+    state = sh.Hv * sh.dv * sh.dk * 4
+    forks, children, resumed = set(), 0, 0
+    for s in tree.segs:
+        if s.cached or s.parent < 0:
+            continue
+        if tree.segs[s.parent].cached:
+            resumed += 1
+        else:
+            forks.add((s.parent, s.fork))
+            children += 1
+    n_states = len(forks) + children + resumed + (3 * resumed if resumed_save else 0)
+    return tree.T * per_tok + n_states * state
+
+
 def measure_conv(wl, steps: int, W: int = 4):
     """The forked short convolution in front of the GDN layer (a row beyond
     the step), timed on its own over the same round: channels = the q|k|v
@@ -577,6 +599,14 @@ def main():
                      "traffic": measured_traffic(args.config), "algorithmic_flops": flops,
                      "visible_pairs_per_head": nvis},
     }
+    if getattr(wl, "gdn_ok", True):
+        gdn_ms = float(phase[:, 3].mean())
+        nbytes = gdn_bytes(tree, sh, 2 if wl.cfg.dtype == "bf16" else 4, resumed_save=args.config == 4)
+        gbs = nbytes / (gdn_ms * 1e-3) / 1e9
+        line["gdn_roofline"] = {"kernels": "GDN prep + one chunk walk per tree level (bf16 MFMA)"
+                                           + (" + checkpoint save" if args.config == 4 else ""),
+                                "bound": "hbm", "ms": gdn_ms, "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": nbytes}
     line["next_rows"] = {"conv": measure_conv(wl, args.steps),
                          "window_attention": measure_rule(wl, args.steps, 1, 1024),
                          "two_way_attention": measure_rule(wl, args.steps, 2),

@@ -1,0 +1,48 @@
+"""The benchmark's work counts, on trees small enough to count by hand: the
+visible (query, key) pairs behind the attention FLOP figure, the pairs under
+the sliding-window and two-way rules, and the GDN pass's algorithmic bytes."""
+from types import SimpleNamespace
+
+import bench
+from workloads import build_tree
+
+# a 10-token root, a 3-token child forked at its end, a 2-token child forked
+# after 4 tokens
+TREE = [[(-1, 0, 10), (0, None, 3), (0, 4, 2)]]
+
+
+def test_visible_pairs_by_hand():
+    t = build_tree(TREE).flatten()
+    root = sum(i + 1 for i in range(10))                 # positions 0..9
+    end_child = sum(10 + i + 1 for i in range(3))        # positions 10..12
+    mid_child = sum(4 + i + 1 for i in range(2))         # positions 4..5
+    assert bench.visible_pairs(t) == root + end_child + mid_child == 102
+
+
+def test_rule_pairs_by_hand():
+    t = build_tree(TREE).flatten()
+    # window W = 3: every row sees min(position + 1, 3) keys
+    w3 = sum(min(i + 1, 3) for i in range(10)) + 3 * 3 + sum(min(4 + i + 1, 3) for i in range(2))
+    assert bench.rule_pairs(t, 1, 3) == w3
+    # two-way: a row sees its ancestors' prefix and its whole own segment
+    two = 10 * 10 + 3 * (10 + 3) + 2 * (4 + 2)
+    assert bench.rule_pairs(t, 2) == two
+    # a window wider than every path is the causal count
+    assert bench.rule_pairs(t, 1, 1000) == bench.visible_pairs(t)
+
+
+def test_gdn_bytes_by_hand():
+    t = build_tree(TREE).flatten()
+    sh = SimpleNamespace(Hk=2, Hv=4, dk=8, dv=16)
+    per_tok = 2 * 2 * 8 * 2 + 2 * 4 * 16 * 2 + 2 * 4 * 4
+    state = 4 * 16 * 8 * 4
+    # two distinct fork points, each written once and read by its one child
+    assert bench.gdn_bytes(t, sh, 2) == 15 * per_tok + 4 * state
+    # siblings at one fork point share its single write
+    t2 = build_tree([[(-1, 0, 10), (0, None, 3), (0, None, 2)]]).flatten()
+    assert bench.gdn_bytes(t2, sh, 2) == 15 * per_tok + 3 * state
+    # a root resumed from a cached history reads its state slot; the resume
+    # step also writes it back and the checkpoint save copies it out
+    t3 = build_tree([[(-1, 0, 7, True), (0, None, 5)]]).flatten()
+    assert bench.gdn_bytes(t3, sh, 2) == 5 * per_tok + 1 * state
+    assert bench.gdn_bytes(t3, sh, 2, resumed_save=True) == 5 * per_tok + 4 * state
