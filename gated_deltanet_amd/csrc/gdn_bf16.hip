@@ -19,7 +19,7 @@
 //             depends only on q, k, a, b -- never on a state.
 // k_gdn_chunk (one launch per tree level, persistent work-groups): each
 //             item (segment, v-head, 64-wide dv slice) walks its chunks in
-//             order.  Each wave keeps its 128 x 16 slice of S^T in fp32 MFMA
+//             order.  Each consumer wave keeps its 128 x 16 slice of S^T in fp32 MFMA
 //             accumulator registers for the whole segment and feeds it
 //             straight back as an MFMA operand (a fixed permutation of the
 //             reduction index makes the accumulator layout the operand
@@ -326,10 +326,10 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
 // dv slice), dealt to the work-groups as `Walk` describes; a work-group runs
 // its items, and within an item its chunks, in order -- one flat sequence of
 // steps.  Waves 0-3 (consumers) own the state slice and run the
-// state-dependent products of step j; waves 4-7 (producers) meanwhile write
-// step j+1 (already in their registers) into the other LDS buffer, issue the
-// global loads of step j+2, and store the output of step j-1 that the
-// consumers left in the value buffer.  When a step starts an item, the
+// state-dependent products of step j; waves 4-11 (producers, 8 token rows
+// each) meanwhile write step j+1 (already in their registers) into the other
+// LDS buffer, issue the global loads of step j+2, and store the output of
+// step j-1 that the consumers left in the value buffer.  When a step starts an item, the
 // producers have staged that item's entering state (zero, state_in, or the
 // parent's fork-point state) in LDS, so no wave waits on HBM at an item
 // boundary.  The assignment of items to work-groups never changes an item's
