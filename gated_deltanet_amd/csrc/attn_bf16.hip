@@ -30,6 +30,8 @@
 // V^T rows are contiguous in LDS.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "fk_common.h"
 
 namespace fk {
@@ -605,10 +607,14 @@ int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv
     if (rows) {
         int dev = 0;
         FK_HIP(hipGetDevice(&dev));
-        static int n_cu[64] = {0};
+        static std::atomic<int> n_cu_dev[64];   // per device, queried once
         if (dev < 0 || dev >= 64) return FK_E_HIP;
-        if (!n_cu[dev]) FK_HIP(hipDeviceGetAttribute(&n_cu[dev], hipDeviceAttributeMultiprocessorCount, dev));
-        const int64_t g = (int64_t)n_rows * Hkv / (3 * (int64_t)n_cu[dev]);
+        int n_cu = n_cu_dev[dev].load(std::memory_order_relaxed);
+        if (!n_cu) {
+            FK_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+            n_cu_dev[dev].store(n_cu, std::memory_order_relaxed);
+        }
+        const int64_t g = (int64_t)n_rows * Hkv / (3 * (int64_t)n_cu);
         group = (int)(g < 1 ? 1 : g > FK_TILE_TOKENS ? FK_TILE_TOKENS : g);
     }
     if (rule == FK_RULE_WINDOW)

@@ -29,6 +29,8 @@
 //             segment's fork points once each.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "fk_common.h"
 
 namespace fk {
@@ -928,17 +930,22 @@ int fk_launch_gdn_bf16(const fk_tree_meta *meta, int level, const void *q, const
     A.state_out = state_out;
     A.fork_states = fork_states;
     // persistent: at most one work-group per compute unit (the LDS holds one)
+    // per device, once: the compute-unit count, published only after the
+    // kernel's LDS limit is raised (a caller on another thread that sees the
+    // count may launch at once; one that sees 0 repeats the idempotent setup)
     int dev = 0;
     FK_HIP(hipGetDevice(&dev));
-    static int n_cu[64] = {0};
+    static std::atomic<int> n_cu_dev[64];
     if (dev < 0 || dev >= 64) return FK_E_HIP;
-    if (!n_cu[dev]) {
-        FK_HIP(hipDeviceGetAttribute(&n_cu[dev], hipDeviceAttributeMultiprocessorCount, dev));
+    int n_cu = n_cu_dev[dev].load(std::memory_order_acquire);
+    if (!n_cu) {
+        FK_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
         FK_HIP(hipFuncSetAttribute((const void *)gdnk::k_gdn_chunk, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)gdnk::CHUNK_LDS));
+        n_cu_dev[dev].store(n_cu, std::memory_order_release);
     }
     const int64_t cap = (int64_t)meta->level_cap * Hv * gdnk::NSL;
-    dim3 grid((unsigned)(cap < n_cu[dev] ? cap : n_cu[dev]));
+    dim3 grid((unsigned)(cap < n_cu ? cap : n_cu));
     const size_t lds = gdnk::CHUNK_LDS;
     gdnk::k_gdn_chunk<<<grid, gdnk::CHUNK_THREADS, lds, st>>>(A);
     return launch_status();
