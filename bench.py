@@ -85,6 +85,53 @@ def calibrate_copy():
     return src.numel() * 4
 
 
+def measured_peaks():
+    """What this device sustains, reported next to the published peaks (the
+    roofline fractions use the published ones): a plain 512 MiB copy through
+    the checkpoint-save kernel (read + write) and the dense bf16 MFMA loop."""
+    import torch
+    import gated_deltanet_amd as fk
+    src = torch.ones((1, 8192, 128, 128), dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src[0])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        fk.gdn_checkpoint_save(src, 0, dst)
+    e0.record()
+    for _ in range(10):
+        fk.gdn_checkpoint_save(src, 0, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    n_wg = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(n_wg, dtype=torch.float32, device="cuda")
+    fk.fk_peak_mfma_bf16(n_wg, 256, sink)
+    e0.record()
+    flops = sum(fk.fk_peak_mfma_bf16(n_wg, 4096, sink) for _ in range(5))
+    e1.record()
+    torch.cuda.synchronize()
+    tf = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    return {"hbm_copy_GBs": copy_gbs, "mfma_bf16_TFLOPs": tf,
+            "published": {"hbm_GBs": PEAK_HBM_GBS, "mfma_bf16_TFLOPs": PEAK_BF16_TFLOPS},
+            "how": "512 MiB copy (checkpoint-save kernel, read + write bytes); eight independent "
+                   "32x32x16 bf16 MFMA chains per wave, two waves per SIMD, register operands"}
+
+
+def path_tokens(tree) -> int:
+    """Isolated-pass work the method avoids: every leaf's whole root-to-leaf
+    path (positions 0 .. pos0 + len - 1), summed over live leaves."""
+    tot = 0
+    for i, sg in enumerate(tree.segs):
+        if sg.cached or any(not tree.segs[c].cached for c in tree.children(i)):
+            continue
+        pos0, j = 0, i
+        while tree.segs[j].parent >= 0:
+            pos0 += tree.segs[j].fork
+            j = tree.segs[j].parent
+        tot += pos0 + sg.length
+    return tot
+
+
 def visible_pairs(tree) -> int:
     """Visible (query, key) pairs per attention head: sum over live segments
     of len*pos0 + len(len+1)/2 (positions continue from the fork)."""
@@ -553,6 +600,7 @@ def main():
     phase = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # ms
     ms_eager = wall * 1e3 / args.steps
     ms_step, mode = ms_eager, "eager launches"
+    dist = None
     if not args.eager:
         # the same step recorded once as a HIP graph and replayed: the
         # headline timing (no launch gaps between the step's kernels)
@@ -567,6 +615,29 @@ def main():
         ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
         mode = "HIP graph replay"
         assert wl.fk.fk_read_status(wl.ws) == 0, "tree build reported an error"
+        # per-replay distribution (HIP events), warm and with the caches
+        # flushed before each step (a 512 MiB write evicts L2 and MALL)
+        rep = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in rep:
+            e[0].record()
+            graph.replay()
+            e[1].record()
+        torch.cuda.synchronize()
+        warm = np.array([e[0].elapsed_time(e[1]) for e in rep])
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold = []
+        for _ in range(min(args.steps, 10)):
+            flush.zero_()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            graph.replay()
+            e[1].record()
+            torch.cuda.synchronize()
+            cold.append(e[0].elapsed_time(e[1]))
+        del flush
+        dist = {"warm_p10": float(np.percentile(warm, 10)), "warm_p50": float(np.percentile(warm, 50)),
+                "warm_p90": float(np.percentile(warm, 90)), "cold_p50": float(np.median(cold)),
+                "cold_flush_bytes": 512 << 20}
     attn_ms = float(phase[:, 2].mean())
     nvis = visible_pairs(tree)
     flops = 4.0 * sh.d * sh.Hq * nvis
@@ -589,6 +660,9 @@ def main():
                    "stream_tokens": tree.T, "branch_tokens": bt, "segments": tree.S,
                    "attn_heads": [sh.Hq, sh.Hkv, sh.d], "gdn_heads": [sh.Hk, sh.Hv, sh.dk, sh.dv]},
         "execution": mode,
+        "step_ms_distribution": dist,
+        "stream_tokens_per_s": tree.T / (ms_step * 1e-3),
+        "path_equivalent_tokens_per_s": path_tokens(tree) / (ms_step * 1e-3),
         "ms_per_step_eager": ms_eager,
         "phases_ms": {("resume+tree_build" if args.config == 4 else "tree_build"): float(phase[:, 0].mean()),
                       "kv_append": float(phase[:, 1].mean()),
@@ -614,6 +688,7 @@ def main():
     if not getattr(wl, "gdn_ok", True):
         line["incomplete"] = "gdn_fork_forward unsupported for this dtype in this build: step lacks GDN"
         line["phases_ms"]["gdn"] = None
+    line["measured_peaks"] = measured_peaks()
     if not args.no_cpu_baseline:
         n_cpu = args.cpu_requests if args.config != 4 else min(args.cpu_requests, 1)
         line["cpu_baseline"] = cpu_baseline(args.config, n_cpu)

@@ -247,3 +247,15 @@ def fk_read_status(ws, stream=None) -> int:
 
 def fk_strerror(code: int) -> str:
     return _lib.load().fk_strerror(int(code)).decode()
+
+
+def fk_peak_mfma_bf16(n_wg: int, iters: int, sink=None, stream=None) -> float:
+    """Launch the dense bf16 MFMA loop (a measurement utility) on `stream`;
+    returns the launch's product flops.  The caller times it."""
+    if sink is None:
+        sink = torch.empty(n_wg, dtype=torch.float32, device="cuda")
+    flops = ctypes.c_double(0.0)
+    _lib.check("fk_peak_mfma_bf16", _lib.load().fk_peak_mfma_bf16(_ptr(sink), int(n_wg), int(iters),
+                                                                  ctypes.byref(flops), _stream(stream)))
+    return flops.value
+

@@ -322,6 +322,19 @@ const char *fk_strerror(int code);
 /* ABI version of this header (host). */
 int fk_abi_version(void);
 
+/*
+ * Measurement utility (not part of the method; used to report the dense bf16
+ * MFMA rate the device sustains next to its published peak).
+ * fk_peak_mfma_bf16 -- launch n_wg work-groups of four waves, each running
+ * `iters` rounds of eight independent 32x32x16 bf16 matrix-core products on
+ * register operands; *flops (host) receives the launch's product flops
+ * (n_wg * 4 * iters * 8 * 32768).  The caller times the launch on `stream`.
+ * sink: n_wg floats of device memory (one result per work-group, written so
+ * the products are not removed).  FK_E_INVALID_ARG for a null pointer or a
+ * count below 1.
+ */
+int fk_peak_mfma_bf16(float *sink, int32_t n_wg, int32_t iters, double *flops, fk_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

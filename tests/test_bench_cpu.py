@@ -46,3 +46,12 @@ def test_gdn_bytes_by_hand():
     t3 = build_tree([[(-1, 0, 7, True), (0, None, 5)]]).flatten()
     assert bench.gdn_bytes(t3, sh, 2) == 5 * per_tok + 1 * state
     assert bench.gdn_bytes(t3, sh, 2, resumed_save=True) == 5 * per_tok + 4 * state
+
+
+def test_path_tokens_by_hand():
+    # the two leaves' whole paths: 10 + 3 and 4 + 2 positions; the root is no leaf
+    t = build_tree(TREE).flatten()
+    assert bench.path_tokens(t) == 13 + 6
+    # a lone root is its own leaf; a cached history counts toward its leaf's path
+    assert bench.path_tokens(build_tree([[(-1, 0, 7)]]).flatten()) == 7
+    assert bench.path_tokens(build_tree([[(-1, 0, 7, True), (0, None, 5)]]).flatten()) == 12
