@@ -496,6 +496,20 @@ def measure_readout(wl, steps: int):
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": nbytes}
 
 
+def host_cpu():
+    """The host CPU the oracle ran on: model name and the CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(index: int, n_req: int):
     """The fp64 oracle, as it stands, on the first ``n_req`` requests of the
     same workload: every root-to-leaf path as its own isolated sequence
@@ -517,7 +531,7 @@ def cpu_baseline(index: int, n_req: int):
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     bt = tree.branch_tokens()
-    return {"value": bt / dt, "unit": "branch tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": bt / dt, "unit": "branch tokens/s", "cores": cores, "kind": "oracle", **host_cpu(),
             "sample": f"first {n_req} request(s) of the workload ({tree.T} stream tokens, {bt} branch "
                       f"tokens, {len(tree.leaves())} leaf paths), fp64 literal isolated-path "
                       f"attention + GDN, {dt:.1f} s"}
@@ -561,7 +575,7 @@ def cpu_baseline_resume(n_req: int):
     dt = (time.perf_counter() - t0) * frac
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     bt = tree.branch_tokens()
-    return {"value": bt / dt, "unit": "branch tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": bt / dt, "unit": "branch tokens/s", "cores": cores, "kind": "oracle", **host_cpu(),
             "sample": f"first {n_req} request(s) of the workload ({tree.T} stream tokens after "
                       f"{sum(n_h)} history tokens, {bt} branch tokens), 1/{frac} of the attention and "
                       f"GDN heads timed and scaled by {frac}: fp64 tree-mode attention + GDN resumed "
