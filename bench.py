@@ -520,6 +520,8 @@ def cpu_baseline(index: int, n_req: int):
 
     if index == 4:
         return cpu_baseline_resume(n_req)
+    if index in (2, 3):
+        return cpu_baseline_sampled(index, 1 if index == 3 else 4)
     cfg, tree = make_config(index, n_requests=n_req)
     inp = draw_inputs(tree, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
     ts, par, fkk, cl = tree.arrays()
@@ -535,6 +537,61 @@ def cpu_baseline(index: int, n_req: int):
             "sample": f"first {n_req} request(s) of the workload ({tree.T} stream tokens, {bt} branch "
                       f"tokens, {len(tree.leaves())} leaf paths), fp64 literal isolated-path "
                       f"attention + GDN, {dt:.1f} s"}
+
+
+def cpu_baseline_sampled(index: int, n_paths: int):
+    """The fp64 oracle on long-path workloads (a full literal run would take
+    hours): ``n_paths`` seeded leaf paths, each run alone in literal mode with
+    one attention q head and one GDN v-head timed, scaled to every head and
+    to every leaf path (attention by the sum of squared path lengths, GDN by
+    the sum of path lengths).  The figure is extrapolated and says so."""
+    import oracle
+    from workloads import make_config, subtree_path
+    from workloads.tensors import draw_inputs
+
+    cfg, tree = make_config(index)
+    sh = cfg.shapes
+    leaves = tree.leaves()
+
+    def path_len(leaf):
+        pos0, j = 0, leaf
+        while tree.segs[j].parent >= 0:
+            pos0 += tree.segs[j].fork
+            j = tree.segs[j].parent
+        return pos0 + tree.segs[leaf].length
+
+    lens = np.array([path_len(x) for x in leaves], np.float64)
+    pick = np.random.default_rng(index).choice(len(leaves), size=min(n_paths, len(leaves)), replace=False)
+    a_sel = (np.arange(sh.Hq) == 0).astype(np.uint8)
+    g_sel = (np.arange(sh.Hv) == 0).astype(np.uint8)
+    t_attn = t_gdn = 0.0
+    for li in pick:
+        leaf = int(leaves[li])
+        sub, _ = subtree_path(tree, leaf)
+        sub.flatten()
+        inp = draw_inputs(sub, sh, cfg.seed, cfg.dtype, cfg.mu_a, request_streams=[tree.segs[leaf].request])
+        ts, par, fkk, cl = sub.arrays()
+        args = {n: inp.f64(n) for n in inp.raw}
+        t0 = time.perf_counter()
+        oracle.attention(ts, par, fkk, cl, inp.hist_off, args["aq"], args["ak"], args["av"], None, None,
+                         sh.d ** -0.5, mode=0, head_sel=a_sel)
+        t1 = time.perf_counter()
+        oracle.gdn(ts, par, fkk, cl, args["gq"], args["gk"], args["gv"], args["ga"], args["gb"], mode=0,
+                   head_sel=g_sel)
+        t2 = time.perf_counter()
+        t_attn += (t1 - t0) * sh.Hq
+        t_gdn += (t2 - t1) * sh.Hv
+    sl = lens[pick]
+    total = t_attn * (lens ** 2).sum() / (sl ** 2).sum() + t_gdn * lens.sum() / sl.sum()
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    bt = tree.branch_tokens()
+    return {"value": bt / total, "unit": "branch tokens/s", "cores": cores, "kind": "oracle", **host_cpu(),
+            "extrapolated": True,
+            "sample": f"{len(pick)} of {len(leaves)} leaf paths (seeded), each alone in fp64 literal mode, "
+                      f"one attention q head and one GDN v-head timed "
+                      f"({(t_attn / sh.Hq + t_gdn / sh.Hv):.1f} s), scaled to all {sh.Hq} q / {sh.Hv} v heads "
+                      f"and to every leaf path (sum of squared path lengths for attention, of lengths for "
+                      f"GDN): {total:.0f} s for the whole workload"}
 
 
 def cpu_baseline_resume(n_req: int):
