@@ -314,6 +314,7 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     const int tok = row0 + w * 4 + n / 8;          // local token of this lane's row
     const int h = g * G + (n % 8);
     const bool row_valid = tok < len;
+    const bool wave_live = row0 + w * 4 < len;   // wave-uniform
     const size_t t_glob = (size_t)seg_start[s] + tok;
     const size_t qrow = t_glob * Hq + h;
 
@@ -373,7 +374,10 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             const int lo = (RULE == WINDOW ? pdiff + tok - window + 1 - key0 : 0) - half * 8;
             const bool full = (causal_own ? (key0 + BN - 1 <= row0) : (key0 + BN <= count)) &&
                               (RULE != WINDOW || key0 >= pdiff + row0 + FK_TILE_TOKENS - window);
-            block_compute<RULE>(k_lds[buf], v_lds[buf], qf, o, m, l, full, hi, lo, prow, half, n, scale_log2e);
+            // a wave whose four tokens all lie past the segment's end (in the
+            // segment's last tile) only helps stage the blocks
+            if (wave_live)
+                block_compute<RULE>(k_lds[buf], v_lds[buf], qf, o, m, l, full, hi, lo, prow, half, n, scale_log2e);
         }
         if (!more) break;
         store_block(k_lds[buf ^ 1], v_lds[buf ^ 1], R);
