@@ -789,7 +789,8 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
 #pragma unroll
         for (int mt = 0; mt < C / 16; ++mt) {
             ua[mt] = mfma(load_perm(B.tm, mt * 16 + c16, 0, G), rb0, f32x4{0.f, 0.f, 0.f, 0.f});
-            ua[mt] = mfma(load_perm(B.tm, mt * 16 + c16, 1, G), rb1, ua[mt]);
+            // T is lower triangular: rows 0..31 have no entries in columns 32..63
+            if (mt >= 2) ua[mt] = mfma(load_perm(B.tm, mt * 16 + c16, 1, G), rb1, ua[mt]);
         }
         __builtin_amdgcn_sched_barrier(0);
         // O = diag(e^l) Y + P U  -> left in the value buffer for the producers
