@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=1, help="workload index (0-4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=16,
@@ -150,7 +150,38 @@ def visible_pairs(tree) -> int:
     return tot
 
 
-class Workload:
+class Step:
+    """One step = four phases on torch's current stream: build (on the resume
+    workload: resume + build), K/V append, ForkAttention, forked GDN (on the
+    resume workload: + checkpoint save).  GDN reads nothing the append or the
+    attention write, so the overlapped form runs the GDN phase on a second
+    stream, forked after the build and joined at the end; its outputs are
+    bit-identical to the serial form's."""
+
+    def step(self, ev=None):
+        """Serial; with ``ev`` (five events) the phase boundaries are recorded."""
+        for i, phase in enumerate((self.build, self.append, self.attention, self.gdn)):
+            if ev:
+                ev[i].record()
+            phase()
+        if ev:
+            ev[4].record()
+
+    def step_overlapped(self):
+        torch = self.torch
+        if not hasattr(self, "_side"):
+            self._side = torch.cuda.Stream()   # default priority
+        self.build()
+        cur = torch.cuda.current_stream()
+        self._side.wait_stream(cur)
+        with torch.cuda.stream(self._side):
+            self.gdn()
+        self.append()
+        self.attention()
+        cur.wait_stream(self._side)
+
+
+class Workload(Step):
     """A config's round resident on the GPU, ready to step."""
 
     def __init__(self, index: int, device="cuda"):
@@ -190,20 +221,20 @@ class Workload:
         self.scale = sh.d ** -0.5
         self.gdn_ok = True
 
-    def step(self, ev=None):
+    def build(self):
+        self.fk.fk_tree_build(self.meta, self.ws)
+
+    def append(self):
+        x = self.x
+        self.fk.kv_append(self.meta, x["ak"], x["av"], self.k_pool, self.v_pool, self.ws)
+
+    def attention(self):
+        x = self.x
+        self.fk.fork_attn_forward(self.meta, x["aq"], None, None, self.k_pool, self.v_pool, self.ws,
+                                  scale=self.scale, out=self.attn_out)
+
+    def gdn(self):
         fk, x = self.fk, self.x
-        if ev:
-            ev[0].record()
-        fk.fk_tree_build(self.meta, self.ws)
-        if ev:
-            ev[1].record()
-        fk.kv_append(self.meta, x["ak"], x["av"], self.k_pool, self.v_pool, self.ws)
-        if ev:
-            ev[2].record()
-        fk.fork_attn_forward(self.meta, x["aq"], None, None, self.k_pool, self.v_pool, self.ws,
-                             scale=self.scale, out=self.attn_out)
-        if ev:
-            ev[3].record()
         if self.gdn_ok:
             try:
                 fk.gdn_fork_forward(self.meta, x["gq"], x["gk"], x["gv"], x["ga"], x["gb"], self.ws,
@@ -212,11 +243,9 @@ class Workload:
                 if e.name != "FK_E_UNSUPPORTED":
                     raise
                 self.gdn_ok = False
-        if ev:
-            ev[4].record()
 
 
-class ResumeWorkload:
+class ResumeWorkload(Step):
     """The expanding-history workload: every request resumes from a checkpoint
     -- the fp32 GDN state and the 16,384-token paged K/V of its history, made
     by an untimed GPU pass over that history -- appends 1,024 new tokens and
@@ -319,26 +348,24 @@ class ResumeWorkload:
         torch.cuda.synchronize()
         del hws, hst
 
-    def step(self, ev=None):
+    def build(self):
+        self.fk.gdn_checkpoint_resume(self.ckpt, self.state_in, 0, count=self.R)
+        self.fk.fk_tree_build(self.meta, self.ws)
+
+    def append(self):
+        x = self.x
+        self.fk.kv_append(self.meta, x["ak"], x["av"], self.k_pool, self.v_pool, self.ws)
+
+    def attention(self):
+        x = self.x
+        self.fk.fork_attn_forward(self.meta, x["aq"], None, None, self.k_pool, self.v_pool, self.ws,
+                                  scale=self.scale, out=self.attn_out)
+
+    def gdn(self):
         fk, x = self.fk, self.x
-        if ev:
-            ev[0].record()
-        fk.gdn_checkpoint_resume(self.ckpt, self.state_in, 0, count=self.R)
-        fk.fk_tree_build(self.meta, self.ws)
-        if ev:
-            ev[1].record()
-        fk.kv_append(self.meta, x["ak"], x["av"], self.k_pool, self.v_pool, self.ws)
-        if ev:
-            ev[2].record()
-        fk.fork_attn_forward(self.meta, x["aq"], None, None, self.k_pool, self.v_pool, self.ws,
-                             scale=self.scale, out=self.attn_out)
-        if ev:
-            ev[3].record()
         fk.gdn_fork_forward(self.meta, x["gq"], x["gk"], x["gv"], x["ga"], x["gb"], self.ws,
                             state_in=self.state_in, state_out=self.state_out, out=self.gdn_out)
         fk.gdn_checkpoint_save(self.state_out, 0, self.ckpt_next, count=self.R)
-        if ev:
-            ev[4].record()
 
 
 def gdn_bytes(tree, sh, elem: int, resumed_save: bool = False) -> int:
@@ -674,27 +701,52 @@ def main():
     dist = None
     if not args.eager:
         # the same step recorded once as a HIP graph and replayed: the
-        # headline timing (no launch gaps between the step's kernels)
-        graph = wl.fk.StepGraph(wl.step, warmup=1)
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
+        # headline timing (no launch gaps between the step's kernels).  Both
+        # forms of the step are recorded -- serial, and the GDN phase on a
+        # second stream beside the append and the attention -- and the one
+        # whose warm replays are faster is timed: the overlap pays where
+        # the GDN phase is comparable to the attention (the mixture) and
+        # costs where a long attention launch shares the chip with it.
+        def warm(g):
+            # untimed replays: at least `warmup`, and at least 30 ms of them
+            # (the first ~20 replays of the mixture run ~6% slower while the
+            # clocks settle)
+            n, tw = 0, time.perf_counter()
+            while n < args.warmup or time.perf_counter() - tw < 0.03:
+                g.replay()
+                n += 1
+                if n % 8 == 0:
+                    torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            return n
+
+        def replay_ms(g, n):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+            for e in ev:
+                e[0].record()
+                g.replay()
+                e[1].record()
+            torch.cuda.synchronize()
+            return np.array([e[0].elapsed_time(e[1]) for e in ev])
+
+        forms, n_warm = {}, 0
+        for name, fn in (("serial", wl.step), ("GDN phase on a second stream", wl.step_overlapped)):
+            g = wl.fk.StepGraph(fn, warmup=1)
+            n_warm += warm(g)
+            forms[name] = (float(np.median(replay_ms(g, 5))), g)
+        form = min(forms, key=lambda k: forms[k][0])
+        graph = forms[form][1]
+        n_warm += warm(graph)
         t0 = time.perf_counter()
         for _ in range(args.steps):
             graph.replay()
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-        mode = "HIP graph replay"
+        mode = f"HIP graph replay ({form})"
         assert wl.fk.fk_read_status(wl.ws) == 0, "tree build reported an error"
         # per-replay distribution (HIP events), warm and with the caches
         # flushed before each step (a 512 MiB write evicts L2 and MALL)
-        rep = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for e in rep:
-            e[0].record()
-            graph.replay()
-            e[1].record()
-        torch.cuda.synchronize()
-        warm = np.array([e[0].elapsed_time(e[1]) for e in rep])
+        warm_ms = replay_ms(graph, args.steps)
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         cold = []
         for _ in range(min(args.steps, 10)):
@@ -706,8 +758,8 @@ def main():
             torch.cuda.synchronize()
             cold.append(e[0].elapsed_time(e[1]))
         del flush
-        dist = {"warm_p10": float(np.percentile(warm, 10)), "warm_p50": float(np.percentile(warm, 50)),
-                "warm_p90": float(np.percentile(warm, 90)), "cold_p50": float(np.median(cold)),
+        dist = {"warm_p10": float(np.percentile(warm_ms, 10)), "warm_p50": float(np.percentile(warm_ms, 50)),
+                "warm_p90": float(np.percentile(warm_ms, 90)), "cold_p50": float(np.median(cold)),
                 "cold_flush_bytes": 512 << 20}
     attn_ms = float(phase[:, 2].mean())
     nvis = visible_pairs(tree)
@@ -731,6 +783,8 @@ def main():
                    "stream_tokens": tree.T, "branch_tokens": bt, "segments": tree.S,
                    "attn_heads": [sh.Hq, sh.Hkv, sh.d], "gdn_heads": [sh.Hk, sh.Hv, sh.dk, sh.dv]},
         "execution": mode,
+        "graph_warmup_replays": None if args.eager else n_warm,
+        "graph_forms_ms": None if args.eager else {k: v[0] for k, v in forms.items()},
         "step_ms_distribution": dist,
         "stream_tokens_per_s": tree.T / (ms_step * 1e-3),
         "path_equivalent_tokens_per_s": path_tokens(tree) / (ms_step * 1e-3),

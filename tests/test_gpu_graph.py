@@ -74,3 +74,46 @@ def test_graph_replay_bitwise():
     assert torch.equal(a_g, a_out)
     assert torch.equal(g_g, g_out)
     assert not torch.equal(a_g, a_ref)
+
+
+def test_graph_two_streams_bitwise():
+    """The GDN calls read nothing the K/V append or the attention writes, so a
+    round may run them on a second stream, forked after the build and joined
+    at the end, inside one graph: every replay gives the serial run's bits."""
+    r = _round(32)
+    print(f"[graph two streams] T={r.inp.tree.T} S={r.inp.tree.S}", flush=True)
+    a_out = torch.empty_like(r.x["aq"])
+    g_out = torch.empty_like(r.x["gv"])
+    _step(r, a_out, g_out)
+    torch.cuda.synchronize()
+    assert r.status() == 0
+    a_ref, g_ref, s_ref = a_out.clone(), g_out.clone(), r.state_out.clone()
+    side = torch.cuda.Stream()
+    x = r.x
+
+    def forked():
+        fk.fk_tree_build(r.meta, r.ws)
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            fk.gdn_fork_forward(r.meta, x["gq"], x["gk"], x["gv"], x["ga"], x["gb"], r.ws,
+                                state_in=r.state_in, state_out=r.state_out if r.n_out else None, out=g_out)
+        fk.kv_append(r.meta, x["ak"], x["av"], r.k_pool, r.v_pool, r.ws)
+        fk.fork_attn_forward(r.meta, x["aq"], None, None, r.k_pool, r.v_pool, r.ws, out=a_out)
+        cur.wait_stream(side)
+
+    graph = fk.StepGraph(forked)
+    for rep in range(3):
+        a_out.zero_()
+        g_out.zero_()
+        r.state_out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        z = torch.randn(512, 512, device="cuda")
+        (z @ z).sum().item()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert r.status() == 0
+        assert torch.equal(a_out, a_ref), rep
+        assert torch.equal(g_out, g_ref), rep
+        if r.n_out:
+            assert torch.equal(r.state_out[: r.n_out], s_ref[: r.n_out]), rep
