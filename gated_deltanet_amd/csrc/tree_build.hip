@@ -4,15 +4,15 @@
 // table is built on the GPU; section 3.3.2: launch sizes come from host-known
 // capacities, so the host never reads the tree).
 //
-// Kernels (five launches):
+// Kernels (four launches):
 //   k_init     grid over S   zero the header and per-segment counters
 //   k_tokens   grid over T   token runs of every segment (start, end, run count)
 //   k_build    one block     validation, lengths, first positions, ancestor
 //                            chains, tile / chunk / level offsets, fork points
-//   k_post     grid          tile and chunk lists, page-id checks (a block per
-//                            segment), per-token positions
-//   k_orders   1 + levels    tile order (heaviest first), each level's
-//                            segments by decreasing chunk count
+//   k_post     grid          tile order (heaviest first) and each level's
+//                            segments by decreasing chunk count (1 + levels
+//                            blocks), tile and chunk lists, page-id checks (a
+//                            block per segment), per-token positions
 // No dense T x T mask is ever formed: a tile's key ranges follow from its
 // segment's ancestor chain and the forks along it.
 #include <hip/hip_runtime.h>
@@ -91,11 +91,18 @@ struct BuildArgs {
     int32_t *seg_tile0, *seg_coff;
 };
 
-__device__ bool block_failed(int32_t *header, int *flag)
+// k_build is the only writer of the status while it runs, so after reading
+// the status once it mirrors its own errors in an LDS flag: a phase boundary
+// is then a barrier, not a round trip to global memory.
+__device__ __forceinline__ void build_error(int32_t *header, int *flag, int code)
+{
+    set_error(header, code);
+    *flag = code;   // any nonzero value marks the failure
+}
+
+__device__ bool block_failed(int *flag)
 {
     __threadfence_block();
-    __syncthreads();
-    if (threadIdx.x == 0) *flag = __hip_atomic_load(header + H_STATUS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     return *flag != FK_OK;
 }
@@ -107,7 +114,8 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
     __shared__ int flag;
     const fk_tree_meta &m = A.m;
     const int S = m.S;
-    if (block_failed(A.header, &flag)) return;   // phase 0 failed
+    if (threadIdx.x == 0) flag = __hip_atomic_load(A.header + H_STATUS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (block_failed(&flag)) return;   // phase 0 failed
 
     // phase 1: lengths
     for (int s = threadIdx.x; s < S; s += blockDim.x) {
@@ -115,11 +123,11 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
         int len = 0;
         const int code = rule_length(m.seg_cached_len[s], nrun,
                                      nrun == 1 ? A.seg_end[s] - A.seg_start[s] : 0, &len);
-        if (code) set_error(A.header, code);
+        if (code) build_error(A.header, &flag, code);
         A.seg_len[s] = len;
         if (m.seg_cached_len[s] > 0) A.seg_start[s] = -1;
     }
-    if (block_failed(A.header, &flag)) return;
+    if (block_failed(&flag)) return;
 
     // phase 2: links, chains, slots, pages; GDN sources of children of cached
     // or fresh roots; child counts of live parents
@@ -129,7 +137,7 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
                                     A.seg_len, m.seg_state_in, m.n_state_in, m.seg_state_out,
                                     m.n_state_out, m.seg_page_off, m.seg_pages, m.page_size,
                                     m.n_pages, &d);
-        if (code) set_error(A.header, code);
+        if (code) build_error(A.header, &flag, code);
         A.seg_depth[s] = d.depth;
         A.seg_pos0[s] = d.pos0;
         for (int j = 0; j < FK_MAX_DEPTH; ++j) A.seg_anc[s * FK_MAX_DEPTH + j] = j <= d.depth ? d.anc[j] : -1;
@@ -142,7 +150,7 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
         }
         A.seg_src[s] = src;
     }
-    if (block_failed(A.header, &flag)) return;
+    if (block_failed(&flag)) return;
 
     // phase 3a: scans -- attention tiles, children CSR, level lists
     if (threadIdx.x < FK_MAX_DEPTH) lvl_lds[threadIdx.x] = 0;
@@ -176,7 +184,7 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
             if (live && depth == dd) {
                 const int rank = lvl_lds[dd] + pos;
                 if (rank < m.level_cap) A.lvl_seg[dd * m.level_cap + rank] = s;
-                else set_error(A.header, FK_E_CAPACITY);
+                else build_error(A.header, &flag, FK_E_CAPACITY);
             }
             __syncthreads();
             if (threadIdx.x == 0) lvl_lds[dd] += tot;
@@ -199,7 +207,7 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
             A.kids[A.kid_off[p] + at] = s;
         }
     }
-    if (block_failed(A.header, &flag)) return;
+    if (block_failed(&flag)) return;
 
     // phase 3b: fork points -- one slot per distinct (parent, fork offset);
     // the lowest-index child at an offset owns it
@@ -231,9 +239,9 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
     if (threadIdx.x == 0) {
         A.emit_off[S] = emit_base;
         A.header[H_NFORKS] = emit_base;
-        if (emit_base > m.fork_cap) set_error(A.header, FK_E_CAPACITY);
+        if (emit_base > m.fork_cap) build_error(A.header, &flag, FK_E_CAPACITY);
     }
-    if (block_failed(A.header, &flag)) return;
+    if (block_failed(&flag)) return;
     for (int c = threadIdx.x; c < S; c += blockDim.x) {
         const int p = m.seg_parent[c];
         if (m.seg_cached_len[c] == 0 && p >= 0 && m.seg_cached_len[p] == 0) {
@@ -283,18 +291,25 @@ __device__ void lists_thread(int i, int S, const int32_t *__restrict__ header, c
 // Tiles by decreasing count of visible 64-key blocks (a bucket sort; order
 // within a bucket is whatever the atomics give).  Only the schedule of the
 // attention launch depends on it -- every tile computes the same way in any
-// order -- so the heaviest tiles start first and the launch ends evenly.
+// order -- so the heaviest tiles start first and the launch ends evenly.  It
+// runs beside the blocks that write the tile list, so it finds each tile's
+// segment itself, with the same search over seg_tile0 (staged in LDS when S
+// fits there).
 constexpr int ORDER_BUCKETS = 2 * BUILD_THREADS;
-__device__ void tile_order_block(const int32_t *__restrict__ header, const int32_t *__restrict__ tile_seg,
-                                 const int32_t *__restrict__ tile_row0, const int32_t *__restrict__ seg_pos0,
-                                 const int32_t *__restrict__ seg_len, int32_t *__restrict__ tile_order, int *cnt,
-                                 int *lds)
+constexpr int ORDER_STAGE = 4096;
+__device__ void tile_order_block(const int32_t *__restrict__ header, int S, const int32_t *__restrict__ seg_tile0,
+                                 const int32_t *__restrict__ seg_pos0, const int32_t *__restrict__ seg_len,
+                                 int32_t *__restrict__ tile_order, int *cnt, int *lds, int *stage)
 {
     const int n = header[H_NTILES];
+    const bool staged = S <= ORDER_STAGE;
+    if (staged)
+        for (int i = threadIdx.x; i < S; i += blockDim.x) stage[i] = seg_tile0[i];
     for (int b = threadIdx.x; b < ORDER_BUCKETS; b += blockDim.x) cnt[b] = 0;
     __syncthreads();
+    const int32_t *first = staged ? stage : seg_tile0;
     auto bucket = [&](int t) {
-        const int s = tile_seg[t], r0 = tile_row0[t];
+        const int s = owner_of(first, S, t), r0 = (t - first[s]) * FK_TILE_TOKENS;
         const int keys = seg_pos0[s] + min(r0 + FK_TILE_TOKENS, seg_len[s]);
         return min((keys + 63) / 64, ORDER_BUCKETS - 1);
     };
@@ -348,22 +363,6 @@ __device__ void level_order_block(int lvl, const int32_t *__restrict__ header, c
     for (int i = threadIdx.x; i < n; i += blockDim.x) dst[atomicAdd(&cnt[bucket(i)], 1)] = src[i];
 }
 
-// Both orders in one launch: block 0 orders the tiles, block 1 + l level l.
-__global__ void __launch_bounds__(BUILD_THREADS)
-k_orders(const int32_t *__restrict__ header, const int32_t *__restrict__ tile_seg,
-         const int32_t *__restrict__ tile_row0, const int32_t *__restrict__ seg_pos0,
-         const int32_t *__restrict__ seg_len, int32_t *__restrict__ tile_order, const int32_t *__restrict__ lvl_seg,
-         const int32_t *__restrict__ seg_src, int level_cap, int32_t *__restrict__ lvl_sorted)
-{
-    __shared__ int cnt[ORDER_BUCKETS];
-    __shared__ int lds[32];
-    if (header[H_STATUS] != FK_OK) return;
-    if (blockIdx.x == 0)
-        tile_order_block(header, tile_seg, tile_row0, seg_pos0, seg_len, tile_order, cnt, lds);
-    else
-        level_order_block(blockIdx.x - 1, header, lvl_seg, seg_len, seg_src, level_cap, lvl_sorted, cnt, lds);
-}
-
 // Phase 3 (pages): one block per segment checks the page ids the segment
 // uses, in parallel.  Runs only when the tree passed every other check.
 __device__ void check_pages_block(int s, const int32_t *__restrict__ seg_len, const int32_t *__restrict__ page_off,
@@ -382,26 +381,38 @@ __device__ void positions_thread(int t, const int32_t *__restrict__ tok_seg, int
     tok_pos[t] = seg_pos0[s] + (t - seg_start[s]);
 }
 
-// After k_build, in one launch of 256-thread blocks: the tile and chunk lists
-// (blocks [0, nl)), the page checks (one block per segment, [nl, nl + np)),
-// the token positions (the rest).
-__global__ void __launch_bounds__(256)
-k_post(int nl, int np, int S, int T, int32_t *header, const int32_t *__restrict__ seg_tile0,
+// After k_build, in one launch of BUILD_THREADS-thread blocks: the orders
+// (block 0 the tiles, block 1 + l level l; [0, no)), the tile and chunk
+// lists ([no, no + nl)), the page checks (one block per segment,
+// [no + nl, no + nl + np)), the token positions (the rest).  No block reads
+// what another writes.
+__global__ void __launch_bounds__(BUILD_THREADS)
+k_post(int no, int nl, int np, int S, int T, int32_t *header, const int32_t *__restrict__ seg_tile0,
        const int32_t *__restrict__ seg_coff, int32_t *__restrict__ tile_seg, int32_t *__restrict__ tile_row0,
        int32_t *__restrict__ chunk_seg, int32_t *__restrict__ chunk_row0, const int32_t *__restrict__ seg_len,
        const int32_t *__restrict__ page_off, const int32_t *__restrict__ pages, int page_size, int n_pages,
        const int32_t *__restrict__ tok_seg, const int32_t *__restrict__ seg_start,
-       const int32_t *__restrict__ seg_pos0, int32_t *__restrict__ tok_pos)
+       const int32_t *__restrict__ seg_pos0, int32_t *__restrict__ tok_pos, int32_t *__restrict__ tile_order,
+       const int32_t *__restrict__ lvl_seg, const int32_t *__restrict__ seg_src, int level_cap,
+       int32_t *__restrict__ lvl_sorted)
 {
+    __shared__ int cnt[ORDER_BUCKETS];
+    __shared__ int stage[ORDER_STAGE];
+    __shared__ int lds[32];
     if (header[H_STATUS] != FK_OK) return;
     const int b = blockIdx.x;
-    if (b < nl)
-        lists_thread(b * 256 + threadIdx.x, S, header, seg_tile0, seg_coff, tile_seg, tile_row0, chunk_seg,
-                     chunk_row0);
-    else if (b < nl + np)
-        check_pages_block(b - nl, seg_len, page_off, pages, page_size, n_pages, header);
+    if (b == 0)
+        tile_order_block(header, S, seg_tile0, seg_pos0, seg_len, tile_order, cnt, lds, stage);
+    else if (b < no)
+        level_order_block(b - 1, header, lvl_seg, seg_len, seg_src, level_cap, lvl_sorted, cnt, lds);
+    else if (b < no + nl)
+        lists_thread((b - no) * BUILD_THREADS + threadIdx.x, S, header, seg_tile0, seg_coff, tile_seg, tile_row0,
+                     chunk_seg, chunk_row0);
+    else if (b < no + nl + np)
+        check_pages_block(b - no - nl, seg_len, page_off, pages, page_size, n_pages, header);
     else
-        positions_thread((b - nl - np) * 256 + threadIdx.x, tok_seg, T, seg_start, seg_pos0, tok_pos);
+        positions_thread((b - no - nl - np) * BUILD_THREADS + threadIdx.x, tok_seg, T, seg_start, seg_pos0,
+                         tok_pos);
 }
 
 int check_meta_scalars(const fk_tree_meta *m)
@@ -475,15 +486,13 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
     if ((rc = launch_status())) return rc;
     {
         const int64_t n = L.tile_cap > L.chunk_cap ? L.tile_cap : L.chunk_cap;
-        const int nl = (int)((n + 255) / 256), np = meta->seg_page_off ? S : 0, nt = (T + 255) / 256;
-        k_post<<<(unsigned)(nl + np + nt), 256, 0, st>>>(
-            nl, np, S, T, A.header, A.seg_tile0, A.seg_coff, A.tile_seg, A.tile_row0, A.chunk_seg, A.chunk_row0,
-            A.seg_len, meta->seg_page_off, meta->seg_pages, meta->page_size, meta->n_pages, meta->tok_seg,
-            A.seg_start, A.seg_pos0, ws_at<int32_t>(ws, L.tok_pos));
-        if ((rc = launch_status())) return rc;
-        k_orders<<<(unsigned)(1 + meta->max_depth), BUILD_THREADS, 0, st>>>(
-            A.header, A.tile_seg, A.tile_row0, A.seg_pos0, A.seg_len, ws_at<int32_t>(ws, L.tile_order), A.lvl_seg,
-            ws_at<int32_t>(ws, L.seg_src), meta->level_cap, ws_at<int32_t>(ws, L.lvl_sorted));
+        const int no = 1 + meta->max_depth, nl = (int)((n + BUILD_THREADS - 1) / BUILD_THREADS);
+        const int np = meta->seg_page_off ? S : 0, nt = (T + BUILD_THREADS - 1) / BUILD_THREADS;
+        k_post<<<(unsigned)(no + nl + np + nt), BUILD_THREADS, 0, st>>>(
+            no, nl, np, S, T, A.header, A.seg_tile0, A.seg_coff, A.tile_seg, A.tile_row0, A.chunk_seg,
+            A.chunk_row0, A.seg_len, meta->seg_page_off, meta->seg_pages, meta->page_size, meta->n_pages,
+            meta->tok_seg, A.seg_start, A.seg_pos0, ws_at<int32_t>(ws, L.tok_pos), ws_at<int32_t>(ws, L.tile_order),
+            A.lvl_seg, ws_at<int32_t>(ws, L.seg_src), meta->level_cap, ws_at<int32_t>(ws, L.lvl_sorted));
         if ((rc = launch_status())) return rc;
     }
     return FK_OK;
