@@ -207,7 +207,9 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
             __bf16 p4[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) p4[r] = (__bf16)acc[r];
-            if (valid && i < n)   // rows past the chunk's last token are never read
+            // rows past the chunk's last token are never read, nor is the
+            // zero block of rows 0-31 x columns 32-63
+            if (valid && i < n && !(it < 2 && jt >= 2))
                 *reinterpret_cast<uint2 *>(pdst + i * C + perm_off(jt * 16 + G * 4)) = __builtin_bit_cast(uint2, p4);
         }
     }
@@ -307,10 +309,13 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     put(3, 0, t30);
     __syncthreads();
     if (!valid || lane >= n) return;   // rows past the chunk's last token are never read
-    // row `lane` of T, stored permuted (both T and P serve as A operands)
+    // row `lane` of T, stored permuted (both T and P serve as A operands);
+    // the zero block of rows 0-31 x columns 32-63 (stored units 4-7) is
+    // never read
     uint16_t *dst = tmat + (((size_t)c * Hv + h) * C + lane) * C;
 #pragma unroll
     for (int j8 = 0; j8 < C / 8; ++j8) {
+        if (j8 >= 4 && lane < 32) continue;
         // stored elements [8 j8, 8 j8 + 8): positions 4G'..4G'+3 and
         // 16+4G'..16+4G'+3 of block j8/4, G' = j8 % 4 (each group of four
         // lies in one 16-column block, above the diagonal block or not)
@@ -554,8 +559,12 @@ __device__ __forceinline__ void load_step(StepRegs &R, const ChunkArgs &A, const
         const int idx = j * 64 + lane, row = rb + (idx >> 3), c8 = idx & 7;
         R.tv[j] = R.pv[j] = R.vv[j] = make_uint4(0, 0, 0, 0);
         if (row < n) {
-            R.tv[j] = buf_load(rt, row * C * 2 + c8 * 16);
-            R.pv[j] = buf_load(rp, row * C * 2 + c8 * 16);
+            // T and P: the block of rows 0-31 x columns 32-63 (units 4-7)
+            // is zero and never read, and is not stored
+            if (row >= 32 || c8 < 4) {
+                R.tv[j] = buf_load(rt, row * C * 2 + c8 * 16);
+                R.pv[j] = buf_load(rp, row * C * 2 + c8 * 16);
+            }
             R.vv[j] = buf_load(rv, row * v_row + c8 * 16);
         }
     }
