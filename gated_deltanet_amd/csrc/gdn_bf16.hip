@@ -130,13 +130,14 @@ __device__ __forceinline__ bf16x8 load_row8(const uint16_t *row, int ks, int G)
 // Key and query rows are loaded straight into MFMA operand registers (the
 // A and B operand layouts of a 16x16x32 product coincide); LDS holds the
 // diagonal blocks and the finished T.  Four items per work-group, one wave
-// each.
+// each.  Query tiles are loaded one at a time, as P uses them, so a wave
+// fits in 128 VGPRs and four work-groups share a CU.
 // ---------------------------------------------------------------------------
 constexpr int PREP_WAVES = 4;
 constexpr int TBS = C + 8;        // LDS stride (bf16) of the finished T rows
 constexpr int PREP_SCR = C * TBS * 2 > 4 * (16 * 16 + 16) * 4 ? C * TBS * 2 : 4 * (16 * 16 + 16) * 4;
 
-__global__ void __launch_bounds__(64 * PREP_WAVES, 3)
+__global__ void __launch_bounds__(64 * PREP_WAVES, 4)
 k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ a,
            const float *__restrict__ b, int Hk, int Hv, const int32_t *__restrict__ header,
            const int32_t *__restrict__ chunk_seg, const int32_t *__restrict__ chunk_row0,
@@ -160,20 +161,20 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     const int n = valid ? min(C, seg_len[s] - r0) : 1;
     const size_t t0 = (size_t)seg_start[s] + r0;
     const int g = h / (Hv / Hk);
-    // operand fragments: rows 16*t + c16, dims 32*kk + 8*G .. +8 (zero past n)
-    bf16x8 kf[4][4], qf[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    // operand fragments: rows 16*t + c16, dims 32*kk + 8*G .. +8 (zero past n);
+    // all key tiles are held, query tiles only while P uses them
+    auto frag = [&](const uint16_t *src, int t, bf16x8 *f) {
         const int row = t * 16 + c16, rr = row < n ? row : n - 1;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            uint4 kv = *reinterpret_cast<const uint4 *>(k + ((t0 + rr) * Hk + g) * DK + kk * 32 + G * 8);
-            uint4 qv = *reinterpret_cast<const uint4 *>(q + ((t0 + rr) * Hk + g) * DK + kk * 32 + G * 8);
-            if (row >= n) kv = qv = make_uint4(0, 0, 0, 0);
-            kf[t][kk] = as_bf16x8(kv);
-            qf[t][kk] = as_bf16x8(qv);
+            uint4 v = *reinterpret_cast<const uint4 *>(src + ((t0 + rr) * Hk + g) * DK + kk * 32 + G * 8);
+            if (row >= n) v = make_uint4(0, 0, 0, 0);
+            f[kk] = as_bf16x8(v);
         }
-    }
+    };
+    bf16x8 kf[4][4], qc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) frag(k, t, kf[t]);
     const int lr = lane < n ? lane : n - 1;
     float la = lane < n ? logf(a[(t0 + lr) * Hv + h]) : 0.f;
     const float eta = lane < n ? b[(t0 + lr) * Hv + h] : 0.f;
@@ -190,6 +191,7 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     uint16_t *pdst = pmat + ((size_t)c * Hv + h) * C * C;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
+        frag(q, it, qc);
         const int i = it * 16 + c16;
         const float li = lsh[i];
 #pragma unroll
@@ -197,7 +199,7 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (jt <= it) {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[jt][kk], qf[it][kk], acc);
+                for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[jt][kk], qc[kk], acc);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = jt * 16 + G * 4 + r;
