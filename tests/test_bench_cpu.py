@@ -55,3 +55,18 @@ def test_path_tokens_by_hand():
     # a lone root is its own leaf; a cached history counts toward its leaf's path
     assert bench.path_tokens(build_tree([[(-1, 0, 7)]]).flatten()) == 7
     assert bench.path_tokens(build_tree([[(-1, 0, 7, True), (0, None, 5)]]).flatten()) == 12
+
+
+def test_more_than_one_gpu_is_refused():
+    # one GPU only: asked for more, the bench says so in its one line and exits
+    import json
+    import subprocess
+    import sys
+    from pathlib import Path
+
+    root = Path(bench.__file__).resolve().parent
+    r = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120, cwd=root)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
