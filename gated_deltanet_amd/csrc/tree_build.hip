@@ -4,10 +4,10 @@
 // table is built on the GPU; section 3.3.2: launch sizes come from host-known
 // capacities, so the host never reads the tree).
 //
-// Kernels (four launches):
-//   k_init     grid over S   zero the header and per-segment counters
-//   k_tokens   grid over T   token runs of every segment (start, end, run count)
-//   k_build    one block     validation, lengths, first positions, ancestor
+// Kernels (two launches):
+//   k_build    one block     clears the status and counters, token runs of
+//                            every segment (start, end, run count),
+//                            validation, lengths, first positions, ancestor
 //                            chains, tile / chunk / level offsets, fork points
 //   k_post     grid          tile order (heaviest first) and each level's
 //                            segments by decreasing chunk count (1 + levels
@@ -25,37 +25,6 @@
 namespace fk {
 
 constexpr int BUILD_THREADS = 1024;
-
-__global__ void k_init(int32_t *header, int32_t *seg_nrun, int32_t *kid_cnt, int32_t *kid_fill,
-                       int S)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < H_WORDS) header[i] = 0;
-    for (int s = i; s < S; s += gridDim.x * blockDim.x) {
-        seg_nrun[s] = 0;
-        kid_cnt[s] = 0;
-        kid_fill[s] = 0;
-    }
-}
-
-// Phase 0: each token checks its segment id; the first token of every run
-// records the run start, the last its end, and counts the run.
-__global__ void k_tokens(const int32_t *__restrict__ tok_seg, int T, int S, int32_t *header,
-                         int32_t *seg_start, int32_t *seg_end, int32_t *seg_nrun)
-{
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= T) return;
-    const int s = tok_seg[t];
-    if (s < 0 || s >= S) {
-        set_error(header, FK_E_SEG_RANGE);
-        return;
-    }
-    if (t == 0 || tok_seg[t - 1] != s) {
-        atomicAdd(seg_nrun + s, 1);   // an integer count: order-independent
-        seg_start[s] = t;             // meaningful only when the run count is 1
-    }
-    if (t == T - 1 || tok_seg[t + 1] != s) seg_end[s] = t + 1;
-}
 
 // Exclusive prefix sum over the block (BUILD_THREADS threads, wave64).
 __device__ int block_scan(int x, int *lds, int *total)
@@ -91,9 +60,9 @@ struct BuildArgs {
     int32_t *seg_tile0, *seg_coff;
 };
 
-// k_build is the only writer of the status while it runs, so after reading
-// the status once it mirrors its own errors in an LDS flag: a phase boundary
-// is then a barrier, not a round trip to global memory.
+// k_build is the only writer of the status while it runs, so it mirrors its
+// own errors in an LDS flag: a phase boundary is then a barrier, not a round
+// trip to global memory.
 __device__ __forceinline__ void build_error(int32_t *header, int *flag, int code)
 {
     set_error(header, code);
@@ -114,8 +83,45 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
     __shared__ int flag;
     const fk_tree_meta &m = A.m;
     const int S = m.S;
-    if (threadIdx.x == 0) flag = __hip_atomic_load(A.header + H_STATUS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (block_failed(&flag)) return;   // phase 0 failed
+    // phase 0: clear the status and the per-segment counters; then each
+    // token checks its segment id, and the first token of every run records
+    // the run start, the last its end, and counts the run
+    for (int i = threadIdx.x; i < H_WORDS; i += blockDim.x) A.header[i] = 0;
+    for (int s = threadIdx.x; s < S; s += blockDim.x) {
+        A.seg_nrun[s] = 0;
+        A.kid_cnt[s] = 0;
+        A.kid_fill[s] = 0;
+    }
+    if (threadIdx.x == 0) flag = FK_OK;
+    __threadfence_block();
+    __syncthreads();
+    const int T = m.T;
+    constexpr int TB = 8;   // tokens per thread per round, their loads in flight together
+    for (int base = 0; base < T; base += TB * BUILD_THREADS) {
+        int sv[TB], pv[TB], nv[TB];
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            const int t = base + u * BUILD_THREADS + threadIdx.x;
+            sv[u] = t < T ? m.tok_seg[t] : 0;
+            pv[u] = t < T && t > 0 ? m.tok_seg[t - 1] : -1;
+            nv[u] = t + 1 < T ? m.tok_seg[t + 1] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            const int t = base + u * BUILD_THREADS + threadIdx.x, s = sv[u];
+            if (t >= T) continue;
+            if (s < 0 || s >= S) {
+                build_error(A.header, &flag, FK_E_SEG_RANGE);
+                continue;
+            }
+            if (t == 0 || pv[u] != s) {
+                atomicAdd(A.seg_nrun + s, 1);   // an integer count: order-independent
+                A.seg_start[s] = t;             // meaningful only when the run count is 1
+            }
+            if (t == T - 1 || nv[u] != s) A.seg_end[s] = t + 1;
+        }
+    }
+    if (block_failed(&flag)) return;
 
     // phase 1: lengths
     for (int s = threadIdx.x; s < S; s += blockDim.x) {
@@ -474,14 +480,6 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
     A.seg_tile0 = ws_at<int32_t>(ws, L.seg_tile0);
     A.seg_coff = ws_at<int32_t>(ws, L.seg_coff);
     const int S = meta->S, T = meta->T;
-    k_init<<<(S + 255) / 256 > 0 ? (S + 255) / 256 : 1, 256, 0, st>>>(A.header, A.seg_nrun, A.kid_cnt,
-                                                                   A.kid_fill, S);
-    if ((rc = launch_status())) return rc;
-    if (T > 0) {
-        k_tokens<<<(T + 255) / 256, 256, 0, st>>>(meta->tok_seg, T, S, A.header, A.seg_start, A.seg_end,
-                                                 A.seg_nrun);
-        if ((rc = launch_status())) return rc;
-    }
     k_build<<<1, BUILD_THREADS, 0, st>>>(A);
     if ((rc = launch_status())) return rc;
     {
