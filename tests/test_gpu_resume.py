@@ -148,3 +148,29 @@ def test_resume_batch_invariance(wl, r):
         idx = torch.tensor(idx, device="cuda")
         assert torch.equal(a, a_mix[idx]), ("attention", r, leaf)
         assert torch.equal(o, g_mix[idx]), ("gdn", r, leaf)
+
+
+def test_resume_two_streams_bitwise(wl):
+    """The bench's overlapped step -- the GDN call and the checkpoint save on a
+    second stream beside the K/V append and the attention -- gives the serial
+    step's bits for the whole round (outputs and the saved states), eagerly
+    and replayed from a graph."""
+    print("[resume] serial step vs the two-stream step", flush=True)
+    wl.step()
+    torch.cuda.synchronize()
+    ref = (wl.attn_out.clone(), wl.gdn_out.clone(), wl.ckpt_next.clone())
+    outs = (wl.attn_out, wl.gdn_out, wl.ckpt_next)
+    for o in outs:
+        o.zero_()
+    wl.step_overlapped()
+    torch.cuda.synchronize()
+    assert fk.fk_read_status(wl.ws) == 0
+    assert all(torch.equal(a, b) for a, b in zip(outs, ref))
+    graph = fk.StepGraph(wl.step_overlapped)
+    for rep in range(2):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(outs, ref)), rep
