@@ -87,6 +87,14 @@ struct BlockRegs {
     uint4 k[BN / FK_TILE_TOKENS], v[BN / FK_TILE_TOKENS];
 };
 
+// The dim row of the transposed value tile that thread pair q (threads 2q,
+// 2q+1, 16 bytes each) moves.  A 16-byte LDS write serves 8 lanes -- 4 pairs
+// -- per cycle over 32 banks; with rows 20 dwords apart, four consecutive rows
+// would put rows r and r+3 on the same banks, while rows of one parity,
+// 2 apart, fill all 32 banks: pairs 4g..4g+3 take rows of one parity.  Each
+// wave still moves 32 whole rows of the page (1 KB contiguous).
+__device__ __forceinline__ int v_row(int q) { return (q & ~7) | ((q & 3) << 1) | ((q >> 2) & 1); }
+
 __device__ __forceinline__ void load_block(BlockRegs &R, const uint16_t *__restrict__ kp,
                                            const uint16_t *__restrict__ vp, const int32_t *__restrict__ plist,
                                            int key0, int count, int g, int Hkv)
@@ -99,7 +107,7 @@ __device__ __forceinline__ void load_block(BlockRegs &R, const uint16_t *__restr
         if (kbase < count) {
             const size_t pb = ((size_t)plist[kbase / FK_TILE_TOKENS] * Hkv + g) * (FK_TILE_TOKENS * D);
             R.k[p] = *reinterpret_cast<const uint4 *>(kp + pb + tid * 8);   // slot tid/16, dims (tid%16)*8
-            R.v[p] = *reinterpret_cast<const uint4 *>(vp + pb + tid * 8);   // dim tid/2, slots (tid%2)*8
+            R.v[p] = *reinterpret_cast<const uint4 *>(vp + pb + v_row(tid / 2) * FK_TILE_TOKENS + (tid % 2) * 8);
         }
     }
 }
@@ -110,7 +118,7 @@ __device__ __forceinline__ void store_block(uint16_t *__restrict__ ks, uint16_t 
 #pragma unroll
     for (int p = 0; p < BN / FK_TILE_TOKENS; ++p) {
         *reinterpret_cast<uint4 *>(ks + (p * FK_TILE_TOKENS + tid / 16) * K_STRIDE + (tid % 16) * 8) = R.k[p];
-        *reinterpret_cast<uint4 *>(vs + (tid / 2) * V_STRIDE + p * FK_TILE_TOKENS + (tid % 2) * 8) = R.v[p];
+        *reinterpret_cast<uint4 *>(vs + v_row(tid / 2) * V_STRIDE + p * FK_TILE_TOKENS + (tid % 2) * 8) = R.v[p];
     }
 }
 
