@@ -5,15 +5,18 @@ A step is one pass over one round of synthetic decision requests: the
 tree-metadata build, the paged K/V append, ForkAttention over the round
 (GQA softmax attention, every branch seeing only its ancestry), and the
 forked Gated DeltaNet layer (trunk once, children from the fork-point state
-by index); for the resume workload also the checkpoint resume and save.
+by index); on the resume workload also the checkpoint resume and save.
 
-Default workload: the 16-request decision mixture (trunks ~U[512, 2048],
-4-8 branches of ~U[16, 48] tokens, bf16, attention 16q/2kv heads d128, GDN
-16 heads 128x128).  Prints ONE JSON line with the throughput in branch
-tokens/s, the dominant kernel's roofline and the fp64 CPU oracle timed on
-a bounded sample of the same workload.
+Default workload (the headline line): the expanding-history resume round --
+64 requests, each resumed from a checkpoint (fp32 GDN state + 16,384-token
+paged K/V), 1,024 new history tokens, then mixed trees of 32-token question
+branches (depth 1-3, fan-out 2-8); bf16, attention 32 q / 4 kv heads d 128,
+GDN 16 k / 32 v heads 128 x 128.  The same run also measures the 16-request
+mixture, the depth-3 agent fan-out and the 32k-token long context
+(``--also``), each reported under ``configs`` with its own rooflines and CPU
+oracle baseline.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 1]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 4] [--also 1,2,3]
 """
 from __future__ import annotations
 
@@ -34,14 +37,18 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
 def parse():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=1, help="workload index (0-4)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, help="headline workload index (1-4)")
+    ap.add_argument("--also", default="1,2,3",
+                    help="further workloads measured in the same run (comma list, '' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the rows beyond the step (conv, rules, readout, projection GEMM)")
     ap.add_argument("--cpu-requests", type=int, default=16,
-                    help="requests of the workload in the CPU oracle sample")
+                    help="requests of the mixture in its CPU oracle sample")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of the step captured as a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -50,8 +57,11 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_mixture_traffic.txt")
-ATTN_SRC = os.path.join(ROOT, "gated_deltanet_amd", "csrc", "attn_bf16.hip")
+CSRC = os.path.join(ROOT, "gated_deltanet_amd", "csrc")
+SLUG = {1: "mixture", 2: "fanout", 3: "long_context", 4: "resume"}
+# kernel family -> (profile name, source file whose hash the counter summary records)
+TRAFFIC_KERNELS = {"attention": ("attn_bf16", "attn_bf16.hip"), "gdn": ("gdn_bf16", "gdn_bf16.hip"),
+                   "kv_append": ("kv_append", "kv_append.hip")}
 
 
 def kernel_hash(path: str) -> str:
@@ -59,17 +69,24 @@ def kernel_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(config: int):
-    """HBM bytes per attention launch from the committed counter summary, or
-    None when it is missing, for another workload, or the kernel changed."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_file(kernel: str, config: int) -> str:
+    return os.path.join(ROOT, "profiles", f"{TRAFFIC_KERNELS[kernel][0]}_{SLUG.get(config, config)}_traffic.txt")
+
+
+def measured_traffic(kernel: str, config: int):
+    """HBM bytes per launch (per step for the GDN phase) of a kernel family from
+    the committed counter summary, or None when it is missing, for another
+    workload, or the kernel source changed since the counters were taken."""
+    path = traffic_file(kernel, config)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         parts = line.split()
         if len(parts) == 2 and not line.startswith("#"):
             kv[parts[0]] = parts[1]
-    if kv.get("kernel_sha256_16") != kernel_hash(ATTN_SRC) or kv.get("config") != str(config):
+    src = os.path.join(CSRC, TRAFFIC_KERNELS[kernel][1])
+    if kv.get("kernel_sha256_16") != kernel_hash(src) or kv.get("config") != str(config):
         return None
     return float(kv["bytes_per_launch"])
 
@@ -182,32 +199,31 @@ class Step:
 
 
 class Workload(Step):
-    """A config's round resident on the GPU, ready to step."""
+    """A config's round resident on the GPU, ready to step.  bf16 inputs are
+    drawn on the GPU (seeded, the workload recipe, torch's generator); the
+    fp32 tiny request uses the host generator."""
 
     def __init__(self, index: int, device="cuda"):
         import torch
 
         import gated_deltanet_amd as fk
         from workloads import make_config
+        from workloads.device import draw_stream
         from workloads.tensors import draw_inputs
 
         self.torch, self.fk = torch, fk
         cfg, tree = make_config(index)
         assert not any(s.cached for s in tree.segs), "the resume workload uses ResumeWorkload"
         self.cfg, self.tree = cfg, tree
-        inp = draw_inputs(tree, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
         sh = cfg.shapes
         self.sh = sh
         dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-
-        def dev(name):
-            x = torch.from_numpy(np.ascontiguousarray(inp.raw[name]))
-            if x.dtype == torch.int16 or inp.raw[name].dtype == np.uint16:
-                x = x.view(torch.bfloat16)
-            return x.to(device)
-
-        self.x = {n: dev(n) for n in inp.raw}
-        del inp
+        if cfg.dtype == "bf16":
+            self.x = draw_stream(tree.T, sh, cfg.seed * 7 + 2, cfg.mu_a, device)
+        else:
+            inp = draw_inputs(tree, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
+            self.x = {n: torch.from_numpy(np.ascontiguousarray(inp.raw[n])).to(device) for n in inp.raw}
+            del inp
         ts, par, fkk, cl = tree.arrays()
         sso = np.full(tree.S, -1, np.int32)
         self.plan = fk.plan_round(ts, par, fkk, cl, seg_state_out=sso, n_state_out=0, device=device)
@@ -368,15 +384,9 @@ class ResumeWorkload(Step):
         fk.gdn_checkpoint_save(self.state_out, 0, self.ckpt_next, count=self.R)
 
 
-def gdn_bytes(tree, sh, elem: int, resumed_save: bool = False) -> int:
-    """Algorithmic HBM bytes of one forked GDN pass: q and k (Hk heads) and v
-    read once, o written once, a and b read once (fp32); each fork-point
-    state written once and read once by every child entering from it; each
-    resumed root reads its state_in slot, and with ``resumed_save`` (the
-    resume workload's step) also writes its state_out slot, which the
-    checkpoint save then reads and copies out."""
-    per_tok = 2 * sh.Hk * sh.dk * elem + 2 * sh.Hv * sh.dv * elem + 2 * sh.Hv * 4
-    state = sh.Hv * sh.dv * sh.dk * 4
+def gdn_forks(tree):
+    """(distinct fork points between live segments, children entering from
+    them, roots resumed from a cached history)."""
     forks, children, resumed = set(), 0, 0
     for s in tree.segs:
         if s.cached or s.parent < 0:
@@ -386,8 +396,27 @@ def gdn_bytes(tree, sh, elem: int, resumed_save: bool = False) -> int:
         else:
             forks.add((s.parent, s.fork))
             children += 1
-    n_states = len(forks) + children + resumed + (3 * resumed if resumed_save else 0)
+    return len(forks), children, resumed
+
+
+def gdn_bytes(tree, sh, elem: int, resumed_save: bool = False) -> int:
+    """Algorithmic HBM bytes of one forked GDN pass: q and k (Hk heads) and v
+    read once, o written once, a and b read once (fp32); each fork-point
+    state written once and read once (the broadcast: children enter from it
+    by index); each resumed root reads its state_in slot, and with
+    ``resumed_save`` (the resume workload's step) also writes its state_out
+    slot, which the checkpoint save then reads and copies out."""
+    per_tok = 2 * sh.Hk * sh.dk * elem + 2 * sh.Hv * sh.dv * elem + 2 * sh.Hv * 4
+    state = sh.Hv * sh.dv * sh.dk * 4
+    n_forks, _, resumed = gdn_forks(tree)
+    n_states = 2 * n_forks + resumed + (3 * resumed if resumed_save else 0)
     return tree.T * per_tok + n_states * state
+
+
+def kv_bytes(tree, sh, elem: int) -> int:
+    """Algorithmic HBM bytes of the K/V append: the stream's keys and values
+    read once and written once into their pages."""
+    return 4 * tree.T * sh.Hkv * sh.d * elem
 
 
 def measure_conv(wl, steps: int, W: int = 4):
@@ -538,17 +567,16 @@ def host_cpu():
 
 
 def cpu_baseline(index: int, n_req: int):
-    """The fp64 oracle, as it stands, on the first ``n_req`` requests of the
-    same workload: every root-to-leaf path as its own isolated sequence
-    (attention and GDN, literal mode).  Returns branch tokens/s."""
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload
+    (branch tokens/s).  The mixture: its first ``n_req`` requests, every
+    root-to-leaf path as its own isolated sequence (attention and GDN,
+    literal mode).  The other workloads: seeded leaf paths, extrapolated."""
     import oracle
     from workloads import make_config
     from workloads.tensors import draw_inputs
 
-    if index == 4:
-        return cpu_baseline_resume(n_req)
-    if index in (2, 3):
-        return cpu_baseline_sampled(index, 1 if index == 3 else 4)
+    if index in (2, 3, 4):
+        return cpu_baseline_sampled(index, {2: 4, 3: 1, 4: 4}[index])
     cfg, tree = make_config(index, n_requests=n_req)
     inp = draw_inputs(tree, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
     ts, par, fkk, cl = tree.arrays()
@@ -561,17 +589,38 @@ def cpu_baseline(index: int, n_req: int):
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     bt = tree.branch_tokens()
     return {"value": bt / dt, "unit": "branch tokens/s", "cores": cores, "kind": "oracle", **host_cpu(),
+            "extrapolated": False,
             "sample": f"first {n_req} request(s) of the workload ({tree.T} stream tokens, {bt} branch "
                       f"tokens, {len(tree.leaves())} leaf paths), fp64 literal isolated-path "
                       f"attention + GDN, {dt:.1f} s"}
 
 
+def path_work(tree, leaf):
+    """(live rows L, cached history rows H) of a leaf's isolated path: the
+    literal oracle evaluates each live row r over its H + r + 1 keys
+    (L H + L (L + 1) / 2 attention pairs) and steps the recurrence over the L
+    live rows from the history's saved state."""
+    L, H, j = tree.segs[leaf].length, 0, leaf
+    while tree.segs[j].parent >= 0:
+        p = tree.segs[j].parent
+        if tree.segs[p].cached:
+            H += tree.segs[j].fork
+        else:
+            L += tree.segs[j].fork
+        j = p
+    return L, H
+
+
 def cpu_baseline_sampled(index: int, n_paths: int):
-    """The fp64 oracle on long-path workloads (a full literal run would take
-    hours): ``n_paths`` seeded leaf paths, each run alone in literal mode with
-    one attention q head and one GDN v-head timed, scaled to every head and
-    to every leaf path (attention by the sum of squared path lengths, GDN by
-    the sum of path lengths).  The figure is extrapolated and says so."""
+    """The fp64 oracle on the long-path workloads (a literal run of every leaf
+    path would take from an hour to days): ``n_paths`` seeded leaf paths, each
+    run alone in literal mode -- its whole isolated sequence, history keys
+    included, with one attention q head and one GDN v-head timed -- scaled to
+    every head and every leaf path (attention by the paths' visible pairs,
+    GDN by their live rows).  On the resume workload the sampled leaves come
+    from one seeded request, whose history state the oracle makes first,
+    untimed, as the GPU's checkpoint pass does.  The figure is extrapolated
+    and says so."""
     import oracle
     from workloads import make_config, subtree_path
     from workloads.tensors import draw_inputs
@@ -579,115 +628,82 @@ def cpu_baseline_sampled(index: int, n_paths: int):
     cfg, tree = make_config(index)
     sh = cfg.shapes
     leaves = tree.leaves()
-
-    def path_len(leaf):
-        pos0, j = 0, leaf
-        while tree.segs[j].parent >= 0:
-            pos0 += tree.segs[j].fork
-            j = tree.segs[j].parent
-        return pos0 + tree.segs[leaf].length
-
-    lens = np.array([path_len(x) for x in leaves], np.float64)
-    pick = np.random.default_rng(index).choice(len(leaves), size=min(n_paths, len(leaves)), replace=False)
+    rng = np.random.default_rng(index)
+    if index == 4:
+        req = int(rng.integers(tree.n_requests))
+        pool = [i for i, x in enumerate(leaves) if tree.segs[x].request == req]
+    else:
+        pool = list(range(len(leaves)))
+    pick = rng.choice(pool, size=min(n_paths, len(pool)), replace=False)
+    work = np.array([path_work(tree, x) for x in leaves], np.float64)
+    pairs = work[:, 0] * work[:, 1] + work[:, 0] * (work[:, 0] + 1) / 2
     a_sel = (np.arange(sh.Hq) == 0).astype(np.uint8)
     g_sel = (np.arange(sh.Hv) == 0).astype(np.uint8)
+    cache = {}
     t_attn = t_gdn = 0.0
     for li in pick:
         leaf = int(leaves[li])
         sub, _ = subtree_path(tree, leaf)
         sub.flatten()
-        inp = draw_inputs(sub, sh, cfg.seed, cfg.dtype, cfg.mu_a, request_streams=[tree.segs[leaf].request])
+        inp = draw_inputs(sub, sh, cfg.seed, cfg.dtype, cfg.mu_a, request_streams=[tree.segs[leaf].request],
+                          cache=cache)
         ts, par, fkk, cl = sub.arrays()
         args = {n: inp.f64(n) for n in inp.raw}
+        st_in, ssi = None, None
+        hist = [i for i, s in enumerate(sub.segs) if s.cached]
+        if hist:   # the history's final state, made untimed (the GPU's checkpoint pass)
+            h = sub.segs[hist[0]].length
+            z = np.zeros(1, np.int32)
+            _, st_in, _ = oracle.gdn(np.zeros(h, np.int32), z - 1, z, z, inp.f64("gq", True), inp.f64("gk", True),
+                                     inp.f64("gv", True), inp.f64("ga", True), inp.f64("gb", True),
+                                     seg_state_out=np.zeros(1, np.int32), n_state_out=1, mode=1, head_sel=g_sel)
+            ssi = np.full(sub.S, -1, np.int32)
+            ssi[hist[0]] = 0
         t0 = time.perf_counter()
-        oracle.attention(ts, par, fkk, cl, inp.hist_off, args["aq"], args["ak"], args["av"], None, None,
-                         sh.d ** -0.5, mode=0, head_sel=a_sel)
+        oracle.attention(ts, par, fkk, cl, inp.hist_off, args["aq"], args["ak"], args["av"], inp.f64("ak", True),
+                         inp.f64("av", True), sh.d ** -0.5, mode=0, head_sel=a_sel)
         t1 = time.perf_counter()
-        oracle.gdn(ts, par, fkk, cl, args["gq"], args["gk"], args["gv"], args["ga"], args["gb"], mode=0,
-                   head_sel=g_sel)
+        oracle.gdn(ts, par, fkk, cl, args["gq"], args["gk"], args["gv"], args["ga"], args["gb"], state_in=st_in,
+                   seg_state_in=ssi, mode=0, head_sel=g_sel)
         t2 = time.perf_counter()
         t_attn += (t1 - t0) * sh.Hq
         t_gdn += (t2 - t1) * sh.Hv
-    sl = lens[pick]
-    total = t_attn * (lens ** 2).sum() / (sl ** 2).sum() + t_gdn * lens.sum() / sl.sum()
+    total = t_attn * pairs.sum() / pairs[pick].sum() + t_gdn * work[:, 0].sum() / work[pick, 0].sum()
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     bt = tree.branch_tokens()
+    where = f" of request {req}" if index == 4 else ""
     return {"value": bt / total, "unit": "branch tokens/s", "cores": cores, "kind": "oracle", **host_cpu(),
             "extrapolated": True,
-            "sample": f"{len(pick)} of {len(leaves)} leaf paths (seeded), each alone in fp64 literal mode, "
+            "sample": f"{len(pick)} of {len(leaves)} leaf paths (seeded{where}), each alone in fp64 literal mode, "
                       f"one attention q head and one GDN v-head timed "
                       f"({(t_attn / sh.Hq + t_gdn / sh.Hv):.1f} s), scaled to all {sh.Hq} q / {sh.Hv} v heads "
-                      f"and to every leaf path (sum of squared path lengths for attention, of lengths for "
-                      f"GDN): {total:.0f} s for the whole workload"}
+                      f"and to every leaf path (by visible pairs for attention, by live rows for GDN): "
+                      f"{total:.0f} s for the whole workload"}
 
 
-def cpu_baseline_resume(n_req: int):
-    """The oracle on the first ``n_req`` requests of the resume workload.  The
-    history states are made first (untimed, like the GPU's checkpoint pass);
-    the timed part is the round: tree-mode attention over history + live
-    tokens and GDN resumed from the saved states (literal per-path mode would
-    re-read each 16,384-token history once per leaf), on a quarter of the
-    heads, scaled to the whole request."""
-    import oracle
-    from workloads import make_config
-    from workloads.tensors import draw_inputs
-
-    cfg, tree = make_config(4, n_requests=n_req)
-    inp = draw_inputs(tree, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
-    ts, par, fkk, cl = tree.arrays()
-    hist = [i for i, sg in enumerate(tree.segs) if sg.cached]
-    ssi = np.full(tree.S, -1, np.int32)
-    for r, sid in enumerate(hist):
-        ssi[sid] = r
-    n_h = [tree.segs[i].length for i in hist]
-    h_ts = np.repeat(np.arange(len(hist), dtype=np.int32), n_h)
-    z = np.zeros(len(hist), np.int32)
-    _, st, _ = oracle.gdn(h_ts, z - 1, z, z, inp.f64("gq", True), inp.f64("gk", True), inp.f64("gv", True),
-                          inp.f64("ga", True), inp.f64("gb", True), seg_state_out=np.arange(len(hist)),
-                          n_state_out=len(hist), mode=1)
-    args = {n: inp.f64(n) for n in inp.raw}
-    sh = cfg.shapes
-    # a quarter of the heads: the first kv group's q heads, the first quarter of the v heads
-    frac = 4
-    a_sel = (np.arange(sh.Hq) < sh.Hq // frac).astype(np.uint8)
-    g_sel = (np.arange(sh.Hv) < sh.Hv // frac).astype(np.uint8)
-    t0 = time.perf_counter()
-    oracle.attention(ts, par, fkk, cl, inp.hist_off, args["aq"], args["ak"], args["av"], inp.f64("ak", True),
-                     inp.f64("av", True), sh.d ** -0.5, mode=1, head_sel=a_sel)
-    oracle.gdn(ts, par, fkk, cl, args["gq"], args["gk"], args["gv"], args["ga"], args["gb"], state_in=st,
-               seg_state_in=ssi, mode=1, head_sel=g_sel)
-    dt = (time.perf_counter() - t0) * frac
-    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    bt = tree.branch_tokens()
-    return {"value": bt / dt, "unit": "branch tokens/s", "cores": cores, "kind": "oracle", **host_cpu(),
-            "sample": f"first {n_req} request(s) of the workload ({tree.T} stream tokens after "
-                      f"{sum(n_h)} history tokens, {bt} branch tokens), 1/{frac} of the attention and "
-                      f"GDN heads timed and scaled by {frac}: fp64 tree-mode attention + GDN resumed "
-                      f"from oracle-made history states, {dt / frac:.1f} s measured"}
-
-
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-    import torch
-
-    if args.calibrate_copy:
-        calibrate_copy()
-    if args.config == 4:
+def make_workload(index: int):
+    if index == 4:
         wl = ResumeWorkload()
         wl.checkpoint()
-    else:
-        wl = Workload(args.config)
+        return wl
+    return Workload(index)
+
+
+def measure(index: int, args, next_rows: bool):
+    """Step one workload: eager steps with HIP events at the phase boundaries
+    (the per-phase times and the kernels' durations for the rooflines), then
+    the step recorded as a HIP graph and replayed (the headline timing).
+    Returns the workload's fields of the JSON line."""
+    import torch
+
+    wl = make_workload(index)
     tree, sh = wl.tree, wl.sh
     for _ in range(args.warmup):
         wl.step()
     torch.cuda.synchronize()
     assert wl.fk.fk_read_status(wl.ws) == 0, "tree build reported an error"
     # eager pass: per-phase times with HIP events on the launch stream (these
-    # give the phases and the attention kernel's duration for the roofline)
+    # give the phases and the kernels' durations for the rooflines)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -698,7 +714,7 @@ def main():
     phase = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # ms
     ms_eager = wall * 1e3 / args.steps
     ms_step, mode = ms_eager, "eager launches"
-    dist = None
+    dist, forms, n_warm = None, {}, None
     if not args.eager:
         # the same step recorded once as a HIP graph and replayed: the
         # headline timing (no launch gaps between the step's kernels).  Both
@@ -729,7 +745,7 @@ def main():
             torch.cuda.synchronize()
             return np.array([e[0].elapsed_time(e[1]) for e in ev])
 
-        forms, n_warm = {}, 0
+        n_warm = 0
         for name, fn in (("serial", wl.step), ("GDN phase on a second stream", wl.step_overlapped)):
             g = wl.fk.StepGraph(fn, warmup=1)
             n_warm += warm(g)
@@ -761,62 +777,98 @@ def main():
         dist = {"warm_p10": float(np.percentile(warm_ms, 10)), "warm_p50": float(np.percentile(warm_ms, 50)),
                 "warm_p90": float(np.percentile(warm_ms, 90)), "cold_p50": float(np.median(cold)),
                 "cold_flush_bytes": 512 << 20}
+        forms = {k: v[0] for k, v in forms.items()}
+        del graph, g
+    resume = index == 4
+    elem = 2 if wl.cfg.dtype == "bf16" else 4
     attn_ms = float(phase[:, 2].mean())
     nvis = visible_pairs(tree)
     flops = 4.0 * sh.d * sh.Hq * nvis
     achieved = flops / (attn_ms * 1e-3) / 1e12
     bt = tree.branch_tokens()
-    line = {
-        "metric": METRIC,
+    kv_ms = float(phase[:, 1].mean())
+    kvb = kv_bytes(tree, sh, elem)
+    out = {
         "value": bt / (ms_step * 1e-3),
         "unit": "branch tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": wl.cfg.dtype,
-        "data": "synthetic",
-        "config": {"workload": wl.cfg.name, "index": args.config, "requests": tree.n_requests,
+        "config": {"workload": wl.cfg.name, "index": index, "requests": tree.n_requests,
                    "stream_tokens": tree.T, "branch_tokens": bt, "segments": tree.S,
-                   "attn_heads": [sh.Hq, sh.Hkv, sh.d], "gdn_heads": [sh.Hk, sh.Hv, sh.dk, sh.dv]},
+                   "leaves": len(tree.leaves()), "attn_heads": [sh.Hq, sh.Hkv, sh.d],
+                   "gdn_heads": [sh.Hk, sh.Hv, sh.dk, sh.dv]},
         "execution": mode,
-        "graph_warmup_replays": None if args.eager else n_warm,
-        "graph_forms_ms": None if args.eager else {k: v[0] for k, v in forms.items()},
+        "graph_warmup_replays": n_warm,
+        "graph_forms_ms": forms or None,
         "step_ms_distribution": dist,
         "stream_tokens_per_s": tree.T / (ms_step * 1e-3),
         "path_equivalent_tokens_per_s": path_tokens(tree) / (ms_step * 1e-3),
         "ms_per_step_eager": ms_eager,
-        "phases_ms": {("resume+tree_build" if args.config == 4 else "tree_build"): float(phase[:, 0].mean()),
-                      "kv_append": float(phase[:, 1].mean()),
-                      "fork_attention": attn_ms,
-                      ("gdn+checkpoint_save" if args.config == 4 else "gdn"): float(phase[:, 3].mean())},
+        "phases_ms": {("resume+tree_build" if resume else "tree_build"): float(phase[:, 0].mean()),
+                      "kv_append": kv_ms, "fork_attention": attn_ms,
+                      ("gdn+checkpoint_save" if resume else "gdn"): float(phase[:, 3].mean())},
         "roofline": {"kernel": "fork attention (bf16 MFMA)", "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic(args.config), "algorithmic_flops": flops,
-                     "visible_pairs_per_head": nvis},
+                     "traffic": measured_traffic("attention", index), "ms": attn_ms,
+                     "algorithmic_flops": flops, "visible_pairs_per_head": nvis},
+        "kv_roofline": {"kernel": "paged K/V append (bf16)", "bound": "hbm", "ms": kv_ms,
+                        "achieved": kvb / (kv_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": kvb / (kv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "traffic": measured_traffic("kv_append", index), "algorithmic_bytes": kvb},
     }
     if getattr(wl, "gdn_ok", True):
         gdn_ms = float(phase[:, 3].mean())
-        nbytes = gdn_bytes(tree, sh, 2 if wl.cfg.dtype == "bf16" else 4, resumed_save=args.config == 4)
+        nbytes = gdn_bytes(tree, sh, elem, resumed_save=resume)
+        n_forks, children, _ = gdn_forks(tree)
         gbs = nbytes / (gdn_ms * 1e-3) / 1e9
-        line["gdn_roofline"] = {"kernels": "GDN prep + one chunk walk per tree level (bf16 MFMA)"
-                                           + (" + checkpoint save" if args.config == 4 else ""),
-                                "bound": "hbm", "ms": gdn_ms, "achieved": gbs, "peak": PEAK_HBM_GBS,
-                                "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": nbytes}
-    line["next_rows"] = {"conv": measure_conv(wl, args.steps),
-                         "window_attention": measure_rule(wl, args.steps, 1, 1024),
-                         "two_way_attention": measure_rule(wl, args.steps, 2),
-                         "readout": measure_readout(wl, args.steps)}
-    if not getattr(wl, "gdn_ok", True):
-        line["incomplete"] = "gdn_fork_forward unsupported for this dtype in this build: step lacks GDN"
-        line["phases_ms"]["gdn"] = None
+        out["gdn_roofline"] = {"kernels": "GDN prep + one chunk walk per tree level (bf16 MFMA)"
+                                          + (" + checkpoint save" if resume else ""),
+                               "bound": "hbm", "ms": gdn_ms, "achieved": gbs, "peak": PEAK_HBM_GBS,
+                               "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": nbytes,
+                               "traffic": measured_traffic("gdn", index), "fork_points": n_forks,
+                               "bytes_if_each_child_copied_its_state":
+                                   nbytes + (children - n_forks) * sh.Hv * sh.dv * sh.dk * 4}
+    else:
+        out["incomplete"] = "gdn_fork_forward unsupported for this dtype in this build: step lacks GDN"
+    if next_rows:
+        out["next_rows"] = {"conv": measure_conv(wl, args.steps),
+                            "window_attention": measure_rule(wl, args.steps, 1, 1024),
+                            "two_way_attention": measure_rule(wl, args.steps, 2),
+                            "readout": measure_readout(wl, args.steps)}
+    del wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+    also = [int(x) for x in args.also.split(",") if x.strip() and int(x) != args.config]
+    print(f"[bench] workload {args.config}", file=sys.stderr, flush=True)
+    head = measure(args.config, args, next_rows=not args.no_next_rows)
+    line = {"metric": METRIC, "value": head.pop("value"), "unit": head.pop("unit"), "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": head.pop("ms_per_step"),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": head.pop("dtype"),
+            "data": "synthetic", "config": head.pop("config")}
+    line.update(head)
+    others = {}
+    for i in also:
+        print(f"[bench] workload {i}", file=sys.stderr, flush=True)
+        others[str(i)] = measure(i, args, next_rows=False)
+    if others:
+        line["configs"] = others
     line["measured_peaks"] = measured_peaks()
     if not args.no_cpu_baseline:
-        n_cpu = args.cpu_requests if args.config != 4 else min(args.cpu_requests, 1)
-        line["cpu_baseline"] = cpu_baseline(args.config, n_cpu)
+        print("[bench] cpu baselines", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_requests)
+        for i, o in others.items():
+            o["cpu_baseline"] = cpu_baseline(int(i), args.cpu_requests)
     print(json.dumps(line))
 
 

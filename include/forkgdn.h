@@ -169,7 +169,11 @@ int fk_token_positions(const fk_tree_meta *meta, const void *ws, int32_t *pos, f
  * page_size, d]; v_pool: [n_pages, Hkv, d, page_size] (values are stored
  * transposed inside a page so that the attention kernel reads them with keys
  * contiguous).  Cached segments' pages are left untouched.  Slots past a
- * segment's last token in its last page are left untouched (readers mask them).
+ * segment's last token in its last page are zero-filled: readers give them a
+ * zero weight, which keeps an output finite only if the slot is finite.
+ * Pages of cached segments that the caller wrote itself must therefore hold
+ * finite values (zero) past the history's last token; pages written by
+ * kv_append always do.
  */
 int kv_append(const fk_tree_meta *meta, const void *k, const void *v, int dtype, int Hkv, int d,
               void *k_pool, void *v_pool, const void *ws, fk_stream_t stream);

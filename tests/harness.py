@@ -8,12 +8,15 @@ the main round then names those pages.  Their recurrent states come from
 """
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 import torch
 
 import gated_deltanet_amd as fk
 import oracle
-from workloads.tensors import ACT
+from workloads import make_config
+from workloads.tensors import ACT, draw_inputs
 
 
 def dev_tensor(inp, name, hist=False, device="cuda"):
@@ -22,6 +25,14 @@ def dev_tensor(inp, name, hist=False, device="cuda"):
     if x.dtype == np.uint16:
         t = t.view(torch.bfloat16) if hasattr(t, "view") else t
     return t.to(device)
+
+
+@functools.lru_cache(maxsize=None)
+def config_inputs(i: int):
+    """(config, host-drawn inputs) of workload i, drawn once per test session
+    (the long-context round takes about a minute to draw)."""
+    cfg, t = make_config(i)
+    return cfg, draw_inputs(t, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
@@ -44,7 +55,8 @@ def state_slots(tree):
 class GpuRound:
     """One round on the GPU: plan, history pages, build, attention, GDN."""
 
-    def __init__(self, inp, state_in_np=None, n_pool_extra=0, device="cuda", want_state_out=True):
+    def __init__(self, inp, state_in_np=None, n_pool_extra=0, device="cuda", want_state_out=True,
+                 pool_fill=0.0):
         self.inp = inp
         tree = inp.tree
         sh = inp.shapes
@@ -67,8 +79,8 @@ class GpuRound:
             nxt += n
         live_pages = sum(-(-tree.segs[i].length // 16) for i in range(tree.S) if not tree.segs[i].cached)
         self.n_pages = max(nxt + live_pages + n_pool_extra, 1)
-        self.k_pool = torch.zeros((self.n_pages, sh.Hkv, 16, sh.d), dtype=dt, device=device)
-        self.v_pool = torch.zeros((self.n_pages, sh.Hkv, sh.d, 16), dtype=dt, device=device)
+        self.k_pool = torch.full((self.n_pages, sh.Hkv, 16, sh.d), pool_fill, dtype=dt, device=device)
+        self.v_pool = torch.full((self.n_pages, sh.Hkv, sh.d, 16), pool_fill, dtype=dt, device=device)
         if cached:
             # history round: each cached segment as a live root of its own
             hts = np.concatenate([np.full(tree.segs[s].length, j, np.int32) for j, s in enumerate(cached)])
@@ -111,6 +123,25 @@ class GpuRound:
         return fk.gdn_fork_forward(self.meta, self.x["gq"], self.x["gk"], self.x["gv"], self.x["ga"],
                                    self.x["gb"], self.ws, state_in=self.state_in,
                                    state_out=self.state_out if self.n_out else None)
+
+
+def stratified_rows(tree, trunk_every=64):
+    """First and last row of every 16-token tile of every non-root segment;
+    first and last row of every ``trunk_every``-th tile of a root segment (and
+    of its last tile)."""
+    sel = np.zeros(tree.T, bool)
+    starts = {}
+    for x, s in enumerate(tree.tok_seg):
+        starts.setdefault(int(s), x)
+    for s, x0 in starts.items():
+        seg = tree.segs[s]
+        root = seg.parent < 0 or tree.segs[seg.parent].cached
+        n_tiles = -(-seg.length // 16)
+        tiles = set(range(0, n_tiles, trunk_every)) | {n_tiles - 1} if root else range(n_tiles)
+        for j in tiles:
+            sel[x0 + 16 * j] = True
+            sel[x0 + min(16 * j + 15, seg.length - 1)] = True
+    return sel
 
 
 def oracle_attention(inp, mode=1, tok_sel=None, scale=None, rule=0, window=0, head_sel=None):

@@ -38,9 +38,11 @@ def test_gdn_bytes_by_hand():
     state = 4 * 16 * 8 * 4
     # two distinct fork points, each written once and read by its one child
     assert bench.gdn_bytes(t, sh, 2) == 15 * per_tok + 4 * state
-    # siblings at one fork point share its single write
+    # siblings at one fork point share its single write and its single read
+    # (the broadcast: both enter from the same state by index)
     t2 = build_tree([[(-1, 0, 10), (0, None, 3), (0, None, 2)]]).flatten()
-    assert bench.gdn_bytes(t2, sh, 2) == 15 * per_tok + 3 * state
+    assert bench.gdn_bytes(t2, sh, 2) == 15 * per_tok + 2 * state
+    assert bench.gdn_forks(t2) == (1, 2, 0)
     # a root resumed from a cached history reads its state slot; the resume
     # step also writes it back and the checkpoint save copies it out
     t3 = build_tree([[(-1, 0, 7, True), (0, None, 5)]]).flatten()
@@ -70,3 +72,18 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_kv_bytes_by_hand():
+    # keys and values of every stream token, read once and written once
+    t = build_tree(TREE).flatten()
+    sh = SimpleNamespace(Hkv=2, d=8)
+    assert bench.kv_bytes(t, sh, 2) == 4 * 15 * 2 * 8 * 2
+
+
+def test_path_work_by_hand():
+    # live rows and cached history rows on each leaf's isolated path
+    t = build_tree(TREE).flatten()
+    assert bench.path_work(t, 1) == (13, 0) and bench.path_work(t, 2) == (6, 0)
+    t3 = build_tree([[(-1, 0, 7, True), (0, None, 5), (1, 2, 4)]]).flatten()
+    assert bench.path_work(t3, 2) == (6, 7)

@@ -1,13 +1,14 @@
 """bf16 ForkAttention (MFMA kernel) against the fp64 oracle: max-abs 2e-2 and
 mean-abs 2e-3 (bf16 inputs, fp32 accumulation, bf16 output), plus batch
-invariance -- a branch's bits are the same alone and inside any round."""
+invariance -- a branch's bits are the same alone and inside any round.  The
+workloads at full size are in test_gpu_configs.py and test_gpu_resume.py."""
 import numpy as np
 import pytest
 import torch
 
 import gated_deltanet_amd as fk
 from tests.harness import GpuRound, oracle_attention, to_f64
-from workloads import make_config, random_tree, subtree_path
+from workloads import random_tree, subtree_path
 from workloads.tensors import Shapes, draw_inputs
 
 pytestmark = pytest.mark.gpu
@@ -43,34 +44,6 @@ def test_attention_bf16_random_trees():
         assert r.status() == 0
         mx, mean = _check(o, oracle_attention(inp))
         assert mx <= MAX_ABS and mean <= MEAN_ABS, (seed, mx, mean)
-
-
-def _sample_rows(tree, rng, per_seg=3):
-    """Each live segment's first, last and a random row, as a token mask."""
-    sel = np.zeros(tree.T, bool)
-    starts = {}
-    for t, s in enumerate(tree.tok_seg):
-        starts.setdefault(int(s), t)
-    for s, st in starts.items():
-        L = tree.segs[s].length
-        for i in {0, L - 1, int(rng.integers(L))}:
-            sel[st + i] = True
-    return sel
-
-
-@pytest.mark.parametrize("which", [1, 2, 3])
-def test_attention_bf16_configs_sampled(which):
-    cfg, t = make_config(which)
-    inp = draw_inputs(t, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
-    print(f"[attn bf16 config {which}] T={t.T}", flush=True)
-    r = GpuRound(inp).build()
-    o = to_f64(r.attention())
-    assert r.status() == 0
-    sel = _sample_rows(t, np.random.default_rng(which))
-    ref = oracle_attention(inp, tok_sel=sel.astype(np.uint8))
-    mx, mean = _check(o, ref, sel)
-    print(f"  max-abs {mx:.3e} mean-abs {mean:.3e}", flush=True)
-    assert mx <= MAX_ABS and mean <= MEAN_ABS
 
 
 def test_attention_bf16_batch_invariance():

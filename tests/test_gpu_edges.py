@@ -98,3 +98,21 @@ def test_empty_round():
     assert r.attention().numel() == 0
     assert r.gdn().numel() == 0
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_pool_of_nan_before_append(dtype):
+    """A pool allocated without clearing (here: every slot NaN) gives the same
+    outputs as a zeroed one: kv_append zero-fills the slots past each
+    segment's last token -- history pages included -- so the masked slots the
+    attention reads in a partial last page are finite."""
+    sh, name = (SH_BF16, "bf16") if dtype == "bf16" else (SH_F32, "f32")
+    nodes = dict(TREES)["cached_history"]
+    inp = _inputs(nodes, sh, name, 99)
+    print(f"[edges nan pool {dtype}] T={inp.tree.T}", flush=True)
+    ref = GpuRound(inp).build().attention()
+    r = GpuRound(inp, pool_fill=float("nan")).build()
+    o = r.attention()
+    assert r.status() == 0
+    assert torch.isfinite(o.float()).all()
+    assert torch.equal(o, ref)

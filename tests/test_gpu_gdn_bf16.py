@@ -2,14 +2,15 @@
 oracle -- max-abs 2e-2, mean-abs 2e-3 on outputs and final states -- plus
 the invariants that only the GPU can show bitwise: batch invariance, the
 fork-point state equals the trunk's own final state, and checkpoint resume
-equals the full pass."""
+equals the full pass.  The workloads at full size are in test_gpu_configs.py
+and test_gpu_resume.py."""
 import numpy as np
 import pytest
 import torch
 
 import gated_deltanet_amd as fk
 from tests.harness import GpuRound, oracle_gdn, state_slots, to_f64
-from workloads import build_tree, make_config, random_tree, subtree_path
+from workloads import build_tree, random_tree, subtree_path
 from workloads.tensors import Shapes, draw_inputs
 
 pytestmark = pytest.mark.gpu
@@ -50,26 +51,6 @@ def test_gdn_bf16_random_trees():
         print(f"  out {mx:.2e}/{mean:.2e} state {smx:.2e}/{smean:.2e}", flush=True)
         assert mx <= MAX_ABS and mean <= MEAN_ABS, (seed, mx, mean)
         assert smx <= MAX_ABS and smean <= MEAN_ABS, (seed, smx, smean)
-
-
-@pytest.mark.parametrize("which,heads", [(1, 4), (2, 3), (3, 2)])
-def test_gdn_bf16_configs(which, heads):
-    """Full-size workloads, every token, on a subset of v-heads."""
-    cfg, t = make_config(which)
-    inp = draw_inputs(t, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
-    print(f"[gdn bf16 config {which}] T={t.T}", flush=True)
-    r = GpuRound(inp).build()
-    o = to_f64(r.gdn())
-    assert r.status() == 0
-    sel = np.zeros(cfg.shapes.Hv, np.uint8)
-    hs = np.linspace(0, cfg.shapes.Hv - 1, heads).astype(int)
-    sel[hs] = 1
-    ref, st_ref = oracle_gdn(inp, head_sel=sel)
-    mx, mean = _err(o[:, hs], ref[:, hs])
-    smx, smean = _err(to_f64(r.state_out)[: len(st_ref)][:, hs], st_ref[:, hs])
-    print(f"  out {mx:.2e}/{mean:.2e} state {smx:.2e}/{smean:.2e}", flush=True)
-    assert mx <= MAX_ABS and mean <= MEAN_ABS
-    assert smx <= MAX_ABS and smean <= MEAN_ABS
 
 
 def _local(tree):

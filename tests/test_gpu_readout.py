@@ -9,8 +9,8 @@ import torch
 
 import gated_deltanet_amd as fk
 from gated_deltanet_amd._lib import FK_RULE_CAUSAL, FK_RULE_TWO_WAY, FK_RULE_WINDOW
-from tests.harness import GpuRound, oracle_attention, to_f64
-from workloads import make_config, random_tree
+from tests.harness import GpuRound, config_inputs, oracle_attention, to_f64
+from workloads import random_tree
 from workloads.tensors import Shapes, draw_inputs
 
 pytestmark = pytest.mark.gpu
@@ -77,8 +77,8 @@ def test_readout_config3_leaves():
     """The 32k-trunk workload: the last token of each of the 64 questions,
     bit-identical to the full launch, and within the bf16 bar of the oracle
     on a quarter of the heads."""
-    cfg, t = make_config(3)
-    inp = draw_inputs(t, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
+    cfg, inp = config_inputs(3)
+    t = inp.tree
     r = GpuRound(inp).build()
     full = to_f64(r.attention())
     rows = _row_buffer(t, np.random.default_rng(3), extra=0)

@@ -2,18 +2,20 @@
 history checkpointed by a GPU pass, 1,024 new tokens, then mixed trees of
 32-token branches) at full size, in the launch configuration the bench
 times.  Two requests carry host-drawn values so the fp64 oracle can check
-them: the history checkpoint, the round's attention rows (sampled) and GDN
-outputs (a head subset), and the saved state of the new root -- the oracle
-runs each history from the zero state, so the checkpoint/resume path is
-checked against a full pass.  Leaves of those requests, run alone, must give
-the mixture's bits (batch invariance, Flide section 3.5)."""
+them: the history checkpoint, the round's attention on stratified rows (the
+first and last row of every 16-token tile of every question, and of every
+8th tile of the new root; every head), the GDN outputs of four v-heads over
+every token, and the saved state of the new root -- the oracle runs each
+history from the zero state, so the checkpoint/resume path is checked against
+a full pass.  Every leaf of those requests, run alone, must give the
+mixture's bits (batch invariance, Flide section 3.5)."""
 import numpy as np
 import pytest
 import torch
 
 import gated_deltanet_amd as fk
 import oracle
-from tests.harness import GpuRound, state_slots, to_f64
+from tests.harness import GpuRound, state_slots, stratified_rows, to_f64
 from workloads import build_tree, subtree_path
 from workloads.configs import CONFIGS, config_requests
 from workloads.tensors import draw_inputs
@@ -84,11 +86,10 @@ def test_resume_matches_oracle(wl, r):
     mx, mean = _err(ck, st_h[0][g])
     print(f"  checkpoint {mx:.2e}/{mean:.2e}", flush=True)
     assert mx <= MAX_ABS and mean <= MEAN_ABS
-    # attention on sampled rows (every head), history + round keys
-    rng = np.random.default_rng(r)
-    sel = np.zeros(t.T, np.uint8)
-    sel[rng.choice(t.T, 160, replace=False)] = 1
-    sel[[0, t.T - 1]] = 1
+    # attention on stratified rows (every head), history + round keys: the
+    # first and last row of every tile of every question and of every 8th
+    # tile of the new root
+    sel = stratified_rows(t, trunk_every=8).astype(np.uint8)
     ts, par, fk_, cl = t.arrays()
     ref, _ = oracle.attention(ts, par, fk_, cl, inp.hist_off, inp.f64("aq"), inp.f64("ak"), inp.f64("av"),
                               inp.f64("ak", True), inp.f64("av", True), SH.d ** -0.5, mode=1, tok_sel=sel)
@@ -134,12 +135,14 @@ def test_resume_batch_invariance(wl, r):
             acc += 1
     a_mix, g_mix = wl.attn_out, wl.gdn_out
     leaves = t.leaves()
-    depth = [t.depth_of(i) for i in leaves]
-    for leaf in (leaves[int(np.argmax(depth))], leaves[0]):
+    cache = {}
+    print(f"[resume alone r={r}] {len(leaves)} leaves", flush=True)
+    for n, leaf in enumerate(leaves):
         sub, chain = subtree_path(t, leaf)
         sub.flatten()
-        print(f"[resume alone r={r}] leaf {leaf} chain {chain}", flush=True)
-        ra = GpuRound(draw_inputs(sub, SH, CFG.seed, "bf16", CFG.mu_a, request_streams=[r]),
+        if n % 10 == 0:
+            print(f"  leaf {n + 1}/{len(leaves)}: {leaf} chain {chain}", flush=True)
+        ra = GpuRound(draw_inputs(sub, SH, CFG.seed, "bf16", CFG.mu_a, request_streams=[r], cache=cache),
                       state_in_np=ck).build()
         a = ra.attention(scale=SH.d ** -0.5)
         o = ra.gdn()

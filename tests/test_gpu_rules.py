@@ -9,8 +9,8 @@ import pytest
 
 import gated_deltanet_amd as fk
 from gated_deltanet_amd._lib import FK_RULE_CAUSAL, FK_RULE_TWO_WAY, FK_RULE_WINDOW
-from tests.harness import GpuRound, oracle_attention, to_f64
-from workloads import make_config, random_tree, subtree_path
+from tests.harness import GpuRound, config_inputs, oracle_attention, to_f64
+from workloads import random_tree, subtree_path
 from workloads.tensors import Shapes, draw_inputs
 
 pytestmark = pytest.mark.gpu
@@ -98,8 +98,8 @@ def test_rules_configs_sampled(which, rule, W):
     """Full-size workloads in the bench's launch configuration, on sampled
     rows (each segment's first, last and one random row) and a quarter of the
     heads."""
-    cfg, t = make_config(which)
-    inp = draw_inputs(t, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
+    cfg, inp = config_inputs(which)
+    t = inp.tree
     print(f"[rules config {which}] rule {rule} W={W} T={t.T}", flush=True)
     r = GpuRound(inp).build()
     o = to_f64(r.attention(rule=rule, window=W))

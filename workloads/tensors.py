@@ -122,11 +122,15 @@ class Inputs:
 
 
 def draw_inputs(tree: Tree, shapes: Shapes, seed: int, dtype: str = "bf16",
-                mu_a: float = 3.0, request_streams: Optional[List[int]] = None) -> Inputs:
+                mu_a: float = 3.0, request_streams: Optional[List[int]] = None,
+                cache: Optional[dict] = None) -> Inputs:
     """Draw every segment's tensors and lay them out in stream order.
 
     ``request_streams[r]`` names the seed stream that request ``r`` of this
     tree uses (for a branch run alone: its request's index in the full round).
+    ``cache`` (optional dict) keeps each segment's draw for later calls with
+    the same seed, shapes and dtype (several paths of one request share their
+    ancestors' values).
     """
     assert tree.tok_seg is not None, "flatten() the tree first"
     assert dtype in ("bf16", "f32")
@@ -134,7 +138,13 @@ def draw_inputs(tree: Tree, shapes: Shapes, seed: int, dtype: str = "bf16",
     vals = []
     for s in tree.segs:
         r = request_streams[s.request] if request_streams is not None else s.request
+        key = (seed, shapes, dtype, mu_a, r, s.key, s.length)
+        if cache is not None and key in cache:
+            vals.append(cache[key])
+            continue
         vals.append(draw_segment(seeds, r, s.key, s.length, shapes, mu_a, dtype))
+        if cache is not None:
+            cache[key] = vals[-1]
     raw, hist = {}, {}
     cached_ids = [i for i, s in enumerate(tree.segs) if s.cached]
     hist_off = np.zeros(tree.S + 1, np.int64)
