@@ -60,6 +60,7 @@ def lib(path: Optional[str] = None) -> ctypes.CDLL:
         L.or_conv.argtypes = [ctypes.c_int, ctypes.c_int, i32p, i32p, i32p, i32p, i64p,
                               ctypes.c_int, ctypes.c_int, f64p, f64p, f64p, i32p, ctypes.c_int,
                               f64p, f64p]
+        L.or_proj.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, f64p, i32p, f64p, f64p]
         _lib_cache[path] = L
     return _lib_cache[path]
 
@@ -200,3 +201,21 @@ def conv(tok_seg, seg_parent, seg_fork, seg_cached_len, hist_off, x, hx, w, seg_
     if rc:
         raise OracleError(rc)
     return y[:T], win[:n_state_out, : W - 1]
+
+
+def proj(x, w, rows=None, y=None, libpath=None):
+    """Projection y[m, n] = sum_k x[r(m), k] w[n, k] (fp64), r(m) = rows[m] or m;
+    an entry rows[m] < 0 leaves row m of ``y`` as it was (NaN when ``y`` is
+    not given).  x [Mx, K], w [N, K]; returns y [M, N]."""
+    x, w = _f64(x), _f64(w)
+    Mx, K = x.shape
+    N = w.shape[0]
+    assert w.shape[1] == K
+    r = None if rows is None else _i32(rows)
+    M = Mx if r is None else len(r)
+    out = np.full((max(M, 1), N), np.nan) if y is None else np.ascontiguousarray(np.array(y, np.float64))
+    rc = lib(libpath).or_proj(M, Mx, K, N, _p(x, ctypes.c_double), _p(r, ctypes.c_int32), _p(w, ctypes.c_double),
+                              _p(out, ctypes.c_double))
+    if rc:
+        raise OracleError(rc)
+    return out[:M]

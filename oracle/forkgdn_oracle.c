@@ -34,6 +34,12 @@
  *    with S in R^{dv x dk}, a zero initial state for a fresh root, and the
  *    saved fp32 state for a cached history (Flide, section 3.4).
  *
+ *  - Projection (Flide, section 3.5: in a batch-invariant engine every matrix
+ *    product sums each output element in one order whatever the number of
+ *    rows; section 3.3.3: the last layer's products run only at the rows of
+ *    the readout index buffer): the plain definition y[m][n] = sum_k
+ *    x[r(m)][k] w[n][k] with r(m) an index buffer of rows, in fp64.
+ *
  *  - Short causal convolution (Flide, section 3.2.2: in front of the Gated
  *    DeltaNet rule a short causal convolution mixes each token with its few
  *    predecessors, and the first tokens of a question see the last tokens
@@ -555,4 +561,36 @@ int or_conv(int T, int S, const int *tok_seg, const int *seg_parent, const int *
 done:
     free(seg_start); free(seg_len); free(seg_pos0); free(seg_depth); free(seg_root); free(tok_pos);
     return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Projection                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* y [M, N] = rows of x [Mx, K] times w [N, K] transposed (w row n = output
+ * feature n, as a linear layer stores it):
+ *     y[m][n] = sum_{k < K} x[r][k] * w[n][k],   r = rows ? rows[m] : m,
+ * summed in fp64, k ascending.  An entry rows[m] < 0 selects no row: y's row
+ * m is left as it was.  An entry >= Mx is an error. */
+int or_proj(int M, int Mx, int K, int N, const double *x, const int *rows, const double *w, double *y)
+{
+    if (M < 0 || Mx < 0 || K <= 0 || N <= 0 || !x || !w || !y) return OR_E_ARG;
+    if (!rows && M > Mx) return OR_E_ARG;
+    for (int m = 0; m < M; ++m)
+        if (rows && rows[m] >= Mx) return OR_E_ARG;
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; ++m) {
+        /* planted: the index buffer ignored */
+        const int r = (rows && !MUT(14)) ? rows[m] : m;
+        if (r < 0 || r >= Mx) continue;
+        const double *xr = x + (size_t)r * K;
+        for (int n = 0; n < N; ++n) {
+            const double *wn = w + (size_t)n * K;
+            double acc = 0.0;
+            /* planted: the last term of the sum dropped */
+            for (int k = 0; k < K - MUT(13); ++k) acc += xr[k] * wn[k];
+            y[(size_t)m * N + n] = acc;
+        }
+    }
+    return OR_OK;
 }

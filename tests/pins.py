@@ -727,4 +727,48 @@ def pin_conv_window_and_resume(libpath=None):
     assert np.array_equal(y_full[head], y_t)
 
 
+# --------------------------------------------------------------------------
+# projection (Flide section 3.5: fixed-order products; section 3.3.3: the
+# last layer's products only at the readout rows)
+# --------------------------------------------------------------------------
+
+def pin_proj_matmul(libpath=None):
+    """The projection equals numpy's matrix product of the same fp64 values
+    (a library routine), on ragged sizes."""
+    rng = np.random.default_rng(11)
+    for M, K, N in ((1, 1, 1), (37, 48, 20), (5, 129, 3)):
+        x = rng.standard_normal((M, K))
+        w = rng.standard_normal((N, K))
+        y = oracle.proj(x, w, libpath=libpath)
+        np.testing.assert_allclose(y, np.matmul(x, w.T), rtol=1e-12, atol=1e-12)
+
+
+def pin_proj_rows(libpath=None):
+    """An index buffer gathers rows of the plain product (duplicates allowed),
+    and an unused entry (-1) leaves its output row untouched."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((9, 16))
+    w = rng.standard_normal((7, 16))
+    rows = np.array([4, -1, 0, 8, 4, -1, 2], np.int32)
+    y0 = np.full((len(rows), 7), 123.0)
+    y = oracle.proj(x, w, rows=rows, y=y0, libpath=libpath)
+    full = np.matmul(x, w.T)
+    for m, r in enumerate(rows):
+        if r < 0:
+            assert np.all(y[m] == 123.0)
+        else:
+            np.testing.assert_allclose(y[m], full[r], rtol=1e-12, atol=1e-12)
+
+
+def pin_proj_closed_forms(libpath=None):
+    """Identity weights return x exactly; a one-hot weight row e_j returns
+    column j of x exactly."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((6, 10))
+    assert np.array_equal(oracle.proj(x, np.eye(10), libpath=libpath), x)
+    w = np.zeros((3, 10))
+    w[0, 9], w[1, 0], w[2, 4] = 1.0, 1.0, 1.0
+    assert np.array_equal(oracle.proj(x, w, libpath=libpath), x[:, [9, 0, 4]])
+
+
 ALL_PINS = [v for k, v in list(globals().items()) if k.startswith("pin_")]

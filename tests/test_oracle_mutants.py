@@ -12,6 +12,8 @@ and check that the pin suite catches every one of them:
 10 conv: predecessors taken one row too far back
 11 sliding window one key too wide (t_x - t_y <= W)
 12 two-way rule misses the last row of the own segment
+13 projection: the last term of the sum dropped
+14 projection: the index buffer of rows ignored
 """
 import pytest
 
@@ -19,7 +21,7 @@ import oracle
 from tests import pins
 
 
-@pytest.mark.parametrize("mutant", range(1, 13))
+@pytest.mark.parametrize("mutant", range(1, 15))
 def test_mutant_is_caught(mutant):
     path = oracle.build(force=False, extra_flags=(f"-DORACLE_MUTANT={mutant}",))
     caught = []
