@@ -552,6 +552,47 @@ def measure_readout(wl, steps: int):
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": nbytes}
 
 
+def measure_proj(wl, steps: int):
+    """The fixed-order projection (a row beyond the step): the attention
+    layer's output projection, width Hq d -> Hq d, over every stream row of
+    the round (the attention output as x; w ~ N(0, 1/K), seeded), and over
+    the readout rows only (the last token of every question, gathered through
+    an index buffer).  MFMA-bound: 2 M N K flops."""
+    torch, fk, sh, tree = wl.torch, wl.fk, wl.sh, wl.tree
+    K = N = sh.Hq * sh.d
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.cfg.seed * 7 + 5)
+    w = (torch.randn((N, K), generator=g, device="cuda") * K ** -0.5).to(torch.bfloat16)
+    x = wl.attn_out.view(tree.T, K)
+    starts, acc = {}, 0
+    for sid in tree.order:
+        starts[sid] = acc
+        acc += tree.segs[sid].length
+    rows = torch.tensor([starts[i] + tree.segs[i].length - 1 for i in tree.leaves()], dtype=torch.int32,
+                        device="cuda")
+    y = torch.empty((tree.T, N), dtype=torch.bfloat16, device="cuda")
+    yr = torch.empty((rows.numel(), N), dtype=torch.bfloat16, device="cuda")
+    out = {}
+    for name, fn, M in (("stream_rows", lambda: fk.fk_proj_gemm(x, w, out=y), tree.T),
+                        ("readout_rows", lambda: fk.fk_proj_gemm(x, w, rows=rows, out=yr), rows.numel())):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        flops = 2.0 * M * N * K
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"kernel": "fixed-order projection (bf16 MFMA)", "M": M, "K": K, "N": N, "ms": ms,
+                     "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "algorithmic_flops": flops}
+    del y, yr, w
+    return out
+
+
 def host_cpu():
     """The host CPU the oracle ran on: model name and the CPUs this process may use."""
     model = "unknown"
@@ -834,7 +875,8 @@ def measure(index: int, args, next_rows: bool):
         out["next_rows"] = {"conv": measure_conv(wl, args.steps),
                             "window_attention": measure_rule(wl, args.steps, 1, 1024),
                             "two_way_attention": measure_rule(wl, args.steps, 2),
-                            "readout": measure_readout(wl, args.steps)}
+                            "readout": measure_readout(wl, args.steps),
+                            "projection": measure_proj(wl, args.steps)}
     del wl
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

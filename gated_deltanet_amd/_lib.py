@@ -23,7 +23,8 @@ STATUS = {0: "FK_OK", -1: "FK_E_INVALID_ARG", -2: "FK_E_UNSUPPORTED", -3: "FK_E_
 # exported symbols, in header order
 SYMBOLS = ("fk_workspace_bytes", "fk_tree_build", "fk_tree_validate_host", "fk_token_positions",
            "kv_append", "fork_attn_forward", "fork_attn_forward_rule", "fork_attn_readout", "gdn_fork_forward", "gdn_conv_forward", "gdn_checkpoint_save",
-           "gdn_checkpoint_resume", "fk_read_status", "fk_strerror", "fk_abi_version", "fk_peak_mfma_bf16")
+           "gdn_checkpoint_resume", "fk_proj_gemm", "fk_read_status", "fk_strerror", "fk_abi_version",
+           "fk_peak_mfma_bf16")
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -74,6 +75,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.gdn_conv_forward.argtypes = [mp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     L.gdn_checkpoint_save.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp]
     L.gdn_checkpoint_resume.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.fk_proj_gemm.argtypes = [vp, i32, vp, i32, i32, vp, i32, i32, vp, vp]
     L.fk_read_status.argtypes = [vp, vp, _i32p]
     L.fk_peak_mfma_bf16.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_double), vp]
     L.fk_strerror.argtypes = [ctypes.c_int]

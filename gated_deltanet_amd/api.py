@@ -239,6 +239,22 @@ def gdn_checkpoint_resume(ckpt, state_in, slot, count=1, stream=None):
         _ptr(ckpt), _ptr(state_in), int(slot), int(count), n, Hv, dk, dv, _stream(stream)))
 
 
+def fk_proj_gemm(x, w, rows=None, out=None, stream=None) -> torch.Tensor:
+    """y[m] = x[rows[m]] @ w.T (rows None: every row of x); x [Mx, K], w [N, K]
+    bf16; rows int32 device tensor [M] (-1 = unused entry, row untouched)."""
+    Mx, K = x.shape
+    N = w.shape[0]
+    assert w.shape[1] == K
+    M = Mx if rows is None else rows.numel()
+    if rows is not None:
+        assert rows.dtype == torch.int32
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    check("fk_proj_gemm", _lib.load().fk_proj_gemm(_ptr(x), Mx, _ptr(rows), M, K, _ptr(w), N, _DT[x.dtype],
+                                                   _ptr(out), _stream(stream)))
+    return out
+
+
 def fk_read_status(ws, stream=None) -> int:
     v = ctypes.c_int32(0)
     check("fk_read_status", _lib.load().fk_read_status(_ptr(ws), _stream(stream), ctypes.byref(v)))

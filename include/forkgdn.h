@@ -315,6 +315,28 @@ int gdn_checkpoint_resume(const float *ckpt, float *state_in, int32_t slot, int3
                           int32_t Hv, int32_t dk, int32_t dv, fk_stream_t stream);
 
 /*
+ * fk_proj_gemm -- a projection either side of the token mixers (the linear
+ * layers of a full model), with a fixed reduction order.  Flide section 3.5:
+ * a batch-invariant engine makes every matrix product sum each output
+ * element in one order whatever the number of rows; section 3.3.3: in the
+ * last layer the products run only at the rows of the readout index buffer.
+ *   y[m, n] = sum_k x[r(m), k] * w[n, k],   r(m) = rows[m], or m if rows is NULL
+ * accumulated in float32 over k in ascending steps of 16, by one work-group
+ * per output element whatever M is, so a row's bits depend only on that row
+ * of x and on w (never on M or on the other rows); output rounded to nearest
+ * even.
+ * x: [Mx, K] bf16 (device); rows: int32 [M] (device) or NULL (then M <= Mx);
+ * an entry outside [0, Mx) selects no row and leaves row m of y untouched;
+ * w: [N, K] bf16 (device; row n holds output feature n, as a linear layer
+ * stores its weight); y: [M, N] bf16 (device).
+ * Supported: FK_BF16 with K % 64 == 0 and N % 128 == 0 (FK_E_UNSUPPORTED
+ * otherwise); FK_E_INVALID_ARG for a negative size, a null pointer, or
+ * M > Mx without an index buffer.  M == 0 enqueues nothing.
+ */
+int fk_proj_gemm(const void *x, int32_t Mx, const int32_t *rows, int32_t M, int32_t K, const void *w, int32_t N,
+                 int dtype, void *y, fk_stream_t stream);
+
+/*
  * fk_read_status -- synchronise `stream` and read the device status word
  * written by fk_tree_build into *status_out (host): FK_OK or a tree error.
  */

@@ -106,3 +106,19 @@ def test_bad_arguments_rejected_on_host():
     m.T, m.S, m.max_depth, m.level_cap, m.fork_cap, m.page_size = 0, 1, 1, 1, 0, 16
     assert L.gdn_fork_forward(ctypes.byref(m), None, None, None, None, None, 0, 1, 1, 48, 48, None,
                               None, None, ctypes.c_void_p(256), 1 << 20, None) == -1  # no seg arrays
+
+
+def test_proj_gemm_host_errors():
+    """Argument errors are reported on the host before anything is enqueued
+    (no GPU call): unsupported widths, negative sizes, missing pointers; an
+    empty batch is a no-op."""
+    L = _lib.load()
+    bf16, f32 = _lib.FK_BF16, _lib.FK_F32
+    p = 16   # a dummy non-null address (never dereferenced on these paths)
+    assert L.fk_proj_gemm(p, 4, None, 4, 64, p, 128, f32, p, None) == -2     # dtype
+    assert L.fk_proj_gemm(p, 4, None, 4, 48, p, 128, bf16, p, None) == -2    # K % 64
+    assert L.fk_proj_gemm(p, 4, None, 4, 64, p, 96, bf16, p, None) == -2     # N % 128
+    assert L.fk_proj_gemm(p, 4, None, -1, 64, p, 128, bf16, p, None) == -1   # M < 0
+    assert L.fk_proj_gemm(p, 4, None, 5, 64, p, 128, bf16, p, None) == -1    # M > Mx, no rows
+    assert L.fk_proj_gemm(None, 4, None, 4, 64, p, 128, bf16, p, None) == -1
+    assert L.fk_proj_gemm(None, 0, None, 0, 64, None, 128, bf16, None, None) == 0   # empty
