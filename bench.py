@@ -198,6 +198,18 @@ class Step:
         cur.wait_stream(self._side)
 
 
+def pad_rows(x: dict, rows: int) -> dict:
+    """Stream tensors padded with zero rows up to a bucket's capacity."""
+    import torch
+
+    out = {}
+    for n, t in x.items():
+        p = torch.zeros((rows,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
+        p[:t.shape[0]] = t
+        out[n] = p
+    return out
+
+
 class Workload(Step):
     """A config's round resident on the GPU, ready to step.  bf16 inputs are
     drawn on the GPU (seeded, the workload recipe, torch's generator); the
@@ -218,22 +230,28 @@ class Workload(Step):
         sh = cfg.shapes
         self.sh = sh
         dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        ts, par, fkk, cl = tree.arrays()
+        # the round in the smallest capacity bucket that holds it (tail
+        # padding, unused segment slots): the graph replayed below is that
+        # bucket's, valid for any round that fits it
+        self.bucket = fk.bucket_for(tree.T, tree.S, *fk.capacities(par, fkk, cl))
         if cfg.dtype == "bf16":
-            self.x = draw_stream(tree.T, sh, cfg.seed * 7 + 2, cfg.mu_a, device)
+            x = draw_stream(tree.T, sh, cfg.seed * 7 + 2, cfg.mu_a, device)
         else:
             inp = draw_inputs(tree, cfg.shapes, cfg.seed, cfg.dtype, cfg.mu_a)
-            self.x = {n: torch.from_numpy(np.ascontiguousarray(inp.raw[n])).to(device) for n in inp.raw}
+            x = {n: torch.from_numpy(np.ascontiguousarray(inp.raw[n])).to(device) for n in inp.raw}
             del inp
-        ts, par, fkk, cl = tree.arrays()
+        self.x = pad_rows(x, self.bucket.T)
         sso = np.full(tree.S, -1, np.int32)
-        self.plan = fk.plan_round(ts, par, fkk, cl, seg_state_out=sso, n_state_out=0, device=device)
+        self.plan = fk.plan_round(ts, par, fkk, cl, seg_state_out=sso, n_state_out=0, bucket=self.bucket,
+                                  device=device)
         self.meta = self.plan.meta
         self.ws = fk.alloc_workspace(self.meta, sh.Hv, sh.dk, sh.dv, device=device)
         n_pages = self.plan.n_pages
         self.k_pool = torch.zeros((n_pages, sh.Hkv, 16, sh.d), dtype=dt, device=device)
         self.v_pool = torch.zeros((n_pages, sh.Hkv, sh.d, 16), dtype=dt, device=device)
-        self.attn_out = torch.empty_like(self.x["aq"])
-        self.gdn_out = torch.empty_like(self.x["gv"])
+        self.attn_out = torch.zeros_like(self.x["aq"])   # padding rows stay zero
+        self.gdn_out = torch.zeros_like(self.x["gv"])
         self.scale = sh.d ** -0.5
         self.gdn_ok = True
 
@@ -291,8 +309,9 @@ class ResumeWorkload(Step):
         # pass 1: every history as a live root, laid out request by request
         self.hx = draw_stream(R * H, sh, cfg.seed * 7 + 1, cfg.mu_a, device,
                               names=("ak", "av", "gq", "gk", "gv", "ga", "gb"))
-        # the round: live stream in tree order
-        self.x = draw_stream(tree.T, sh, cfg.seed * 7 + 2, cfg.mu_a, device)
+        # the round: live stream in tree order, padded to its capacity bucket
+        self.bucket = fk.bucket_for(tree.T, tree.S, *fk.capacities(*tree.arrays()[1:]))
+        self.x = pad_rows(draw_stream(tree.T, sh, cfg.seed * 7 + 2, cfg.mu_a, device), self.bucket.T)
         starts, acc = {}, 0
         for sid in tree.order:
             starts[sid] = acc
@@ -331,7 +350,7 @@ class ResumeWorkload(Step):
             sso[root] = r
         self.plan = fk.plan_round(ts, par, fkk, cl, cached_pages=cached_pages, first_page=n_hist_pages,
                                   n_pages=n_pages, seg_state_in=ssi, seg_state_out=sso, n_state_in=R,
-                                  n_state_out=R, device=device)
+                                  n_state_out=R, bucket=self.bucket, device=device)
         assert n_hist_pages + self.plan.pages_used == n_pages
         self.meta = self.plan.meta
         self.hplan = fk.plan_round(np.repeat(np.arange(R, dtype=np.int32), H), np.full(R, -1), np.zeros(R),
@@ -345,8 +364,8 @@ class ResumeWorkload(Step):
         self.state_out = torch.zeros(st, dtype=torch.float32, device=device)
         self.ckpt = torch.zeros(st, dtype=torch.float32, device=device)
         self.ckpt_next = torch.zeros(st, dtype=torch.float32, device=device)
-        self.attn_out = torch.empty_like(self.x["aq"])
-        self.gdn_out = torch.empty_like(self.x["gv"])
+        self.attn_out = torch.zeros_like(self.x["aq"])   # padding rows stay zero
+        self.gdn_out = torch.zeros_like(self.x["gv"])
         self.scale = sh.d ** -0.5
         self.ws = fk.alloc_workspace(self.meta, sh.Hv, sh.dk, sh.dv, device=device)
 
@@ -428,7 +447,7 @@ def measure_conv(wl, steps: int, W: int = 4):
     once (+ windows)."""
     torch, fk, sh, meta = wl.torch, wl.fk, wl.sh, wl.meta
     C = 2 * sh.Hk * sh.dk + sh.Hv * sh.dv
-    T = wl.tree.T
+    T = wl.meta.T   # the bucket's stream capacity (padding rows are never read or written)
     g = torch.Generator(device="cuda")
     g.manual_seed(wl.cfg.seed * 7 + 3)
     x = torch.empty((T, C), dtype=torch.bfloat16, device="cuda")
@@ -453,7 +472,7 @@ def measure_conv(wl, steps: int, W: int = 4):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    nbytes = 2.0 * T * C * 2 + (meta.n_state_in + meta.n_state_out) * (W - 1) * C * 2
+    nbytes = 2.0 * wl.tree.T * C * 2 + (meta.n_state_in + meta.n_state_out) * (W - 1) * C * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": "forked short conv (bf16)", "channels": C, "width": W, "ms": ms, "bound": "hbm",
             "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
@@ -563,7 +582,7 @@ def measure_proj(wl, steps: int):
     g = torch.Generator(device="cuda")
     g.manual_seed(wl.cfg.seed * 7 + 5)
     w = (torch.randn((N, K), generator=g, device="cuda") * K ** -0.5).to(torch.bfloat16)
-    x = wl.attn_out.view(tree.T, K)
+    x = wl.attn_out[:tree.T].view(tree.T, K)
     starts, acc = {}, 0
     for sid in tree.order:
         starts[sid] = acc
@@ -839,6 +858,9 @@ def measure(index: int, args, next_rows: bool):
                    "leaves": len(tree.leaves()), "attn_heads": [sh.Hq, sh.Hkv, sh.d],
                    "gdn_heads": [sh.Hk, sh.Hv, sh.dk, sh.dv]},
         "execution": mode,
+        "graph_bucket": {"stream_tokens": wl.bucket.T, "segment_slots": wl.bucket.S,
+                         "levels": wl.bucket.max_depth, "level_cap": wl.bucket.level_cap,
+                         "fork_cap": wl.bucket.fork_cap},
         "graph_warmup_replays": n_warm,
         "graph_forms_ms": forms or None,
         "step_ms_distribution": dist,

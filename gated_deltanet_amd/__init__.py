@@ -12,5 +12,5 @@ from .api import (TreeMeta, alloc_workspace, fk_read_status, fk_strerror,  # noq
                   gdn_checkpoint_resume, gdn_checkpoint_save, gdn_conv_forward,
                   gdn_fork_forward,
                   kv_append, make_tree_meta, fk_peak_mfma_bf16, fk_proj_gemm)
-from .rounds import RoundPlan, capacities, plan_round  # noqa: F401,E402
-from .graph import StepGraph  # noqa: F401,E402
+from .rounds import Bucket, RoundPlan, bucket_for, capacities, plan_arrays, plan_round  # noqa: F401,E402
+from .graph import BucketRound, GraphFamily, StepGraph  # noqa: F401,E402

@@ -67,6 +67,7 @@ __global__ void __launch_bounds__(64) k_attn_f32(const float *__restrict__ q, in
         const int t = sel_rows[tile];
         if (t < 0 || t >= T) return;   // an unused entry of the row buffer
         s = tok_seg[t];
+        if (s < 0) return;             // a padding token: no output
         row0 = t - seg_start[s];
         nrows = 1;
     } else {

@@ -434,7 +434,7 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
     // loads are issued first and land while the walk is planned
     const int slot = w * 4 + n / 8, e = grp * group + slot;
     const int t = (slot < group && e < n_rows) ? sel_rows[e] : -1;
-    const bool row_valid = t >= 0 && t < T;
+    const bool row_valid = t >= 0 && t < T && tok_seg[t] >= 0;   // not unused, not padding
     const int h = g * G + (n % 8);
     const size_t qrow = (size_t)e * Hq + h;
     bf16x8 qf[D / 16];
@@ -453,8 +453,9 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
         const int ce = grp * group + cslot;
         int cseg = -1, clim = 0, clo = 0;
         const int ct = (cslot < group && ce < n_rows) ? sel_rows[ce] : -1;
-        if (ct >= 0 && ct < T) {
-            const int cs = tok_seg[ct], cdep = seg_depth[cs];
+        const int cs = (ct >= 0 && ct < T) ? tok_seg[ct] : -1;
+        if (cs >= 0) {
+            const int cdep = seg_depth[cs];
             const int cloc = ct - seg_start[cs];
             if (cd <= cdep) {
                 const int32_t *ca = seg_anc + (size_t)cs * FK_MAX_DEPTH;

@@ -110,6 +110,10 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
         for (int u = 0; u < TB; ++u) {
             const int t = base + u * BUILD_THREADS + threadIdx.x, s = sv[u];
             if (t >= T) continue;
+            if (s == FK_PAD_TOKEN) {   // padding: only more padding may follow
+                if (t + 1 < T && nv[u] != FK_PAD_TOKEN) build_error(A.header, &flag, FK_E_SEG_RANGE);
+                continue;
+            }
             if (s < 0 || s >= S) {
                 build_error(A.header, &flag, FK_E_SEG_RANGE);
                 continue;
@@ -131,7 +135,7 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
                                      nrun == 1 ? A.seg_end[s] - A.seg_start[s] : 0, &len);
         if (code) build_error(A.header, &flag, code);
         A.seg_len[s] = len;
-        if (m.seg_cached_len[s] > 0) A.seg_start[s] = -1;
+        if (m.seg_cached_len[s] != 0) A.seg_start[s] = -1;   // cached or unused: no stream tokens
     }
     if (block_failed(&flag)) return;
 
@@ -384,7 +388,7 @@ __device__ void positions_thread(int t, const int32_t *__restrict__ tok_seg, int
 {
     if (t >= T) return;
     const int s = tok_seg[t];
-    tok_pos[t] = seg_pos0[s] + (t - seg_start[s]);
+    tok_pos[t] = s >= 0 ? seg_pos0[s] + (t - seg_start[s]) : -1;   // padding: no position
 }
 
 // After k_build, in one launch of BUILD_THREADS-thread blocks: the orders
@@ -505,6 +509,10 @@ extern "C" int fk_tree_validate_host(const fk_tree_meta *m)
     int code = FK_OK;
     for (int t = 0; t < T; ++t) {
         const int s = m->tok_seg[t];
+        if (s == FK_PAD_TOKEN) {   // padding: only more padding may follow
+            if (t + 1 < T && m->tok_seg[t + 1] != FK_PAD_TOKEN) code = imin(code, FK_E_SEG_RANGE);
+            continue;
+        }
         if (s < 0 || s >= S) { code = imin(code, FK_E_SEG_RANGE); continue; }
         if (t == 0 || m->tok_seg[t - 1] != s) { nrun[s]++; start[s] = t; }
         if (t == T - 1 || m->tok_seg[t + 1] != s) end[s] = t + 1;
@@ -525,7 +533,7 @@ extern "C" int fk_tree_validate_host(const fk_tree_meta *m)
     // phase 3: capacities
     std::vector<int> per_level(FK_MAX_DEPTH, 0);
     for (int s = 0; s < S; ++s) {
-        if (m->seg_cached_len[s] > 0) continue;
+        if (m->seg_cached_len[s] != 0) continue;   // cached or unused
         int depth = 0;
         for (int i = s; m->seg_parent[i] >= 0; i = m->seg_parent[i]) ++depth;
         per_level[depth]++;
@@ -535,7 +543,7 @@ extern "C" int fk_tree_validate_host(const fk_tree_meta *m)
     long long forks = 0;
     for (int c = 0; c < S; ++c) {
         const int p = m->seg_parent[c];
-        if (m->seg_cached_len[c] > 0 || p < 0 || m->seg_cached_len[p] > 0) continue;
+        if (m->seg_cached_len[c] != 0 || p < 0 || m->seg_cached_len[p] != 0) continue;
         bool owner = true;
         for (int o = 0; o < c; ++o)
             if (m->seg_parent[o] == p && m->seg_cached_len[o] == 0 && m->seg_fork[o] == m->seg_fork[c])

@@ -5,11 +5,15 @@
 // Rules (Flide section 3.2: tokens of a segment are contiguous in the flat
 // stream and positions continue from the fork; section 3.4: a cached history
 // is continued from its end; ForkServe item 1: a child sees a prefix of its
-// parent):
-//   phase 0  every token names a segment in [0, S)                 FK_E_SEG_RANGE
+// parent; section 3.3.2: a round fills a graph captured for a larger
+// capacity, with padding only at the tail):
+//   phase 0  every token names a segment in [0, S), or is padding   FK_E_SEG_RANGE
+//            (FK_PAD_TOKEN) followed only by padding
 //   phase 1  a live segment has >= 1 token in one contiguous run;   FK_E_EMPTY /
-//            a cached segment has no stream tokens                  FK_E_NONCONTIG
-//   phase 2  parent in [-1, S) and not itself; root fork 0; child   FK_E_PARENT,
+//            a cached segment, and an unused slot                   FK_E_NONCONTIG
+//            (FK_UNUSED_SEGMENT), has no stream tokens
+//   phase 2  parent in [-1, S), not itself, not an unused slot;     FK_E_PARENT,
+//            root fork 0; child
 //            fork in [0, len(parent)]; cached only under cached;    FK_E_FORK,
 //            a live child of a cached segment forks at its end;     FK_E_CACHED,
 //            chain reaches a root within max_depth levels;          FK_E_CYCLE,
@@ -35,10 +39,17 @@ namespace fk {
 
 FK_HD int imin(int a, int b) { return a < b ? a : b; }
 
-// phase 1: segment length from its token runs (nrun) or cached length
+FK_HD bool is_unused(int cached_len) { return cached_len == FK_UNUSED_SEGMENT; }
+
+// phase 1: segment length from its token runs (nrun) or cached length; an
+// unused slot has length 0 and no tokens
 FK_HD int rule_length(int cached_len, int nrun, int run_len, int *len_out)
 {
     int code = FK_OK;
+    if (is_unused(cached_len)) {
+        *len_out = 0;
+        return nrun > 0 ? FK_E_EMPTY : FK_OK;
+    }
     if (cached_len < 0) code = imin(code, FK_E_EMPTY);
     if (cached_len > 0 && nrun > 0) code = imin(code, FK_E_EMPTY);
     if (cached_len == 0 && nrun == 0) code = imin(code, FK_E_EMPTY);
@@ -64,7 +75,13 @@ FK_HD int rule_links(int s, int S, int max_depth, const int32_t *parent, const i
     int code = FK_OK;
     const int p = parent[s];
     const bool cached = cached_len[s] > 0;
-    if (p < -1 || p >= S || p == s) {
+    if (is_unused(cached_len[s])) {   // an unused slot: nothing to derive
+        out->depth = 0;
+        out->pos0 = 0;
+        out->anc[0] = s;
+        return FK_OK;
+    }
+    if (p < -1 || p >= S || p == s || (p >= 0 && is_unused(cached_len[p]))) {
         code = imin(code, FK_E_PARENT);
     } else if (p == -1) {
         if (fork[s] != 0) code = imin(code, FK_E_FORK);

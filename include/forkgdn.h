@@ -78,6 +78,11 @@ enum fk_status {
 /* Tokens per Gated DeltaNet chunk of the bf16 path (anchored at the start of
    every segment, so a trunk's chunking never depends on its branches). */
 #define FK_GDN_CHUNK 64
+/* tok_seg value of a padding token (the stream's tail past the round's live
+   tokens, when T is a capacity), and seg_cached_len value of an unused
+   segment slot (when S is a capacity). */
+#define FK_PAD_TOKEN (-1)
+#define FK_UNUSED_SEGMENT (-1)
 
 /*
  * Round description (Flide section 3.3.1: all variables set by the round
@@ -93,6 +98,16 @@ enum fk_status {
  * Cached segments must be roots or children of cached segments, and a live
  * child of a cached segment must fork at the cached segment's end.
  *
+ * Capacities (Flide section 3.3.2: graphs are captured once per stream
+ * capacity and a round pads only at the tail): T and S may exceed the round.
+ * Tokens past the round's last live token are padding (tok_seg ==
+ * FK_PAD_TOKEN; padding may be followed only by padding) and segment slots
+ * the round does not use have seg_cached_len == FK_UNUSED_SEGMENT (no tokens;
+ * no segment may name one as its parent; their other fields are ignored).
+ * Padding and unused slots get no tile, chunk, page write, position (-1) or
+ * output row, so a round padded into a larger capacity gives the bits of the
+ * same round described exactly.
+ *
  * K/V pages: segment s owns pages seg_pages[seg_page_off[s] ..
  * seg_page_off[s+1]); its token i lives in page seg_pages[off + i/page_size],
  * slot i % page_size.  Every segment starts on a fresh page; a child aliases
@@ -100,8 +115,8 @@ enum fk_status {
  * fork copies the parent page table and an alias length).
  */
 typedef struct fk_tree_meta {
-    int32_t T;           /* live stream tokens (>= 0)                            */
-    int32_t S;           /* segments, live + cached (>= 1)                       */
+    int32_t T;           /* stream tokens, live + padding (>= 0)                 */
+    int32_t S;           /* segment slots, live + cached + unused (>= 1)         */
     int32_t max_depth;   /* capacity: tree levels, 1..FK_MAX_DEPTH               */
     int32_t level_cap;   /* capacity: live segments on any one level (>= 1)      */
     int32_t fork_cap;    /* capacity: distinct (parent, fork offset) fork points */
@@ -109,10 +124,12 @@ typedef struct fk_tree_meta {
     int32_t n_pages;     /* pages in the K/V pool                                */
     int32_t n_state_in;  /* slots in state_in (may be 0)                         */
     int32_t n_state_out; /* slots in state_out (may be 0)                        */
-    const int32_t *tok_seg;        /* [T]   segment of every stream token         */
+    const int32_t *tok_seg;        /* [T]   segment of every stream token, or
+                                            FK_PAD_TOKEN                          */
     const int32_t *seg_parent;     /* [S]   parent segment, -1 for a root         */
     const int32_t *seg_fork;       /* [S]   parent tokens this segment sees       */
-    const int32_t *seg_cached_len; /* [S]   history length if cached, else 0      */
+    const int32_t *seg_cached_len; /* [S]   history length if cached, 0 if live,
+                                            FK_UNUSED_SEGMENT if unused           */
     const int32_t *seg_page_off;   /* [S+1] CSR offsets into seg_pages            */
     const int32_t *seg_pages;      /* [seg_page_off[S]] page ids                  */
     const int32_t *seg_state_in;   /* [S]   state_in slot of a cached segment, -1 */
@@ -228,7 +245,8 @@ int fork_attn_forward_rule(const fk_tree_meta *meta, const void *q, const void *
  * final layer every token still contributes its keys and values while the
  * rest of the layer runs only at these rows, listed in an index buffer of
  * fixed size).  rows: int32 [n_rows] (device), stream token index of each
- * entry, or -1 for an unused entry (its output row is left untouched).
+ * entry, or -1 for an unused entry (its output row is left untouched; so is
+ * that of an entry naming a padding token).
  * q_rows, out_rows: [n_rows, Hq, d] -- the queries and outputs of the entries.
  * The round's keys/values must already be in the pool (kv_append or a full
  * fork_attn_forward of the round).  Each entry's output has the same bits as

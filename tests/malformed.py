@@ -6,7 +6,10 @@ import numpy as np
 # (name, tok_seg, seg_parent, seg_fork, seg_cached_len, expected class)
 CASES = [
     ("seg_out_of_range", [0, 0, 2], [-1, 0], [0, 2], [0, 0], "seg_range"),
-    ("negative_seg", [0, -1], [-1, 0], [0, 1], [0, 0], "seg_range"),
+    ("negative_seg", [0, -2], [-1, 0], [0, 1], [0, 0], "seg_range"),
+    # -1 marks tail padding of a capacity bucket on the GPU side; before a
+    # live token it is malformed on both sides
+    ("padding_before_live", [-1, 0, 1], [-1, 0], [0, 1], [0, 0], "seg_range"),
     ("noncontiguous", [0, 1, 0], [-1, 0], [0, 1], [0, 0], "noncontig"),
     ("parent_out_of_range", [0, 1], [-1, 5], [0, 1], [0, 0], "parent"),
     ("self_parent", [0, 1], [-1, 1], [0, 0], [0, 0], "parent"),

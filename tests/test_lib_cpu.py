@@ -122,3 +122,45 @@ def test_proj_gemm_host_errors():
     assert L.fk_proj_gemm(p, 4, None, 5, 64, p, 128, bf16, p, None) == -1    # M > Mx, no rows
     assert L.fk_proj_gemm(None, 4, None, 4, 64, p, 128, bf16, p, None) == -1
     assert L.fk_proj_gemm(None, 0, None, 0, 64, None, 128, bf16, None, None) == 0   # empty
+
+
+def test_host_validator_padding_and_unused_slots():
+    """A round planned into a larger capacity bucket (tail padding, unused
+    segment slots) validates, with the same rules as the exact round; padding
+    before a live token, tokens in an unused slot, and an unused slot as a
+    parent are rejected."""
+    rng = np.random.default_rng(8)
+    for _ in range(20):
+        t = random_tree(rng, p_cached_root=0.3, p_internal_fork=0.4).flatten()
+        ts, par, fkk, cl = t.arrays()
+        ssi = np.where(cl > 0, 0, -1)
+        caps = fk.capacities(par, fkk, cl)
+        b = fk.bucket_for(len(ts), len(par), *caps)
+        a, _, _, _ = fk.plan_arrays(ts, par, fkk, cl, seg_state_in=ssi, bucket=b)
+        assert len(a["tok_seg"]) == b.T >= len(ts) and len(a["seg_parent"]) == b.S >= len(par)
+        assert fk.fk_tree_validate_host(a["tok_seg"], a["seg_parent"], a["seg_fork"], a["seg_cached_len"],
+                                        seg_state_in=a["seg_state_in"], n_state_in=1, max_depth=b.max_depth,
+                                        level_cap=b.level_cap, fork_cap=b.fork_cap) == 0
+    ts = np.array([0, 0, -1, -1], np.int32)
+    par, fkk = np.array([-1, -1]), np.array([0, 0])
+    cl = np.array([0, -1])
+    assert fk.fk_tree_validate_host(ts, par, fkk, cl) == 0
+    bad = np.array([0, -1, 0, -1], np.int32)       # padding before a live token
+    assert _lib.STATUS[fk.fk_tree_validate_host(bad, par, fkk, cl)] == "FK_E_SEG_RANGE"
+    bad = np.array([0, 0, 1, -1], np.int32)        # a token in an unused slot
+    assert _lib.STATUS[fk.fk_tree_validate_host(bad, par, fkk, cl)] == "FK_E_EMPTY"
+    assert _lib.STATUS[fk.fk_tree_validate_host(ts, np.array([1, -1]), np.array([0, 0]), cl)] == "FK_E_PARENT"
+
+
+def test_bucket_ladder():
+    b = fk.bucket_for(24526, 117, 2, 101, 16)
+    assert b.T >= 24526 and b.T < 1.25 * 24526 + 1024 and b.S >= 117 and b.max_depth == 2
+    assert fk.bucket_for(1, 1, 1, 1, 0) == fk.Bucket(T=1024, S=16, max_depth=2, level_cap=16, fork_cap=16)
+    # every member fits the round it was chosen for, and a larger round never gets a smaller member
+    prev = None
+    for T in (1000, 5000, 40000, 220640):
+        b = fk.bucket_for(T, T // 40, 3, T // 50, T // 200)
+        assert b.T >= T and b.S >= T // 40 and b.max_depth == 4
+        if prev:
+            assert b.T >= prev.T
+        prev = b
