@@ -85,16 +85,18 @@ __global__ void __launch_bounds__(256) k_kv_append_bf16(const uint16_t *__restri
     *reinterpret_cast<uint4 *>(kp + page_base + r * KV_D + c8 * 8) = kv;
     *reinterpret_cast<uint4 *>(vt + r * KV_VS + c8 * 8) = vv;
     __syncthreads();
-    // dim x = tid / 2, slots [8 (tid % 2), +8)
-    const int x = threadIdx.x >> 1, r8 = (threadIdx.x & 1) * 8;
+    // dim x = tid / 2, slots [8 (tid % 2), +8).  The two lanes of a pair read
+    // slot rows 8 apart (8 x 68 dwords: the same bank); the odd lane walks its
+    // rows rotated by four (rows 68 x 4 dwords further on: 16 banks away), so
+    // every read of a wave is free of bank conflicts, and swaps the halves of
+    // its result back into slot order.
+    const int x = threadIdx.x >> 1, odd = threadIdx.x & 1, r8 = odd * 8;
     uint16_t e[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = vt[(r8 + j) * KV_VS + x];
-    uint4 out;
-    out.x = e[0] | ((uint32_t)e[1] << 16);
-    out.y = e[2] | ((uint32_t)e[3] << 16);
-    out.z = e[4] | ((uint32_t)e[5] << 16);
-    out.w = e[6] | ((uint32_t)e[7] << 16);
+    for (int j = 0; j < 8; ++j) e[j] = vt[(r8 + ((j + 4 * odd) & 7)) * KV_VS + x];
+    const uint32_t p0 = e[0] | ((uint32_t)e[1] << 16), p1 = e[2] | ((uint32_t)e[3] << 16);
+    const uint32_t p2 = e[4] | ((uint32_t)e[5] << 16), p3 = e[6] | ((uint32_t)e[7] << 16);
+    const uint4 out = odd ? make_uint4(p2, p3, p0, p1) : make_uint4(p0, p1, p2, p3);
     *reinterpret_cast<uint4 *>(vp + page_base + x * FK_TILE_TOKENS + r8) = out;
 }
 
