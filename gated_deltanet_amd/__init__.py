@@ -8,7 +8,7 @@ rounds (``rounds``).
 from . import _lib  # noqa: F401
 from .api import (TreeMeta, alloc_workspace, fk_read_status, fk_strerror,  # noqa: F401
                   fk_token_positions, fk_tree_build, fk_tree_validate_host, fk_workspace_bytes,
-                  fork_attn_forward, fork_attn_forward_rule, fork_attn_readout,
+                  fork_attn_forward, fork_attn_forward_noalloc, fork_attn_forward_rule, fork_attn_readout,
                   gdn_checkpoint_resume, gdn_checkpoint_save, gdn_conv_forward,
                   gdn_fork_forward,
                   kv_append, make_tree_meta, fk_peak_mfma_bf16, fk_proj_gemm)

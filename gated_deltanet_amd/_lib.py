@@ -22,7 +22,7 @@ STATUS = {0: "FK_OK", -1: "FK_E_INVALID_ARG", -2: "FK_E_UNSUPPORTED", -3: "FK_E_
 
 # exported symbols, in header order
 SYMBOLS = ("fk_workspace_bytes", "fk_tree_build", "fk_tree_validate_host", "fk_token_positions",
-           "kv_append", "fork_attn_forward", "fork_attn_forward_rule", "fork_attn_readout", "gdn_fork_forward", "gdn_conv_forward", "gdn_checkpoint_save",
+           "kv_append", "fork_attn_forward", "fork_attn_forward_noalloc", "fork_attn_forward_rule", "fork_attn_readout", "gdn_fork_forward", "gdn_conv_forward", "gdn_checkpoint_save",
            "gdn_checkpoint_resume", "fk_proj_gemm", "fk_read_status", "fk_strerror", "fk_abi_version",
            "fk_peak_mfma_bf16")
 
@@ -68,6 +68,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.fk_token_positions.argtypes = [mp, vp, vp, vp]
     L.kv_append.argtypes = [mp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     L.fork_attn_forward.argtypes = [mp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
+    L.fork_attn_forward_noalloc.argtypes = [mp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]
     L.fork_attn_forward_rule.argtypes = [mp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, sz,
                                          vp]
     L.fork_attn_readout.argtypes = [mp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, sz, vp]

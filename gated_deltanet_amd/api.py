@@ -163,6 +163,23 @@ def fork_attn_forward(meta: TreeMeta, q, k, v, k_pool, v_pool, ws, scale=None, o
     return out
 
 
+def fork_attn_forward_noalloc(meta: TreeMeta, q, k, v, k_pool, v_pool, scale=None, out=None, status=None,
+                              stream=None) -> torch.Tensor:
+    """fk_tree_build + fork_attn_forward without a workspace (the library's
+    fixed per-GPU array holds the round's metadata); ``status`` (int32 device
+    tensor of one element, optional) receives the round's status word."""
+    T, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    scale = float(scale if scale is not None else d ** -0.5)
+    m = meta.c()
+    check("fork_attn_forward_noalloc", _lib.load().fork_attn_forward_noalloc(
+        ctypes.byref(m), _ptr(q), _ptr(k), _ptr(v), _DT[q.dtype], Hq, Hkv, d, scale, _ptr(k_pool), _ptr(v_pool),
+        _ptr(out), _ptr(status), _stream(stream)))
+    return out
+
+
 def fork_attn_forward_rule(meta: TreeMeta, q, k, v, k_pool, v_pool, ws, rule, window=0, scale=None,
                            out=None, stream=None) -> torch.Tensor:
     """Attention under a visibility rule: _lib.FK_RULE_CAUSAL / FK_RULE_WINDOW

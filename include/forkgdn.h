@@ -279,6 +279,29 @@ int gdn_fork_forward(const fk_tree_meta *meta, const void *q, const void *k, con
                      const float *state_in, float *state_out, void *out, void *ws, size_t ws_bytes,
                      fk_stream_t stream);
 
+/* Size of the library's fixed per-GPU metadata array used by
+   fork_attn_forward_noalloc. */
+#define FK_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * fork_attn_forward_noalloc -- for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): fk_tree_build followed by
+ * fork_attn_forward in one call, with the round's derived metadata kept in
+ * the library's own fixed array of FK_NOALLOC_SCRATCH_BYTES per GPU instead
+ * of a caller workspace.  Same kernels, so the same output bits.  Arguments
+ * as fork_attn_forward (k and v NULL: the keys/values are already paged);
+ * status: int32 (device) or NULL -- receives the round's status word (FK_OK
+ * or a tree error), copied on `stream` after the attention.  Returns
+ * FK_E_WORKSPACE when fk_workspace_bytes(meta, 0, 0, 0) exceeds
+ * FK_NOALLOC_SCRATCH_BYTES.  Calls no allocator.  All calls on one GPU share
+ * its array (the first call on a device looks up the array's address there);
+ * calls that overlap on one GPU race.
+ */
+int fork_attn_forward_noalloc(const fk_tree_meta *meta, const void *q, const void *k, const void *v, int dtype,
+                              int Hq, int Hkv, int d, float scale, void *k_pool, void *v_pool, void *out,
+                              int32_t *status, fk_stream_t stream);
+
 /* Widest short convolution of gdn_conv_forward. */
 #define FK_CONV_MAX_W 8
 
