@@ -396,30 +396,62 @@ struct Item {
 
 __device__ __forceinline__ int item_nch(const Item &I) { return (I.len + C - 1) / C; }
 
-// How a level's items are dealt to the G work-groups.  Items are numbered
-// (v-head, dv slice) major, segment rank minor, so consecutive items of a
-// group are sibling segments on the same head and slice -- they enter from
-// the same fork-point state.  A level with at least 4 G items is dealt in
-// contiguous runs (work-group b takes items [b per, b per + per)), so a run of
-// siblings stages their common entering state once; a smaller level is dealt
-// forward and backward in turn (items b, 2G-1-b, 2G+b, ...), pairing its long
-// items with its short ones.  Once an id reaches n_items every later id of
-// the same work-group does too.
+// How a level's items are dealt to the G work-groups.  The items of one
+// segment that read the same key and query rows -- every v-head of a k-head
+// and every dv slice, M of them -- form a group, and M work-groups on one
+// XCD (work-group b runs on XCD b mod 8) take the M members of the same
+// groups in the same order, so the M reads of a chunk's keys and queries
+// (and the two reads of its T and P per v-head) meet in that XCD's L2 at
+// about the same time: the members of a group walk the same number of chunks.
+// Groups are numbered k-head major, segment rank minor, so a member's
+// consecutive groups are sibling segments on the same v-head and slice --
+// they enter from the same fork-point state.  A level with at least 4 Q
+// groups per member set (Q = G / M sets) is dealt in contiguous runs (set q
+// takes groups [q per, q per + per)), so a run of siblings stages their
+// common entering state once; a smaller level is dealt forward and backward
+// in turn (groups q, 2Q-1-q, 2Q+q, ...), pairing its long segments with its
+// short ones.  When G is not a multiple of 8 M, every item is its own group
+// (M = 1).  Item id = group * M + member; once an id reaches n_items every
+// later id of the same work-group does too.
 struct Walk {
-    int n_items, nseg, G, per;
+    int n_items, nseg, n_grp, Q, per, M, set, mem;
     bool runs;
 };
 
-__device__ __forceinline__ int item_id(const Walk &W, int b, int k)
+__device__ __forceinline__ Walk make_walk(int nseg, int Hv, int Hk, int G, int b)
 {
-    if (W.runs) return k < W.per ? b * W.per + k : 0x7fffffff;
-    return k * W.G + ((k & 1) ? W.G - 1 - b : b);
+    Walk W;
+    W.nseg = nseg;
+    W.n_items = nseg * Hv * NSL;
+    const int M = (Hv / Hk) * NSL;
+    W.M = G % (8 * M) == 0 ? M : 1;
+    // work-group b: XCD x = b mod 8, y = b / 8; member y mod M of set x + 8 (y / M)
+    const int x = b & 7, y = b >> 3;
+    W.mem = W.M == 1 ? 0 : y % W.M;
+    W.set = W.M == 1 ? b : x + 8 * (y / W.M);
+    W.Q = G / W.M;
+    W.n_grp = W.n_items / W.M;
+    W.runs = W.n_grp >= 4 * W.Q;
+    W.per = (W.n_grp + W.Q - 1) / W.Q;
+    return W;
+}
+
+__device__ __forceinline__ int item_id(const Walk &W, int k)
+{
+    int g;
+    if (W.runs)
+        g = k < W.per ? W.set * W.per + k : W.n_grp;
+    else
+        g = k * W.Q + ((k & 1) ? W.Q - 1 - W.set : W.set);
+    return g >= W.n_grp ? 0x7fffffff : g * W.M + W.mem;
 }
 
 __device__ __forceinline__ Item item_at(const ChunkArgs &A, const Walk &W, int it)
 {
     Item I;
-    const int rank = it % W.nseg, hs = it / W.nseg;
+    // group g = (k-head block, segment rank); member m -> (v-head, slice)
+    const int g = it / W.M, m = it % W.M;
+    const int rank = g % W.nseg, hs = (g / W.nseg) * W.M + m;
     I.s = ldc(A.lvl_sorted, A.level * A.level_cap + rank);
     I.h = hs / NSL;
     I.dv0 = (hs % NSL) * DVS;
@@ -645,14 +677,9 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
     float *s0buf = reinterpret_cast<float *>(smem + 2 * sizeof(ChunkBuf));
     if (ldc(A.header, H_STATUS) != FK_OK) return;
     // item ids: (segment rank, v-head, dv slice), slice fastest
-    Walk W;
-    W.nseg = ldc(A.header, H_LEVEL0 + A.level);
-    W.n_items = W.nseg * A.Hv * NSL;
-    W.G = gridDim.x;
-    W.runs = W.n_items >= 4 * W.G;
-    W.per = (W.n_items + W.G - 1) / W.G;
+    const Walk W = make_walk(ldc(A.header, H_LEVEL0 + A.level), A.Hv, A.Hk, gridDim.x, blockIdx.x);
     const int n_items = W.n_items;
-    const int b0 = item_id(W, blockIdx.x, 0);
+    const int b0 = item_id(W, 0);
     if (b0 >= n_items) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int G = lane >> 4, c16 = lane & 15;
@@ -670,11 +697,11 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
         // the item after the last one handed to a step, looked up one item
         // ahead so its (dependent) scalar loads are long done when it is used
         int la_k = 1;
-        int la_it = item_id(W, blockIdx.x, la_k);
+        int la_it = item_id(W, la_k);
         Item la = la_it < n_items ? item_at(A, W, la_it) : cur;
         auto take = [&](Item &I) {
             I = la;
-            la_it = item_id(W, blockIdx.x, ++la_k);
+            la_it = item_id(W, ++la_k);
             if (la_it < n_items) la = item_at(A, W, la_it);
         };
         // the entering state staged last (in item order): a sibling entering
@@ -750,7 +777,7 @@ __global__ void __launch_bounds__(CHUNK_THREADS) k_gdn_chunk(ChunkArgs A)
         const int dvc = cur.dv0 + wv * 16 + c16;   // this lane's state column (dv index)
         const bool last = c + 1 == item_nch(cur);
         // the next item's metadata, fetched while this step computes
-        const int next_it = item_id(W, blockIdx.x, ik + 1);
+        const int next_it = item_id(W, ik + 1);
         const bool more = !last || next_it < n_items;
         Item nxt = cur;
         Emits nE = E;
