@@ -49,12 +49,24 @@ __global__ void __launch_bounds__(256) k_kv_append(const E *__restrict__ k, cons
     }
 }
 
-// bf16, d = 128: 16-byte accesses on both sides.  Thread (r, c8) moves key
-// dims [8 c8, 8 c8 + 8) of slot r; values go through LDS ([slot][d], padded
-// rows) and leave as 8 consecutive slots of one dim row of the page.
+// bf16, d = 128: 16-byte accesses on both sides, HPB kv heads of one page
+// per block (a page's metadata is read once for all of them, and every
+// thread has 2 HPB loads in flight).  Thread (r, c8) moves key dims
+// [8 c8, 8 c8 + 8) of slot r; values go through LDS ([slot][d], padded rows)
+// and leave as 8 consecutive slots of one dim row of the page.  The stream's
+// keys and values are read once, so their loads are non-temporal.
 constexpr int KV_D = 128;
 constexpr int KV_VS = KV_D + 8;   // LDS row stride (bf16): slot rows on different banks
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_nt(const uint16_t *p)
+{
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
+template <int HPB>
 __global__ void __launch_bounds__(256) k_kv_append_bf16(const uint16_t *__restrict__ k,
                                                         const uint16_t *__restrict__ v, int Hkv,
                                                         const int32_t *__restrict__ header,
@@ -66,24 +78,31 @@ __global__ void __launch_bounds__(256) k_kv_append_bf16(const uint16_t *__restri
                                                         const int32_t *__restrict__ pages, uint16_t *__restrict__ kp,
                                                         uint16_t *__restrict__ vp)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t vt[FK_TILE_TOKENS * KV_VS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[HPB][FK_TILE_TOKENS * KV_VS];
     if (header[H_STATUS] != FK_OK) return;
-    const int tile = blockIdx.x, h = blockIdx.y;
+    const int tile = blockIdx.x, h0 = blockIdx.y * HPB;
     if (tile >= header[H_NTILES]) return;
     const int s = tile_seg[tile], row0 = tile_row0[tile];
     const int count = min(FK_TILE_TOKENS, seg_len[s] - row0);
     const int page = pages[page_off[s] + row0 / FK_TILE_TOKENS];
     const int t0 = seg_start[s] + row0;
-    const size_t page_base = ((size_t)page * Hkv + h) * (size_t)FK_TILE_TOKENS * KV_D;
+    const size_t page_base = ((size_t)page * Hkv + h0) * (size_t)FK_TILE_TOKENS * KV_D;
     const int r = threadIdx.x >> 4, c8 = threadIdx.x & 15;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (r < count) {
-        const size_t src = ((size_t)(t0 + r) * Hkv + h) * KV_D + c8 * 8;
-        kv = *reinterpret_cast<const uint4 *>(k + src);
-        vv = *reinterpret_cast<const uint4 *>(v + src);
+    uint4 kv[HPB], vv[HPB];
+#pragma unroll
+    for (int hh = 0; hh < HPB; ++hh) {
+        kv[hh] = vv[hh] = make_uint4(0, 0, 0, 0);
+        if (r < count) {
+            const size_t src = ((size_t)(t0 + r) * Hkv + h0 + hh) * KV_D + c8 * 8;
+            kv[hh] = load_nt(k + src);
+            vv[hh] = load_nt(v + src);
+        }
     }
-    *reinterpret_cast<uint4 *>(kp + page_base + r * KV_D + c8 * 8) = kv;
-    *reinterpret_cast<uint4 *>(vt + r * KV_VS + c8 * 8) = vv;
+#pragma unroll
+    for (int hh = 0; hh < HPB; ++hh) {
+        *reinterpret_cast<uint4 *>(kp + page_base + ((size_t)hh * FK_TILE_TOKENS + r) * KV_D + c8 * 8) = kv[hh];
+        *reinterpret_cast<uint4 *>(vt[hh] + r * KV_VS + c8 * 8) = vv[hh];
+    }
     __syncthreads();
     // dim x = tid / 2, slots [8 (tid % 2), +8).  The two lanes of a pair read
     // slot rows 8 apart (8 x 68 dwords: the same bank); the odd lane walks its
@@ -91,13 +110,17 @@ __global__ void __launch_bounds__(256) k_kv_append_bf16(const uint16_t *__restri
     // every read of a wave is free of bank conflicts, and swaps the halves of
     // its result back into slot order.
     const int x = threadIdx.x >> 1, odd = threadIdx.x & 1, r8 = odd * 8;
-    uint16_t e[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = vt[(r8 + ((j + 4 * odd) & 7)) * KV_VS + x];
-    const uint32_t p0 = e[0] | ((uint32_t)e[1] << 16), p1 = e[2] | ((uint32_t)e[3] << 16);
-    const uint32_t p2 = e[4] | ((uint32_t)e[5] << 16), p3 = e[6] | ((uint32_t)e[7] << 16);
-    const uint4 out = odd ? make_uint4(p2, p3, p0, p1) : make_uint4(p0, p1, p2, p3);
-    *reinterpret_cast<uint4 *>(vp + page_base + x * FK_TILE_TOKENS + r8) = out;
+    for (int hh = 0; hh < HPB; ++hh) {
+        uint16_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = vt[hh][(r8 + ((j + 4 * odd) & 7)) * KV_VS + x];
+        const uint32_t p0 = e[0] | ((uint32_t)e[1] << 16), p1 = e[2] | ((uint32_t)e[3] << 16);
+        const uint32_t p2 = e[4] | ((uint32_t)e[5] << 16), p3 = e[6] | ((uint32_t)e[7] << 16);
+        const uint4 out = odd ? make_uint4(p2, p3, p0, p1) : make_uint4(p0, p1, p2, p3);
+        *reinterpret_cast<uint4 *>(vp + page_base + (size_t)hh * FK_TILE_TOKENS * KV_D + x * FK_TILE_TOKENS + r8) =
+            out;
+    }
 }
 
 }  // namespace fk
@@ -113,11 +136,14 @@ int fk_launch_kv_append(const fk_tree_meta *meta, const void *k, const void *v, 
     const int32_t *hdr = ws_at<int32_t>(ws, L.header);
     const int32_t *ts = ws_at<int32_t>(ws, L.tile_seg), *tr = ws_at<int32_t>(ws, L.tile_row0);
     const int32_t *ss = ws_at<int32_t>(ws, L.seg_start), *sl = ws_at<int32_t>(ws, L.seg_len);
-    if (dtype == FK_BF16 && d == KV_D)
-        k_kv_append_bf16<<<grid, 256, 0, st>>>((const uint16_t *)k, (const uint16_t *)v, Hkv, hdr, ts, tr, ss, sl,
-                                               meta->seg_page_off, meta->seg_pages, (uint16_t *)k_pool,
-                                               (uint16_t *)v_pool);
-    else if (dtype == FK_BF16)
+    if (dtype == FK_BF16 && d == KV_D) {
+        // heads per block: 4, 2 or 1, whichever divides Hkv
+        const int hpb = Hkv % 4 == 0 ? 4 : Hkv % 2 == 0 ? 2 : 1;
+        dim3 g2((unsigned)L.tile_cap, (unsigned)(Hkv / hpb));
+        auto kern = hpb == 4 ? k_kv_append_bf16<4> : hpb == 2 ? k_kv_append_bf16<2> : k_kv_append_bf16<1>;
+        kern<<<g2, 256, 0, st>>>((const uint16_t *)k, (const uint16_t *)v, Hkv, hdr, ts, tr, ss, sl,
+                                 meta->seg_page_off, meta->seg_pages, (uint16_t *)k_pool, (uint16_t *)v_pool);
+    } else if (dtype == FK_BF16)
         k_kv_append<uint16_t><<<grid, 256, 0, st>>>((const uint16_t *)k, (const uint16_t *)v, Hkv, d, hdr, ts, tr,
                                                    ss, sl, meta->seg_page_off, meta->seg_pages,
                                                    (uint16_t *)k_pool, (uint16_t *)v_pool);
