@@ -248,41 +248,55 @@ __device__ __forceinline__ void block_compute(const uint16_t *kl, const uint16_t
                 sacc[mt][r] = vis ? sacc[mt][r] : -INFINITY;
             }
     }
-    // row max on raw scores (scale > 0); the two wave halves hold disjoint
-    // keys of the same row and swap maxima with one permlane
-    float mloc = sacc[0][0];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = (mt == 0 ? 1 : 0); r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[mt][r]);
-    const float mrow = pair_max(mloc) * scale_log2e;
-    // lazy rescale: a row moves its reference max only when the block's
-    // max exceeds it by more than RESCALE_LOG2 (the exponents then stay
-    // <= 2^RESCALE_LOG2); rows that do not move multiply by exactly 1
-    const bool need = mrow > m + RESCALE_LOG2;
-    if (__any(need)) {   // wave-uniform branch
-        const float mnew = need ? mrow : m;
-        const float corr = __builtin_amdgcn_exp2f(m - mnew);
-        l *= corr;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) o[i] *= corr;
-        m = mnew;
-    }
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    // exponentials against the row's current reference max m
+    float ps[4];
     bf16x8 pf[2 * MT];
+    auto exponentials = [&]() {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            float pv[8];
+            for (int hh = 0; hh < 2; ++hh) {
+                float pv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][hh * 8 + e], scale_log2e, -m));
-                ps[e & 3] += pv[e];
+                for (int e = 0; e < 8; ++e) {
+                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][hh * 8 + e], scale_log2e, -m));
+                    // the first four start the partial sums (exactly 0 + p)
+                    ps[e & 3] = (mt == 0 && hh == 0 && e < 4) ? pv[e] : ps[e & 3] + pv[e];
+                }
+                pf[mt * 2 + hh] = as_bf16x8(pack8(pv));
             }
-            pf[mt * 2 + hh] = as_bf16x8(pack8(pv));
+    };
+    exponentials();
+    float lblk = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    // lazy rescale: a row moves its reference max only when the block's max
+    // exceeds it by more than 2^RESCALE_LOG2 (the exponentials then stay
+    // <= 2^RESCALE_LOG2); rows that do not move multiply by exactly 1.  Such
+    // a row has an exponential above 2^(RESCALE_LOG2 - 1) in one half of the
+    // wave, so that lane's partial sum exceeds it too: only then is the
+    // block's row max taken, and the decision is the same as if it were
+    // always taken (a block that passes this test moves no row).
+    if (__any(!(lblk <= __builtin_exp2f(RESCALE_LOG2 - 1.f)))) {   // wave-uniform branch
+        // row max on raw scores (scale > 0); the two wave halves hold
+        // disjoint keys of the same row and swap maxima with one permlane
+        float mloc = sacc[0][0];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = (mt == 0 ? 1 : 0); r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[mt][r]);
+        const float mrow = pair_max(mloc) * scale_log2e;
+        const bool need = mrow > m + RESCALE_LOG2;
+        if (__any(need)) {   // wave-uniform branch
+            const float mnew = need ? mrow : m;
+            const float corr = __builtin_amdgcn_exp2f(m - mnew);
+            l *= corr;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) o[i] *= corr;
+            m = mnew;
+            exponentials();
+            lblk = (ps[0] + ps[1]) + (ps[2] + ps[3]);
         }
-    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
+    l += lblk;
     // O^T += V^T . P^T ; k-step kk covers keys 16*kk + [0, 16)
     {
         const uint16_t *vrow = vl + n * V_STRIDE + half * 8;
