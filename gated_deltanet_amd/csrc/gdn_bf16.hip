@@ -158,7 +158,11 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     float *am = reinterpret_cast<float *>(scr_all[w]), *lsh = lsh_all[w], *esh = esh_all[w];
     uint16_t *tb = reinterpret_cast<uint16_t *>(scr_all[w]);
     const int s = chunk_seg[c], r0 = chunk_row0[c];
-    const int n = valid ? min(C, seg_len[s] - r0) : 1;
+    const int n = __builtin_amdgcn_readfirstlane(valid ? min(C, seg_len[s] - r0) : 1);
+    // a chunk of at most 32 tokens needs only the top-left 32 x 32 blocks of
+    // T and P (the rest belongs to rows past its last token, never stored;
+    // the blocks it needs do not depend on them, so their bits are the same)
+    const bool shortc = n <= C / 2;
     const size_t t0 = (size_t)seg_start[s] + r0;
     const int g = h / (Hv / Hk);
     // operand fragments: rows 16*t + c16, dims 32*kk + 8*G .. +8 (zero past n);
@@ -174,7 +178,14 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     };
     bf16x8 kf[4][4], qc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) frag(k, t, kf[t]);
+    for (int t = 0; t < 4; ++t) {
+        if (t < 2 || !shortc) {
+            frag(k, t, kf[t]);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) kf[t][kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
+        }
+    }
     const int lr = lane < n ? lane : n - 1;
     float la = lane < n ? logf(a[(t0 + lr) * Hv + h]) : 0.f;
     const float eta = lane < n ? b[(t0 + lr) * Hv + h] : 0.f;
@@ -191,6 +202,7 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     uint16_t *pdst = pmat + ((size_t)c * Hv + h) * C * C;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
+        if (it >= 2 && shortc) continue;   // rows 32..63: none
         frag(q, it, qc);
         const int i = it * 16 + c16;
         const float li = lsh[i];
@@ -230,6 +242,10 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
 #pragma unroll
     for (int p = 0; p < 6; ++p) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (BI[p] >= 2 && shortc) {
+            aop[p] = acc;
+            continue;
+        }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[BK[p]][kk], kf[BI[p]][kk], acc);
         const int i = BI[p] * 16 + c16;
@@ -243,8 +259,9 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (bk < 2 || !shortc)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[bk][kk], kf[bk][kk], acc);
+            for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[bk][kk], kf[bk][kk], acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int ri = G * 4 + r, i = bk * 16 + ri, j = bk * 16 + c16;
@@ -289,11 +306,14 @@ k_gdn_prep(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const
     const f32x4 t00 = tB(0), t11 = tB(1), t22 = tB(2);
     const f32x4 a1 = tA(1), a2 = tA(2), a3 = tA(3);
     const f32x4 t10 = -mm(a1, mm(aop[0], t00, z), z);
-    const f32x4 t21 = -mm(a2, mm(aop[2], t11, z), z);
-    const f32x4 t32 = -mm(a3, mm(aop[5], t22, z), z);
-    const f32x4 t20 = -mm(a2, mm(aop[2], t10, mm(aop[1], t00, z)), z);
-    const f32x4 t31 = -mm(a3, mm(aop[5], t21, mm(aop[4], t11, z)), z);
-    const f32x4 t30 = -mm(a3, mm(aop[5], t20, mm(aop[4], t10, mm(aop[3], t00, z))), z);
+    f32x4 t21 = z, t32 = z, t20 = z, t31 = z, t30 = z;
+    if (!shortc) {
+        t21 = -mm(a2, mm(aop[2], t11, z), z);
+        t32 = -mm(a3, mm(aop[5], t22, z), z);
+        t20 = -mm(a2, mm(aop[2], t10, mm(aop[1], t00, z)), z);
+        t31 = -mm(a3, mm(aop[5], t21, mm(aop[4], t11, z)), z);
+        t30 = -mm(a3, mm(aop[5], t20, mm(aop[4], t10, mm(aop[3], t00, z))), z);
+    }
     __syncthreads();
     // (4) T as bf16 rows (the blocks above the diagonal are never read)
     auto tbw = [&](int row, int col, float v_) { tb[row * TBS + col] = __builtin_bit_cast(uint16_t, (__bf16)v_); };
