@@ -86,3 +86,20 @@ def test_attention_bf16_run_twice_bitwise():
     a1 = r.attention().clone()
     a2 = r.attention().clone()
     assert torch.equal(a1, a2)
+
+
+def test_attention_bf16_kv_head_counts():
+    """The K/V append moves 4, 2 or 1 kv heads of a page per block, whichever
+    divides the kv head count: odd and even counts page and attend alike."""
+    for seed, hkv in ((21, 1), (22, 3), (23, 6)):
+        sh = Shapes(8 * hkv, hkv, 128, 2, 4, 128, 128)
+        rng = np.random.default_rng(1000 + seed)
+        t = random_tree(rng, n_requests=3, p_cached_root=0.4, p_internal_fork=0.4, max_len=60)
+        t.flatten()
+        inp = draw_inputs(t, sh, 77 + seed, "bf16")
+        print(f"[attn bf16 kv heads] Hkv {hkv} T={t.T}", flush=True)
+        r = GpuRound(inp).build()
+        o = to_f64(r.attention())
+        assert r.status() == 0
+        mx, mean = _check(o, oracle_attention(inp))
+        assert mx <= MAX_ABS and mean <= MEAN_ABS, (hkv, mx, mean)
