@@ -53,6 +53,15 @@ constexpr int V_LDS = D * V_STRIDE;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// Read-only metadata read through the constant address space: with a uniform
+// index it stays a scalar load even where the compiler cannot prove that no
+// store in the loop aliases it (the block loads below are opaque to it), so
+// it never waits on the vector-memory counter the block loads use.
+__device__ __forceinline__ int ldc(const int32_t *p, int i)
+{
+    return ((const __attribute__((address_space(4))) int32_t *)p)[i];
+}
+
 // max / sum of a lane's value and that of lane (lane ^ 32): one permlane32
 // swap gives every lane both values (the two halves of a wave hold disjoint
 // keys of the same rows); the sum is commutative, so both halves agree
@@ -151,9 +160,10 @@ __device__ __forceinline__ void cursor_level(BlockCursor &c, int lvl, const Tile
 {
     c.lvl = lvl;
     c.own = lvl == t.depth;
-    c.count = c.own ? (RULE == TWO_WAY ? t.len : min(t.row0 + FK_TILE_TOKENS, t.len)) : t.seg_fork[t.anc[lvl + 1]];
-    c.plist = t.pages + t.page_off[t.anc[lvl]];
-    c.pdiff = t.pos0 - t.seg_pos0[t.anc[lvl]];
+    const int a = ldc(t.anc, lvl);
+    c.count = c.own ? (RULE == TWO_WAY ? t.len : min(t.row0 + FK_TILE_TOKENS, t.len)) : ldc(t.seg_fork, ldc(t.anc, lvl + 1));
+    c.plist = t.pages + ldc(t.page_off, a);
+    c.pdiff = t.pos0 - ldc(t.seg_pos0, a);
     c.key0 = 0;
     if (RULE == WINDOW) {
         const int lo = c.pdiff + t.row0 - t.window + 1;   // first key the tile's first row sees
@@ -208,22 +218,28 @@ __device__ __forceinline__ void store_rows(const f32x16 (&o)[D / 32], float l, b
 // when the block is not `full` for every row of the wave: hi / lo = last /
 // first visible key offset of the lane's row within the block, minus
 // 8 * half), online softmax with the per-row lazy rescale, O^T += V^T . P^T.
-template <int RULE>
-__device__ __forceinline__ void block_compute(const uint16_t *kl, const uint16_t *vl, const bf16x8 (&qf)[D / 16],
+// Where a lane's operands sit in a staged block (bf16 elements): K fragment
+// (key tile mt, k-step ks) at krow + mt * KMT + ks * KS, value fragment
+// (dim tile i, key step kk) at vrow + i * VI + kk * VKK.
+struct PaddedTiles {   // [key][K_STRIDE] and [dim][V_STRIDE] tiles written from registers
+    static constexpr int KS = 16, KMT = 32 * K_STRIDE, VI = 32 * V_STRIDE, VKK = 16;
+};
+
+template <int RULE, class LAY>
+__device__ __forceinline__ void block_compute(const uint16_t *krow, const uint16_t *vrow, const bf16x8 (&qf)[D / 16],
                                               f32x16 (&o)[D / 32], float &m, float &l, bool full, int hi, int lo,
-                                              int prow, int half, int n, float scale_log2e)
+                                              float scale_log2e)
 {
     // S^T = K . Q^T
     f32x16 sacc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
     {
-        const uint16_t *krow = kl + prow * K_STRIDE + half * 8;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + mt * 32 * K_STRIDE + ks * 16));
+                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + mt * LAY::KMT + ks * LAY::KS));
                 sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
             }
         // keep LOOKAHEAD operand reads in flight ahead of the MFMAs
@@ -299,15 +315,87 @@ __device__ __forceinline__ void block_compute(const uint16_t *kl, const uint16_t
     l += lblk;
     // O^T += V^T . P^T ; k-step kk covers keys 16*kk + [0, 16)
     {
-        const uint16_t *vrow = vl + n * V_STRIDE + half * 8;
 #pragma unroll
         for (int kk = 0; kk < 2 * MT; ++kk)
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) {
-                const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + i * 32 * V_STRIDE + kk * 16));
+                const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + i * LAY::VI + kk * LAY::VKK));
                 o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[i], 0, 0, 0);
             }
     }
+}
+
+// The full launch stages blocks in a ring of three LDS stages filled by
+// direct global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land
+// at M0 + 16 * lane), two blocks ahead of the one computed, so no register
+// holds a block in flight.  Stage layout (bf16 elements): K of the block's two
+// pages at [page][k-step 8][half 2][slot 16][8], V^T at 4096 + [page][dim tile
+// 4][half 2][dim 32][8].  A 16-lane read group then meets 16 distinct 16-byte
+// bank groups (keys: 16 slots; values: 16 dims), and each read of a lane is
+// its base plus an immediate offset.  The lane that fills 16-byte unit c of a
+// page region loads the unit of the page that belongs there (ring_k_off,
+// ring_v_off).
+struct RingTiles {
+    static constexpr int KS = 256, KMT = 0, VI = 512, VKK = 2048;
+};
+constexpr int RING = 3;                 // stages
+constexpr int STAGE = 2 * BN * D;       // bf16 elements per stage: K and V^T of one block
+static_assert(MT == 1 && BN == 2 * FK_TILE_TOKENS, "the ring layout holds two 16-key pages per block");
+
+// byte offsets inside a 4 KB K / V page of the 16 bytes lane `lane` of wave
+// `w` loads (see the stage layout above)
+__device__ __forceinline__ uint32_t ring_k_off(int w, int lane) { return (lane & 15) * 256 + (4 * w + (lane >> 4)) * 16; }
+__device__ __forceinline__ uint32_t ring_v_off(int w, int lane) { return (32 * w + (lane & 31)) * 32 + (lane >> 5) * 16; }
+
+__device__ __forceinline__ const uint16_t *uniform_ptr(const uint16_t *p)
+{
+    const uint64_t u = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (const uint16_t *)(((uint64_t)hi << 32) | lo);
+}
+
+// one 16-byte direct global->LDS load per lane: global address gbase + voff,
+// LDS address m0 + 16 * lane
+__device__ __forceinline__ void lds_dma16(const uint16_t *gbase, uint32_t voff, uint32_t m0)
+{
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(m0) : "memory");
+}
+
+// The two page ids of a block.  Pages past the range's last key repeat its
+// last page: those keys are masked, so their scores are -inf and their
+// weights exactly 0, and the repeated values are finite.
+struct BlockPages {
+    int p0, p1;
+};
+__device__ __forceinline__ BlockPages ring_pages(const int32_t *__restrict__ plist, int key0, int count)
+{
+    const int last = (count - 1) / FK_TILE_TOKENS, pi = key0 / FK_TILE_TOKENS;
+    return BlockPages{ldc(plist, min(pi, last)), ldc(plist, min(pi + 1, last))};
+}
+
+// Issue the four loads (K and V of the two pages) of one block into a stage;
+// every wave issues exactly four loads per block.
+__device__ __forceinline__ void ring_issue(uint32_t stage_bytes, const uint16_t *__restrict__ kp,
+                                           const uint16_t *__restrict__ vp, BlockPages pg, int g, int Hkv,
+                                           uint32_t koff, uint32_t voff, int w)
+{
+#pragma unroll
+    for (int p = 0; p < BN / FK_TILE_TOKENS; ++p) {
+        const size_t pb = ((size_t)(p ? pg.p1 : pg.p0) * Hkv + g) * (FK_TILE_TOKENS * D);
+        const uint32_t mk = __builtin_amdgcn_readfirstlane(stage_bytes + p * 4096 + w * 1024);
+        const uint32_t mv = __builtin_amdgcn_readfirstlane(stage_bytes + 8192 + p * 4096 + w * 1024);
+        lds_dma16(uniform_ptr(kp + pb), koff, mk);
+        lds_dma16(uniform_ptr(vp + pb), voff, mv);
+    }
+}
+
+// wait until at most N of this wave's loads are in flight, then meet the
+// work-group at a barrier (the loads are in-order, so the older block's
+// loads have landed in LDS)
+template <int N>
+__device__ __forceinline__ void ring_wait_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 template <int RULE>
@@ -321,8 +409,7 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             const int32_t *__restrict__ seg_anc, const int32_t *__restrict__ seg_fork,
             const int32_t *__restrict__ page_off, const int32_t *__restrict__ pages)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][K_LDS];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][V_LDS];
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[RING * STAGE];
     if (header[H_STATUS] != FK_OK) return;
     // heaviest tiles first (both kv heads of a tile side by side), so the
     // launch does not end on a long tile started late
@@ -359,6 +446,10 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     const int *anc = seg_anc + s * FK_MAX_DEPTH;
     // MFMA row m of a 32-key tile holds key perm(m): bits 2 and 3 swapped
     const int prow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+    const uint32_t koff = ring_k_off(w, lane), voff = ring_v_off(w, lane);
+    const uint32_t ring_bytes = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)ring;
+    const uint16_t *krow0 = ring + (n >> 4) * 2048 + half * 128 + (prow & 15) * 8;
+    const uint16_t *vrow0 = ring + 4096 + half * 256 + n * 8;
 
     TileCtx tc;
     tc.depth = depth;
@@ -374,18 +465,30 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     BlockCursor cur;
     cursor_level<RULE>(cur, 0, tc);
     cursor_settle<RULE>(cur, tc);
-    {
-        BlockRegs R;
-        load_block(R, kp, vp, cur.plist, cur.key0, cur.count, g, Hkv);
-        store_block(k_lds[0], v_lds[0], R);
-    }
-    __syncthreads();
-    for (int buf = 0;; buf ^= 1) {
-        // prefetch the next block into registers while this one is computed
-        BlockCursor nxt = cur;
-        const bool more = cursor_next<RULE>(nxt, tc);
-        BlockRegs R;
-        if (more) load_block(R, kp, vp, nxt.plist, nxt.key0, nxt.count, g, Hkv);
+    // blocks j and j+1 in flight before the walk starts, block j+2's page ids
+    // known: each iteration issues block j+2's loads right after its barrier
+    // and, after computing block j, finds block j+3 and reads its page ids --
+    // scalar loads that land while the wave waits at the next barrier, not
+    // while LDS operand reads (which share their wait counter) are in flight
+    ring_issue(ring_bytes, kp, vp, ring_pages(cur.plist, cur.key0, cur.count), g, Hkv, koff, voff, w);
+    BlockCursor nxt = cur;
+    bool more = cursor_next<RULE>(nxt, tc);
+    if (more) ring_issue(ring_bytes + STAGE * 2, kp, vp, ring_pages(nxt.plist, nxt.key0, nxt.count), g, Hkv, koff, voff, w);
+    BlockCursor nxt2 = nxt;
+    bool more2 = more && cursor_next<RULE>(nxt2, tc);
+    BlockPages pg2 = more2 ? ring_pages(nxt2.plist, nxt2.key0, nxt2.count) : BlockPages{0, 0};
+    // the query loads (and the first two blocks) complete here, so the
+    // compiler's own wait for them is not repeated inside the walk, where a
+    // full wait would also drain the block loads in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    for (int st = 0;;) {
+        // block j landed in every wave, and every wave is done with block j-1,
+        // whose stage block j+2 now takes
+        if (more)
+            ring_wait_barrier<4>();
+        else
+            ring_wait_barrier<0>();
+        if (more2) ring_issue(ring_bytes + (st == 0 ? 2 : st - 1) * (STAGE * 2), kp, vp, pg2, g, Hkv, koff, voff, w);
         {
             const int key0 = cur.key0, count = cur.count, pdiff = cur.pdiff;
             const bool own = cur.own;
@@ -399,12 +502,19 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             // a wave whose four tokens all lie past the segment's end (in the
             // segment's last tile) only helps stage the blocks
             if (wave_live)
-                block_compute<RULE>(k_lds[buf], v_lds[buf], qf, o, m, l, full, hi, lo, prow, half, n, scale_log2e);
+                block_compute<RULE, RingTiles>(krow0 + st * STAGE, vrow0 + st * STAGE, qf, o, m, l, full, hi, lo,
+                                               scale_log2e);
         }
         if (!more) break;
-        store_block(k_lds[buf ^ 1], v_lds[buf ^ 1], R);
+        BlockCursor nxt3 = nxt2;
+        const bool more3 = more2 && cursor_next<RULE>(nxt3, tc);
+        if (more3) pg2 = ring_pages(nxt3.plist, nxt3.key0, nxt3.count);
         cur = nxt;
-        __syncthreads();   // next block staged; this buffer free for reuse
+        nxt = nxt2;
+        nxt2 = nxt3;
+        more = more2;
+        more2 = more3;
+        st = st == 2 ? 0 : st + 1;
     }
     store_rows(o, l, row_valid, out + qrow * D, half);
 }
@@ -579,7 +689,8 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
             const bool full = __all(lane_full);
             const int hi = lim_r - 1 - key0 - half * 8;
             const int lo = (RULE == WINDOW ? lo_r - key0 : 0) - half * 8;
-            block_compute<RULE>(k_lds[buf], v_lds[buf], qf, o, m, l, full, hi, lo, prow, half, n, scale_log2e);
+            block_compute<RULE, PaddedTiles>(k_lds[buf] + prow * K_STRIDE + half * 8, v_lds[buf] + n * V_STRIDE + half * 8,
+                                             qf, o, m, l, full, hi, lo, scale_log2e);
         }
         if (!more) break;
         store_block(k_lds[buf ^ 1], v_lds[buf ^ 1], R);
