@@ -225,10 +225,16 @@ struct PaddedTiles {   // [key][K_STRIDE] and [dim][V_STRIDE] tiles written from
     static constexpr int KS = 16, KMT = 32 * K_STRIDE, VI = 32 * V_STRIDE, VKK = 16;
 };
 
-template <int RULE, class LAY>
+// `mid` runs once the score products are issued (the full launch issues a
+// later block's loads there, while the matrix cores work on this one).
+struct NoMid {
+    __device__ void operator()() const {}
+};
+
+template <int RULE, class LAY, class MID = NoMid>
 __device__ __forceinline__ void block_compute(const uint16_t *krow, const uint16_t *vrow, const bf16x8 (&qf)[D / 16],
                                               f32x16 (&o)[D / 32], float &m, float &l, bool full, int hi, int lo,
-                                              float scale_log2e)
+                                              float scale_log2e, const MID &mid = MID())
 {
     // S^T = K . Q^T
     f32x16 sacc[MT];
@@ -251,6 +257,7 @@ __device__ __forceinline__ void block_compute(const uint16_t *krow, const uint16
         }
         __builtin_amdgcn_sched_group_barrier(0x008, LOOKAHEAD, 0);
     }
+    mid();
     // mask: register r of tile mt holds key 32*mt + 16*(r/8) + 8*half + r%8
     // of the block; masked in place unless the block is `full`
     if (!full) {
@@ -488,7 +495,12 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             ring_wait_barrier<4>();
         else
             ring_wait_barrier<0>();
-        if (more2) ring_issue(ring_bytes + (st == 0 ? 2 : st - 1) * (STAGE * 2), kp, vp, pg2, g, Hkv, koff, voff, w);
+        // block j+2's loads are issued once this block's score products are
+        // (their issue can stall on the memory pipeline while those run)
+        const uint32_t st2_bytes = ring_bytes + (st == 0 ? 2 : st - 1) * (STAGE * 2);
+        auto issue_next = [&]() {
+            if (more2) ring_issue(st2_bytes, kp, vp, pg2, g, Hkv, koff, voff, w);
+        };
         {
             const int key0 = cur.key0, count = cur.count, pdiff = cur.pdiff;
             const bool own = cur.own;
@@ -503,7 +515,9 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             // segment's last tile) only helps stage the blocks
             if (wave_live)
                 block_compute<RULE, RingTiles>(krow0 + st * STAGE, vrow0 + st * STAGE, qf, o, m, l, full, hi, lo,
-                                               scale_log2e);
+                                               scale_log2e, issue_next);
+            else
+                issue_next();
         }
         if (!more) break;
         BlockCursor nxt3 = nxt2;
