@@ -376,23 +376,24 @@ struct BlockPages {
 };
 __device__ __forceinline__ BlockPages ring_pages(const int32_t *__restrict__ plist, int key0, int count)
 {
-    const int last = (count - 1) / FK_TILE_TOKENS, pi = key0 / FK_TILE_TOKENS;
+    // count >= 1 and key0 >= 0: shifts, not signed divisions
+    const int last = (int)((uint32_t)(count - 1) >> 4), pi = (int)((uint32_t)key0 >> 4);
+    static_assert(FK_TILE_TOKENS == 16, "page index by shift");
     return BlockPages{ldc(plist, min(pi, last)), ldc(plist, min(pi + 1, last))};
 }
 
 // Issue the four loads (K and V of the two pages) of one block into a stage;
-// every wave issues exactly four loads per block.
-__device__ __forceinline__ void ring_issue(uint32_t stage_bytes, const uint16_t *__restrict__ kp,
-                                           const uint16_t *__restrict__ vp, BlockPages pg, int g, int Hkv,
-                                           uint32_t koff, uint32_t voff, int w)
+// every wave issues exactly four loads per block.  kg / vg: the pools at this
+// kv head's first page (page p at + p * pstride elements); m0: the stage's
+// LDS byte address plus this wave's 1 KB quarter (all wave-uniform).
+__device__ __forceinline__ void ring_issue(uint32_t m0, const uint16_t *kg, const uint16_t *vg, BlockPages pg,
+                                           uint32_t pstride, uint32_t koff, uint32_t voff)
 {
 #pragma unroll
     for (int p = 0; p < BN / FK_TILE_TOKENS; ++p) {
-        const size_t pb = ((size_t)(p ? pg.p1 : pg.p0) * Hkv + g) * (FK_TILE_TOKENS * D);
-        const uint32_t mk = __builtin_amdgcn_readfirstlane(stage_bytes + p * 4096 + w * 1024);
-        const uint32_t mv = __builtin_amdgcn_readfirstlane(stage_bytes + 8192 + p * 4096 + w * 1024);
-        lds_dma16(uniform_ptr(kp + pb), koff, mk);
-        lds_dma16(uniform_ptr(vp + pb), voff, mv);
+        const size_t pb = (size_t)(uint32_t)(p ? pg.p1 : pg.p0) * pstride;
+        lds_dma16(kg + pb, koff, m0 + p * 4096);
+        lds_dma16(vg + pb, voff, m0 + 8192 + p * 4096);
     }
 }
 
@@ -430,7 +431,7 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     const int tok = row0 + w * 4 + n / 8;          // local token of this lane's row
     const int h = g * G + (n % 8);
     const bool row_valid = tok < len;
-    const bool wave_live = row0 + w * 4 < len;   // wave-uniform
+    const bool wave_live = __builtin_amdgcn_readfirstlane(row0 + w * 4 < len);   // wave-uniform
     const size_t t_glob = (size_t)seg_start[s] + tok;
     const size_t qrow = t_glob * Hq + h;
 
@@ -454,7 +455,12 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     // MFMA row m of a 32-key tile holds key perm(m): bits 2 and 3 swapped
     const int prow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
     const uint32_t koff = ring_k_off(w, lane), voff = ring_v_off(w, lane);
-    const uint32_t ring_bytes = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)ring;
+    // this wave's quarter of stage 0 (LDS bytes), and the pools at head g
+    const uint32_t ring_bytes =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)ring + w * 1024);
+    const uint16_t *kg = uniform_ptr(kp + (size_t)g * (FK_TILE_TOKENS * D));
+    const uint16_t *vg = uniform_ptr(vp + (size_t)g * (FK_TILE_TOKENS * D));
+    const uint32_t pstride = (uint32_t)Hkv * (FK_TILE_TOKENS * D);
     const uint16_t *krow0 = ring + (n >> 4) * 2048 + half * 128 + (prow & 15) * 8;
     const uint16_t *vrow0 = ring + 4096 + half * 256 + n * 8;
 
@@ -477,10 +483,10 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     // and, after computing block j, finds block j+3 and reads its page ids --
     // scalar loads that land while the wave waits at the next barrier, not
     // while LDS operand reads (which share their wait counter) are in flight
-    ring_issue(ring_bytes, kp, vp, ring_pages(cur.plist, cur.key0, cur.count), g, Hkv, koff, voff, w);
+    ring_issue(ring_bytes, kg, vg, ring_pages(cur.plist, cur.key0, cur.count), pstride, koff, voff);
     BlockCursor nxt = cur;
     bool more = cursor_next<RULE>(nxt, tc);
-    if (more) ring_issue(ring_bytes + STAGE * 2, kp, vp, ring_pages(nxt.plist, nxt.key0, nxt.count), g, Hkv, koff, voff, w);
+    if (more) ring_issue(ring_bytes + STAGE * 2, kg, vg, ring_pages(nxt.plist, nxt.key0, nxt.count), pstride, koff, voff);
     BlockCursor nxt2 = nxt;
     bool more2 = more && cursor_next<RULE>(nxt2, tc);
     BlockPages pg2 = more2 ? ring_pages(nxt2.plist, nxt2.key0, nxt2.count) : BlockPages{0, 0};
@@ -499,7 +505,7 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
         // (their issue can stall on the memory pipeline while those run)
         const uint32_t st2_bytes = ring_bytes + (st == 0 ? 2 : st - 1) * (STAGE * 2);
         auto issue_next = [&]() {
-            if (more2) ring_issue(st2_bytes, kp, vp, pg2, g, Hkv, koff, voff, w);
+            if (more2) ring_issue(st2_bytes, kg, vg, pg2, pstride, koff, voff);
         };
         {
             const int key0 = cur.key0, count = cur.count, pdiff = cur.pdiff;
