@@ -14,16 +14,18 @@
 //
 // Tiles: a work-group of 4 waves computes a 128 (n) x 128 (m) block of y^T
 // = w x^T with v_mfma_f32_32x32x16_bf16 (A = rows of w, B = rows of x; each
-// wave a 64 x 64 quarter, 2 x 2 products), k in steps of 64 through a
-// double-buffered LDS tile (32 KB per stage), the next step's global loads in
-// registers under the current step's products.  A lane's accumulator then
-// holds 4 consecutive output features of one row: 8-byte stores.  LDS rows
-// are 128 bytes, their 16-byte units XOR-swizzled by bits 1-3 of the row, so
-// the operand reads (16 lanes: 16 rows, one unit) and the row writes (8 lanes:
-// one row) are free of bank conflicts.  Tiles are dealt to the eight XCDs in
-// contiguous ranges of row blocks, and within an XCD in groups of GM row
-// blocks (row block fastest), so blocks that run together share their x and
-// w tiles in that XCD's L2.
+// wave a 64 x 64 quarter, 2 x 2 products), k in steps of 32 through a ring of
+// three LDS stages (16 KB each: the w and x tiles of one step) filled by
+// direct global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes
+// land at M0 + 16 * lane) two steps ahead, so no register holds a tile in
+// flight and three work-groups share a CU.  LDS rows are 64 bytes, their four
+// 16-byte units XOR-swizzled by bits 2-3 of the row, so the operand reads
+// (16 lanes: 16 rows, one unit) are free of bank conflicts; the lane that
+// fills unit u of row r loads the unit that belongs there.  A lane's
+// accumulator holds 4 consecutive output features of one row: 8-byte stores.
+// Tiles are dealt to the eight XCDs in contiguous ranges of row blocks, and
+// within an XCD in groups of GM row blocks (row block fastest), so blocks
+// that run together share their x and w tiles in that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include "fk_common.h"
@@ -34,13 +36,30 @@ namespace proj {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int K_MULT = 64;      // K must be a multiple of this (the documented contract)
 constexpr int THREADS = 256;
 constexpr int TILE = BM * BK;   // bf16 elements of one operand tile in LDS
+constexpr int RING = 3;         // stages
+constexpr int STAGE = 2 * TILE; // w tile, then x tile
 constexpr int GM = 8;           // row blocks per group within an XCD
 constexpr int XCDS = 8;
 
-__device__ __forceinline__ int swz(int row, int unit) { return row * BK + ((unit ^ ((row >> 1) & 7)) << 3); }
+__device__ __forceinline__ int swz_unit(int row, int unit) { return unit ^ ((row >> 2) & 3); }
+__device__ __forceinline__ int swz(int row, int unit) { return row * BK + (swz_unit(row, unit) << 3); }
+
+// one 16-byte direct global->LDS load per lane: global address g (per lane),
+// LDS address m0 + 16 * lane
+__device__ __forceinline__ void lds_dma16(const uint16_t *g, uint32_t m0)
+{
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 struct Args {
     const uint16_t *x, *w;
@@ -69,43 +88,40 @@ __device__ __forceinline__ bool tile_of(const Args &A, int b, int &mb, int &nb)
     return true;
 }
 
-__global__ void __launch_bounds__(THREADS, 2) k_proj_bf16(Args A)
+__global__ void __launch_bounds__(THREADS, 3) k_proj_bf16(Args A)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lw[2][TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t lx[2][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[RING * STAGE];
     int mb, nb;
     if (!tile_of(A, blockIdx.x, mb, nb)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wn = w & 1, wm = w >> 1, half = lane >> 5, c32 = lane & 31;
     const int m0 = mb * BM, n0 = nb * BN;
 
-    // loader: thread t moves unit t % 8 of rows t / 8 + 32 i (i < 4) of both tiles
-    const int lunit = tid & 7, lrow = tid >> 3;
-    const uint16_t *wsrc[4];
-    const uint16_t *xsrc[4];
+    // loads: wave w fills rows 32 w .. 32 w + 31 of both tiles, 16 rows (1 KB)
+    // an instruction; lane l: row 32 w + 16 i + l / 4, LDS unit l % 4
+    const uint16_t *wsrc[2], *xsrc[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = lrow + 32 * i;
-        wsrc[i] = A.w + (size_t)(n0 + r) * A.K + lunit * 8;
+    for (int i = 0; i < 2; ++i) {
+        const int r = 32 * w + 16 * i + (lane >> 2), u = swz_unit(r, lane & 3);
+        wsrc[i] = A.w + (size_t)(n0 + r) * A.K + u * 8;
+        // a row past M, or an unused index entry, reads row 0 of x: that
+        // output row is never stored, and no other row uses it
         const int m = m0 + r;
         int src = -1;
         if (m < A.M) src = A.rows ? A.rows[m] : m;
-        xsrc[i] = (src >= 0 && src < A.Mx) ? A.x + (size_t)src * A.K + lunit * 8 : nullptr;
+        if (src < 0 || src >= A.Mx) src = 0;
+        xsrc[i] = A.x + (size_t)src * A.K + u * 8;
     }
-    uint4 rw[4], rx[4];
-    auto load = [&](int k0) {
+    const uint32_t ring_bytes = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)ring + w * 32 * BK * 2);
+    // stage s of k-step kt: w tile, then x tile (four loads a wave)
+    auto issue = [&](int kt, int s) {
+        const int k0 = kt * BK;
+        const uint32_t m = ring_bytes + s * (STAGE * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rw[i] = *reinterpret_cast<const uint4 *>(wsrc[i] + k0);
-            rx[i] = xsrc[i] ? *reinterpret_cast<const uint4 *>(xsrc[i] + k0) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int off = swz(lrow + 32 * i, lunit);
-            *reinterpret_cast<uint4 *>(&lw[buf][off]) = rw[i];
-            *reinterpret_cast<uint4 *>(&lx[buf][off]) = rx[i];
+        for (int i = 0; i < 2; ++i) {
+            lds_dma16(wsrc[i] + k0, m + i * 1024);
+            lds_dma16(xsrc[i] + k0, m + TILE * 2 + i * 1024);
         }
     };
 
@@ -115,14 +131,19 @@ __global__ void __launch_bounds__(THREADS, 2) k_proj_bf16(Args A)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    const int nk = A.K / BK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) load((kt + 1) * BK);
+    const int nk = A.K / BK;   // >= 2
+    issue(0, 0);
+    issue(1, 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the index reads and the first stages
+    for (int kt = 0, s = 0; kt < nk; ++kt) {
+        // step kt landed in every wave; every wave is done with step kt-1,
+        // whose stage step kt+2 now takes (the loads complete in order)
+        if (kt + 1 < nk)
+            wait_barrier<4>();
+        else
+            wait_barrier<0>();
+        const uint16_t *lw = ring + s * STAGE, *lx = lw + TILE;
+        const int s2 = s == 0 ? 2 : s - 1;   // (s + 2) % 3
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int unit = ks * 2 + half;
@@ -130,18 +151,19 @@ __global__ void __launch_bounds__(THREADS, 2) k_proj_bf16(Args A)
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                                                      &lw[buf][swz(wn * 64 + i * 32 + c32, unit)]));
+                                                      &lw[swz(wn * 64 + i * 32 + c32, unit)]));
                 b[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                                                      &lx[buf][swz(wm * 64 + i * 32 + c32, unit)]));
+                                                      &lx[swz(wm * 64 + i * 32 + c32, unit)]));
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            // step kt+2's loads go out once the first products are issued
+            if (ks == 0 && kt + 2 < nk) issue(kt + 2, s2);
         }
-        if (more) store(buf ^ 1);
-        __syncthreads();
+        s = s == 2 ? 0 : s + 1;
     }
     // y^T tile: lane holds row m = .. + c32 and features 8 (r / 4) + 4 half + r % 4
 #pragma unroll
@@ -175,7 +197,7 @@ extern "C" int fk_proj_gemm(const void *x, int32_t Mx, const int32_t *rows, int3
 {
     if (dtype != FK_BF16) return FK_E_UNSUPPORTED;
     if (M < 0 || Mx < 0 || K <= 0 || N <= 0) return FK_E_INVALID_ARG;
-    if (K % proj::BK || N % proj::BN) return FK_E_UNSUPPORTED;
+    if (K % proj::K_MULT || N % proj::BN) return FK_E_UNSUPPORTED;
     if (!rows && M > Mx) return FK_E_INVALID_ARG;
     if (M == 0) return FK_OK;
     if (!x || !w || !y) return FK_E_INVALID_ARG;
