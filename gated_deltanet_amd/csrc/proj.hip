@@ -39,11 +39,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int K_MULT = 64;      // K must be a multiple of this (the documented contract)
 constexpr int THREADS = 256;
-constexpr int TILE = BM * BK;   // bf16 elements of one operand tile in LDS
 constexpr int RING = 3;         // stages
-constexpr int STAGE = 2 * TILE; // w tile, then x tile
 constexpr int GM = 8;           // row blocks per group within an XCD
 constexpr int XCDS = 8;
+// NF: 32-feature fragments per wave (2: 128 x 128 blocks, three work-groups a
+// CU; 4: 256 features x 128 rows, two work-groups a CU and half the LDS
+// operand bytes per product, used when N is a multiple of 256)
+template <int NF>
+struct Shape {
+    static constexpr int BNW = 64 * NF;            // features per work-group
+    static constexpr int WT = BNW * BK, XT = BM * BK;   // bf16 elements of the w / x tiles
+    static constexpr int STAGE = WT + XT;
+    static constexpr int OCC = NF == 2 ? 3 : 2;     // work-groups a CU
+};
 
 __device__ __forceinline__ int swz_unit(int row, int unit) { return unit ^ ((row >> 2) & 3); }
 __device__ __forceinline__ int swz(int row, int unit) { return row * BK + (swz_unit(row, unit) << 3); }
@@ -88,22 +96,28 @@ __device__ __forceinline__ bool tile_of(const Args &A, int b, int &mb, int &nb)
     return true;
 }
 
-__global__ void __launch_bounds__(THREADS, 3) k_proj_bf16(Args A)
+template <int NF>
+__global__ void __launch_bounds__(THREADS, Shape<NF>::OCC) k_proj_bf16(Args A)
 {
-    __shared__ __attribute__((aligned(1024))) uint16_t ring[RING * STAGE];
+    using SH = Shape<NF>;
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[RING * SH::STAGE];
     int mb, nb;
     if (!tile_of(A, blockIdx.x, mb, nb)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wn = w & 1, wm = w >> 1, half = lane >> 5, c32 = lane & 31;
-    const int m0 = mb * BM, n0 = nb * BN;
+    const int m0 = mb * BM, n0 = nb * SH::BNW;
 
-    // loads: wave w fills rows 32 w .. 32 w + 31 of both tiles, 16 rows (1 KB)
-    // an instruction; lane l: row 32 w + 16 i + l / 4, LDS unit l % 4
-    const uint16_t *wsrc[2], *xsrc[2];
+    // loads, 16 rows (1 KB) an instruction, lane l: row r0 + l / 4, LDS unit
+    // l % 4.  Wave w fills w rows 16 NF w .. +16 NF and x rows 32 w .. +32.
+    const uint16_t *wsrc[NF / 2 * 2], *xsrc[2];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        const int r = 16 * NF * w + 16 * i + (lane >> 2), u = swz_unit(r, lane & 3);
+        wsrc[i] = A.w + (size_t)(n0 + r) * A.K + u * 8;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int r = 32 * w + 16 * i + (lane >> 2), u = swz_unit(r, lane & 3);
-        wsrc[i] = A.w + (size_t)(n0 + r) * A.K + u * 8;
         // a row past M, or an unused index entry, reads row 0 of x: that
         // output row is never stored, and no other row uses it
         const int m = m0 + r;
@@ -112,22 +126,22 @@ __global__ void __launch_bounds__(THREADS, 3) k_proj_bf16(Args A)
         if (src < 0 || src >= A.Mx) src = 0;
         xsrc[i] = A.x + (size_t)src * A.K + u * 8;
     }
-    const uint32_t ring_bytes = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)ring + w * 32 * BK * 2);
-    // stage s of k-step kt: w tile, then x tile (four loads a wave)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)ring;
+    const uint32_t wq = __builtin_amdgcn_readfirstlane(lds0 + w * 16 * NF * BK * 2);
+    const uint32_t xq = __builtin_amdgcn_readfirstlane(lds0 + SH::WT * 2 + w * 32 * BK * 2);
+    // stage s of k-step kt: w tile, then x tile (NF + 2 loads a wave)
     auto issue = [&](int kt, int s) {
         const int k0 = kt * BK;
-        const uint32_t m = ring_bytes + s * (STAGE * 2);
+        const uint32_t so = s * (SH::STAGE * 2);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            lds_dma16(wsrc[i] + k0, m + i * 1024);
-            lds_dma16(xsrc[i] + k0, m + TILE * 2 + i * 1024);
-        }
+        for (int i = 0; i < NF; ++i) lds_dma16(wsrc[i] + k0, wq + so + i * 1024);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + k0, xq + so + i * 1024);
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[NF][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NF; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
@@ -139,24 +153,25 @@ __global__ void __launch_bounds__(THREADS, 3) k_proj_bf16(Args A)
         // step kt landed in every wave; every wave is done with step kt-1,
         // whose stage step kt+2 now takes (the loads complete in order)
         if (kt + 1 < nk)
-            wait_barrier<4>();
+            wait_barrier<NF + 2>();
         else
             wait_barrier<0>();
-        const uint16_t *lw = ring + s * STAGE, *lx = lw + TILE;
+        const uint16_t *lw = ring + s * SH::STAGE, *lx = lw + SH::WT;
         const int s2 = s == 0 ? 2 : s - 1;   // (s + 2) % 3
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int unit = ks * 2 + half;
-            bf16x8 a[2], b[2];
+            bf16x8 a[NF], b[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < NF; ++i)
                 a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                                                      &lw[swz(wn * 64 + i * 32 + c32, unit)]));
-                b[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                                                      &lx[swz(wm * 64 + i * 32 + c32, unit)]));
-            }
+                                                      &lw[swz(wn * 32 * NF + i * 32 + c32, unit)]));
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j)
+                b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
+                                                      &lx[swz(wm * 64 + j * 32 + c32, unit)]));
+#pragma unroll
+            for (int i = 0; i < NF; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -174,9 +189,9 @@ __global__ void __launch_bounds__(THREADS, 3) k_proj_bf16(Args A)
             const int src = A.rows[m];
             if (src < 0 || src >= A.Mx) continue;
         }
-        uint16_t *yrow = A.y + (size_t)m * A.N + n0 + wn * 64;
+        uint16_t *yrow = A.y + (size_t)m * A.N + n0 + wn * 32 * NF;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NF; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 uint2 p;
@@ -211,10 +226,14 @@ extern "C" int fk_proj_gemm(const void *x, int32_t Mx, const int32_t *rows, int3
     A.K = K;
     A.N = N;
     A.mt = (M + proj::BM - 1) / proj::BM;
-    A.nt = N / proj::BN;
+    const bool wide = N % 256 == 0;
+    A.nt = N / (wide ? proj::Shape<4>::BNW : proj::Shape<2>::BNW);
     const int m_per = (A.mt + proj::XCDS - 1) / proj::XCDS;
     const int64_t blocks = (int64_t)proj::XCDS * m_per * A.nt;
     if (blocks > INT32_MAX) return FK_E_UNSUPPORTED;
-    proj::k_proj_bf16<<<dim3((unsigned)blocks), proj::THREADS, 0, (hipStream_t)stream>>>(A);
+    if (wide)
+        proj::k_proj_bf16<4><<<dim3((unsigned)blocks), proj::THREADS, 0, (hipStream_t)stream>>>(A);
+    else
+        proj::k_proj_bf16<2><<<dim3((unsigned)blocks), proj::THREADS, 0, (hipStream_t)stream>>>(A);
     return launch_status();
 }
