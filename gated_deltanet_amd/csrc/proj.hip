@@ -38,19 +38,23 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int K_MULT = 64;      // K must be a multiple of this (the documented contract)
-constexpr int THREADS = 256;
+#ifndef PROJ_WM
+#define PROJ_WM 4
+#endif
 constexpr int RING = 3;         // stages
 constexpr int GM = 8;           // row blocks per group within an XCD
 constexpr int XCDS = 8;
 // NF: 32-feature fragments per wave (2: 128 x 128 blocks, three work-groups a
 // CU; 4: 256 features x 128 rows, two work-groups a CU and half the LDS
 // operand bytes per product, used when N is a multiple of 256)
-template <int NF>
+template <int NF, int WM>   // WM: waves along the rows (64 rows each)
 struct Shape {
     static constexpr int BNW = 64 * NF;            // features per work-group
-    static constexpr int WT = BNW * BK, XT = BM * BK;   // bf16 elements of the w / x tiles
+    static constexpr int BMW = 64 * WM;            // rows per work-group
+    static constexpr int NT = 128 * WM;            // threads (2 x WM waves)
+    static constexpr int WT = BNW * BK, XT = BMW * BK;   // bf16 elements of the w / x tiles
     static constexpr int STAGE = WT + XT;
-    static constexpr int OCC = NF == 2 ? 3 : 2;     // work-groups a CU
+    static constexpr int OCC = NF == 2 ? 3 : (WM == 2 ? 2 : 1);   // work-groups a CU
 };
 
 __device__ __forceinline__ int swz_unit(int row, int unit) { return unit ^ ((row >> 2) & 3); }
@@ -96,23 +100,24 @@ __device__ __forceinline__ bool tile_of(const Args &A, int b, int &mb, int &nb)
     return true;
 }
 
-template <int NF>
-__global__ void __launch_bounds__(THREADS, Shape<NF>::OCC) k_proj_bf16(Args A)
+template <int NF, int WM>
+__global__ void __launch_bounds__((Shape<NF, WM>::NT), (Shape<NF, WM>::OCC)) k_proj_bf16(Args A)
 {
-    using SH = Shape<NF>;
+    using SH = Shape<NF, WM>;
     __shared__ __attribute__((aligned(1024))) uint16_t ring[RING * SH::STAGE];
     int mb, nb;
     if (!tile_of(A, blockIdx.x, mb, nb)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wn = w & 1, wm = w >> 1, half = lane >> 5, c32 = lane & 31;
-    const int m0 = mb * BM, n0 = nb * SH::BNW;
+    const int m0 = mb * SH::BMW, n0 = nb * SH::BNW;
+    constexpr int WF = NF * 2 / WM;   // w loads a wave: 16-row pieces of the w tile
 
     // loads, 16 rows (1 KB) an instruction, lane l: row r0 + l / 4, LDS unit
-    // l % 4.  Wave w fills w rows 16 NF w .. +16 NF and x rows 32 w .. +32.
-    const uint16_t *wsrc[NF / 2 * 2], *xsrc[2];
+    // l % 4.  Wave w fills w rows 16 WF w .. +16 WF and x rows 32 w .. +32.
+    const uint16_t *wsrc[WF], *xsrc[2];
 #pragma unroll
-    for (int i = 0; i < NF; ++i) {
-        const int r = 16 * NF * w + 16 * i + (lane >> 2), u = swz_unit(r, lane & 3);
+    for (int i = 0; i < WF; ++i) {
+        const int r = 16 * WF * w + 16 * i + (lane >> 2), u = swz_unit(r, lane & 3);
         wsrc[i] = A.w + (size_t)(n0 + r) * A.K + u * 8;
     }
 #pragma unroll
@@ -127,14 +132,14 @@ __global__ void __launch_bounds__(THREADS, Shape<NF>::OCC) k_proj_bf16(Args A)
         xsrc[i] = A.x + (size_t)src * A.K + u * 8;
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)ring;
-    const uint32_t wq = __builtin_amdgcn_readfirstlane(lds0 + w * 16 * NF * BK * 2);
+    const uint32_t wq = __builtin_amdgcn_readfirstlane(lds0 + w * 16 * WF * BK * 2);
     const uint32_t xq = __builtin_amdgcn_readfirstlane(lds0 + SH::WT * 2 + w * 32 * BK * 2);
-    // stage s of k-step kt: w tile, then x tile (NF + 2 loads a wave)
+    // stage s of k-step kt: w tile, then x tile (WF + 2 loads a wave)
     auto issue = [&](int kt, int s) {
         const int k0 = kt * BK;
         const uint32_t so = s * (SH::STAGE * 2);
 #pragma unroll
-        for (int i = 0; i < NF; ++i) lds_dma16(wsrc[i] + k0, wq + so + i * 1024);
+        for (int i = 0; i < WF; ++i) lds_dma16(wsrc[i] + k0, wq + so + i * 1024);
 #pragma unroll
         for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + k0, xq + so + i * 1024);
     };
@@ -153,7 +158,7 @@ __global__ void __launch_bounds__(THREADS, Shape<NF>::OCC) k_proj_bf16(Args A)
         // step kt landed in every wave; every wave is done with step kt-1,
         // whose stage step kt+2 now takes (the loads complete in order)
         if (kt + 1 < nk)
-            wait_barrier<NF + 2>();
+            wait_barrier<WF + 2>();
         else
             wait_barrier<0>();
         const uint16_t *lw = ring + s * SH::STAGE, *lx = lw + SH::WT;
@@ -225,15 +230,17 @@ extern "C" int fk_proj_gemm(const void *x, int32_t Mx, const int32_t *rows, int3
     A.Mx = Mx;
     A.K = K;
     A.N = N;
-    A.mt = (M + proj::BM - 1) / proj::BM;
     const bool wide = N % 256 == 0;
-    A.nt = N / (wide ? proj::Shape<4>::BNW : proj::Shape<2>::BNW);
+    using S2 = proj::Shape<2, 2>;
+    using S4 = proj::Shape<4, PROJ_WM>;
+    A.mt = (M + (wide ? S4::BMW : S2::BMW) - 1) / (wide ? S4::BMW : S2::BMW);
+    A.nt = N / (wide ? S4::BNW : S2::BNW);
     const int m_per = (A.mt + proj::XCDS - 1) / proj::XCDS;
     const int64_t blocks = (int64_t)proj::XCDS * m_per * A.nt;
     if (blocks > INT32_MAX) return FK_E_UNSUPPORTED;
     if (wide)
-        proj::k_proj_bf16<4><<<dim3((unsigned)blocks), proj::THREADS, 0, (hipStream_t)stream>>>(A);
+        proj::k_proj_bf16<4, PROJ_WM><<<dim3((unsigned)blocks), S4::NT, 0, (hipStream_t)stream>>>(A);
     else
-        proj::k_proj_bf16<2><<<dim3((unsigned)blocks), proj::THREADS, 0, (hipStream_t)stream>>>(A);
+        proj::k_proj_bf16<2, 2><<<dim3((unsigned)blocks), S2::NT, 0, (hipStream_t)stream>>>(A);
     return launch_status();
 }
