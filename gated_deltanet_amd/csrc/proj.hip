@@ -12,17 +12,20 @@
 // k ascending, always by one work-group (no split of k, no choice that depends
 // on M), so its bits depend only on its own row of x and column of w.
 //
-// Tiles: a work-group of 4 waves computes a 128 (n) x 128 (m) block of y^T
-// = w x^T with v_mfma_f32_32x32x16_bf16 (A = rows of w, B = rows of x; each
-// wave a 64 x 64 quarter, 2 x 2 products), k in steps of 32 through a ring of
-// three LDS stages (16 KB each: the w and x tiles of one step) filled by
-// direct global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes
+// Tiles: waves compute 32-row x 32-feature products of y^T = w x^T with
+// v_mfma_f32_32x32x16_bf16 (A = rows of w, B = rows of x), k in steps of 32
+// through a ring of three LDS stages (the w and x tiles of one step) filled
+// by direct global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes
 // land at M0 + 16 * lane) two steps ahead, so no register holds a tile in
-// flight and three work-groups share a CU.  LDS rows are 64 bytes, their four
-// 16-byte units XOR-swizzled by bits 2-3 of the row, so the operand reads
-// (16 lanes: 16 rows, one unit) are free of bank conflicts; the lane that
-// fills unit u of row r loads the unit that belongs there.  A lane's
-// accumulator holds 4 consecutive output features of one row: 8-byte stores.
+// flight.  When N is a multiple of 256 a work-group of eight waves computes a
+// 256-feature x 256-row block (a wave 128 x 64: four w and two x fragments
+// per k-step for eight products; 96 KB, one work-group a CU); otherwise four
+// waves compute 128 x 128 (a wave 64 x 64; 48 KB, three a CU).  LDS rows are
+// 64 bytes, their four 16-byte units XOR-swizzled by bits 2-3 of the row, so
+// the operand reads (16 lanes: 16 rows, one unit) are free of bank
+// conflicts; the lane that fills unit u of row r loads the unit that belongs
+// there.  A lane's accumulator holds 4 consecutive output features of one
+// row: 8-byte stores.
 // Tiles are dealt to the eight XCDs in contiguous ranges of row blocks, and
 // within an XCD in groups of GM row blocks (row block fastest), so blocks
 // that run together share their x and w tiles in that XCD's L2.
@@ -38,9 +41,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int K_MULT = 64;      // K must be a multiple of this (the documented contract)
-#ifndef PROJ_WM
-#define PROJ_WM 4
-#endif
+constexpr int WIDE_WM = 4;      // waves along the rows of the 256-feature blocks
 constexpr int RING = 3;         // stages
 constexpr int GM = 8;           // row blocks per group within an XCD
 constexpr int XCDS = 8;
@@ -232,14 +233,14 @@ extern "C" int fk_proj_gemm(const void *x, int32_t Mx, const int32_t *rows, int3
     A.N = N;
     const bool wide = N % 256 == 0;
     using S2 = proj::Shape<2, 2>;
-    using S4 = proj::Shape<4, PROJ_WM>;
+    using S4 = proj::Shape<4, proj::WIDE_WM>;
     A.mt = (M + (wide ? S4::BMW : S2::BMW) - 1) / (wide ? S4::BMW : S2::BMW);
     A.nt = N / (wide ? S4::BNW : S2::BNW);
     const int m_per = (A.mt + proj::XCDS - 1) / proj::XCDS;
     const int64_t blocks = (int64_t)proj::XCDS * m_per * A.nt;
     if (blocks > INT32_MAX) return FK_E_UNSUPPORTED;
     if (wide)
-        proj::k_proj_bf16<4, PROJ_WM><<<dim3((unsigned)blocks), S4::NT, 0, (hipStream_t)stream>>>(A);
+        proj::k_proj_bf16<4, proj::WIDE_WM><<<dim3((unsigned)blocks), S4::NT, 0, (hipStream_t)stream>>>(A);
     else
         proj::k_proj_bf16<2, 2><<<dim3((unsigned)blocks), S2::NT, 0, (hipStream_t)stream>>>(A);
     return launch_status();
