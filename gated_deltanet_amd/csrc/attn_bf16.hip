@@ -419,8 +419,10 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
 {
     __shared__ __attribute__((aligned(1024))) uint16_t ring[RING * STAGE];
     if (header[H_STATUS] != FK_OK) return;
-    // heaviest tiles first (both kv heads of a tile side by side), so the
-    // launch does not end on a long tile started late
+    // tiles in the builder's order -- heaviest first by band of work, a
+    // request's tiles together within a band -- the kv heads of a tile side
+    // by side (so with work-groups dealt to the XCDs in turn, an XCD sees one
+    // kv head's tiles of a few requests at a time)
     const int rank = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int half = lane >> 5, n = lane & 31;

@@ -21,8 +21,10 @@ enum HeaderSlot {
     H_NFORKS = 2,       // distinct fork points (GDN fork-state slots used)
     H_NCHUNKS = 3,      // GDN chunks in chunk_seg / chunk_row0
     H_LEVEL0 = 4,       // live segments per level: H_LEVEL0 + d, d < FK_MAX_DEPTH
+    H_MAXKEYS = H_LEVEL0 + FK_MAX_DEPTH,   // most keys any tile's rows see (>= 1)
     H_WORDS = 64
 };
+static_assert(H_MAXKEYS < H_WORDS, "header slots");
 
 struct WsLayout {
     size_t header;        // int32[H_WORDS]
@@ -45,7 +47,7 @@ struct WsLayout {
     size_t tok_pos;       // int32[T]
     size_t tile_seg;      // int32[tile_cap]
     size_t tile_row0;     // int32[tile_cap]
-    size_t tile_order;    // int32[tile_cap]   tiles by decreasing number of visible key blocks
+    size_t tile_order;    // int32[tile_cap]   tiles by decreasing work, grouped by root
     size_t seg_tile0;     // int32[S]  first tile of each segment (non-decreasing)
     size_t seg_coff;      // int32[S]  first chunk of each segment (non-decreasing)
     size_t lvl_seg;       // int32[FK_MAX_DEPTH*level_cap]

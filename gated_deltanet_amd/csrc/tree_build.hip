@@ -9,7 +9,8 @@
 //                            every segment (start, end, run count),
 //                            validation, lengths, first positions, ancestor
 //                            chains, tile / chunk / level offsets, fork points
-//   k_post     grid          tile order (heaviest first) and each level's
+//   k_post     grid          tile order (heaviest first, by root within a
+//                            band of work) and each level's
 //                            segments by decreasing chunk count (1 + levels
 //                            blocks), tile and chunk lists, page-id checks (a
 //                            block per segment), per-token positions
@@ -50,6 +51,20 @@ __device__ int block_scan(int x, int *lds, int *total)
     *total = lds[nw - 1];
     __syncthreads();
     return before + v - x;
+}
+
+// Maximum over the block (BUILD_THREADS threads, wave64).
+__device__ int block_max(int x, int *lds)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int v = x;
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    if (lane == 0) lds[wid] = v;
+    __syncthreads();
+    int r = lds[0];
+    for (int i = 1; i < nw; ++i) r = max(r, lds[i]);
+    __syncthreads();
+    return r;
 }
 
 struct BuildArgs {
@@ -165,7 +180,7 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
     // phase 3a: scans -- attention tiles, children CSR, level lists
     if (threadIdx.x < FK_MAX_DEPTH) lvl_lds[threadIdx.x] = 0;
     __syncthreads();
-    int tile_base = 0, kid_base = 0, chunk_base = 0;
+    int tile_base = 0, kid_base = 0, chunk_base = 0, max_keys = 1;
     for (int base = 0; base < S; base += blockDim.x) {
         const int s = base + threadIdx.x;
         const bool in = s < S;
@@ -175,6 +190,8 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
         int tot;
         const int toff = tile_base + block_scan(ntile, lds, &tot);
         tile_base += tot;
+        // the most keys a row of this segment sees (its last tile's rows)
+        max_keys = max(max_keys, block_max(live ? A.seg_pos0[s] + len : 0, lds));
         const int nchunk = live ? (len + FK_GDN_CHUNK - 1) / FK_GDN_CHUNK : 0;
         const int coff = chunk_base + block_scan(nchunk, lds, &tot);
         chunk_base += tot;
@@ -205,6 +222,7 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
         A.kid_off[S] = kid_base;
         A.header[H_NTILES] = tile_base;
         A.header[H_NCHUNKS] = chunk_base;
+        A.header[H_MAXKEYS] = max_keys;
         for (int dd = 0; dd < FK_MAX_DEPTH; ++dd) A.header[H_LEVEL0 + dd] = dd < m.max_depth ? lvl_lds[dd] : 0;
     }
     __syncthreads();
@@ -298,20 +316,29 @@ __device__ void lists_thread(int i, int S, const int32_t *__restrict__ header, c
     }
 }
 
-// Tiles by decreasing count of visible 64-key blocks (a bucket sort; order
-// within a bucket is whatever the atomics give).  Only the schedule of the
-// attention launch depends on it -- every tile computes the same way in any
-// order -- so the heaviest tiles start first and the launch ends evenly.  It
-// runs beside the blocks that write the tile list, so it finds each tile's
-// segment itself, with the same search over seg_tile0 (staged in LDS when S
-// fits there).
+// Tiles by decreasing work, grouped by root: a bucket sort over (band of the
+// tile's visible keys, root of its segment).  The bands split [0, most keys
+// of any tile] into ORDER_BANDS equal parts, so the launch runs heaviest
+// first at that granularity and does not end on a long tile started late;
+// within a band a root's tiles are consecutive ranks, so the work-groups
+// resident on an XCD at one time (consecutive ranks of one kv head) mostly
+// walk one request's history and share it in L2 -- on the expanding-history
+// resume round, heaviest first alone interleaves all 64 requests.  Order
+// within a bucket is whatever the atomics give; only the schedule depends on
+// the order (every tile computes the same way in any order).  It runs beside
+// the blocks that write the tile list, so it finds each tile's segment
+// itself, with the same search over seg_tile0 (staged in LDS when S fits
+// there).
 constexpr int ORDER_BUCKETS = 2 * BUILD_THREADS;
+constexpr int ORDER_BANDS = 64, ORDER_ROOTS = ORDER_BUCKETS / ORDER_BANDS;
 constexpr int ORDER_STAGE = 4096;
 __device__ void tile_order_block(const int32_t *__restrict__ header, int S, const int32_t *__restrict__ seg_tile0,
                                  const int32_t *__restrict__ seg_pos0, const int32_t *__restrict__ seg_len,
-                                 int32_t *__restrict__ tile_order, int *cnt, int *lds, int *stage)
+                                 const int32_t *__restrict__ seg_anc, int32_t *__restrict__ tile_order, int *cnt,
+                                 int *lds, int *stage)
 {
     const int n = header[H_NTILES];
+    const int64_t max_keys = header[H_MAXKEYS];
     const bool staged = S <= ORDER_STAGE;
     if (staged)
         for (int i = threadIdx.x; i < S; i += blockDim.x) stage[i] = seg_tile0[i];
@@ -321,7 +348,9 @@ __device__ void tile_order_block(const int32_t *__restrict__ header, int S, cons
     auto bucket = [&](int t) {
         const int s = owner_of(first, S, t), r0 = (t - first[s]) * FK_TILE_TOKENS;
         const int keys = seg_pos0[s] + min(r0 + FK_TILE_TOKENS, seg_len[s]);
-        return min((keys + 63) / 64, ORDER_BUCKETS - 1);
+        const int band = min(ORDER_BANDS - 1, (int)((int64_t)keys * ORDER_BANDS / (max_keys + 1)));
+        const int root = seg_anc[s * FK_MAX_DEPTH];
+        return band * ORDER_ROOTS + (ORDER_ROOTS - 1 - root % ORDER_ROOTS);
     };
     for (int t = threadIdx.x; t < n; t += blockDim.x) atomicAdd(&cnt[bucket(t)], 1);
     __syncthreads();
@@ -404,7 +433,7 @@ k_post(int no, int nl, int np, int S, int T, int32_t *header, const int32_t *__r
        const int32_t *__restrict__ tok_seg, const int32_t *__restrict__ seg_start,
        const int32_t *__restrict__ seg_pos0, int32_t *__restrict__ tok_pos, int32_t *__restrict__ tile_order,
        const int32_t *__restrict__ lvl_seg, const int32_t *__restrict__ seg_src, int level_cap,
-       int32_t *__restrict__ lvl_sorted)
+       int32_t *__restrict__ lvl_sorted, const int32_t *__restrict__ seg_anc)
 {
     __shared__ int cnt[ORDER_BUCKETS];
     __shared__ int stage[ORDER_STAGE];
@@ -412,7 +441,7 @@ k_post(int no, int nl, int np, int S, int T, int32_t *header, const int32_t *__r
     if (header[H_STATUS] != FK_OK) return;
     const int b = blockIdx.x;
     if (b == 0)
-        tile_order_block(header, S, seg_tile0, seg_pos0, seg_len, tile_order, cnt, lds, stage);
+        tile_order_block(header, S, seg_tile0, seg_pos0, seg_len, seg_anc, tile_order, cnt, lds, stage);
     else if (b < no)
         level_order_block(b - 1, header, lvl_seg, seg_len, seg_src, level_cap, lvl_sorted, cnt, lds);
     else if (b < no + nl)
@@ -494,7 +523,7 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
             no, nl, np, S, T, A.header, A.seg_tile0, A.seg_coff, A.tile_seg, A.tile_row0, A.chunk_seg,
             A.chunk_row0, A.seg_len, meta->seg_page_off, meta->seg_pages, meta->page_size, meta->n_pages,
             meta->tok_seg, A.seg_start, A.seg_pos0, ws_at<int32_t>(ws, L.tok_pos), ws_at<int32_t>(ws, L.tile_order),
-            A.lvl_seg, ws_at<int32_t>(ws, L.seg_src), meta->level_cap, ws_at<int32_t>(ws, L.lvl_sorted));
+            A.lvl_seg, ws_at<int32_t>(ws, L.seg_src), meta->level_cap, ws_at<int32_t>(ws, L.lvl_sorted), A.seg_anc);
         if ((rc = launch_status())) return rc;
     }
     return FK_OK;
