@@ -9,8 +9,9 @@
 // tile's ancestor chain (each ancestor's first `fork` tokens, then the own
 // segment causally), in 32-key blocks anchored at every range start; a row's
 // reduction order therefore depends only on its own chain (Flide 3.5).
-// A block pair of LDS buffers takes 38 KB, and the kernel 161 VGPRs, so three
-// work-groups (12 waves) share a compute unit.
+// Blocks are staged in a ring of three 16 KB LDS stages by direct global->LDS
+// loads two blocks ahead (48 KB), and the kernels take at most 147 VGPRs, so
+// three work-groups (12 waves) share a compute unit.
 //
 // Per block and wave, with v_mfma_f32_32x32x16_bf16 (fp32 accumulate):
 //   S^T[32 keys x 32 rows] = K_blk[32 x 128] . Q^T[128 x 32]       8 MFMAs
@@ -46,10 +47,6 @@ constexpr int BN = 32;           // keys per block
 constexpr int MT = BN / 32;      // 32-key MFMA tiles per block
 constexpr int WAVES = 4;
 constexpr int THREADS = WAVES * 64;
-constexpr int K_STRIDE = D + 8;  // LDS row stride (bf16) of the key tile, padded
-constexpr int V_STRIDE = BN + 8; // LDS row stride (bf16) of the transposed value tile
-constexpr int K_LDS = BN * K_STRIDE;
-constexpr int V_LDS = D * V_STRIDE;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -85,50 +82,6 @@ __device__ __forceinline__ uint4 pack8(const float *x)
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[e];
     return __builtin_bit_cast(uint4, v);
-}
-
-// One block of a range = BN / 16 pages of 16 keys.  Keys [BN][D] and
-// transposed values [D][BN] of a block are loaded into registers (two 16-byte
-// pieces per page and thread) and later written into one of two LDS buffers.
-// Pages past the range's valid keys are zero, so no page-list entry beyond
-// the range is ever read.
-struct BlockRegs {
-    uint4 k[BN / FK_TILE_TOKENS], v[BN / FK_TILE_TOKENS];
-};
-
-// The dim row of the transposed value tile that thread pair q (threads 2q,
-// 2q+1, 16 bytes each) moves.  A 16-byte LDS write serves 8 lanes -- 4 pairs
-// -- per cycle over 32 banks; with rows 20 dwords apart, four consecutive rows
-// would put rows r and r+3 on the same banks, while rows of one parity,
-// 2 apart, fill all 32 banks: pairs 4g..4g+3 take rows of one parity.  Each
-// wave still moves 32 whole rows of the page (1 KB contiguous).
-__device__ __forceinline__ int v_row(int q) { return (q & ~7) | ((q & 3) << 1) | ((q >> 2) & 1); }
-
-__device__ __forceinline__ void load_block(BlockRegs &R, const uint16_t *__restrict__ kp,
-                                           const uint16_t *__restrict__ vp, const int32_t *__restrict__ plist,
-                                           int key0, int count, int g, int Hkv)
-{
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int p = 0; p < BN / FK_TILE_TOKENS; ++p) {
-        const int kbase = key0 + p * FK_TILE_TOKENS;
-        R.k[p] = R.v[p] = make_uint4(0, 0, 0, 0);
-        if (kbase < count) {
-            const size_t pb = ((size_t)plist[kbase / FK_TILE_TOKENS] * Hkv + g) * (FK_TILE_TOKENS * D);
-            R.k[p] = *reinterpret_cast<const uint4 *>(kp + pb + tid * 8);   // slot tid/16, dims (tid%16)*8
-            R.v[p] = *reinterpret_cast<const uint4 *>(vp + pb + v_row(tid / 2) * FK_TILE_TOKENS + (tid % 2) * 8);
-        }
-    }
-}
-
-__device__ __forceinline__ void store_block(uint16_t *__restrict__ ks, uint16_t *__restrict__ vs, const BlockRegs &R)
-{
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int p = 0; p < BN / FK_TILE_TOKENS; ++p) {
-        *reinterpret_cast<uint4 *>(ks + (p * FK_TILE_TOKENS + tid / 16) * K_STRIDE + (tid % 16) * 8) = R.k[p];
-        *reinterpret_cast<uint4 *>(vs + v_row(tid / 2) * V_STRIDE + p * FK_TILE_TOKENS + (tid % 2) * 8) = R.v[p];
-    }
 }
 
 // Visibility rules (Flide section 3.2.1): causal (t_y <= t_x); a sliding
@@ -220,10 +173,8 @@ __device__ __forceinline__ void store_rows(const f32x16 (&o)[D / 32], float l, b
 // 8 * half), online softmax with the per-row lazy rescale, O^T += V^T . P^T.
 // Where a lane's operands sit in a staged block (bf16 elements): K fragment
 // (key tile mt, k-step ks) at krow + mt * KMT + ks * KS, value fragment
-// (dim tile i, key step kk) at vrow + i * VI + kk * VKK.
-struct PaddedTiles {   // [key][K_STRIDE] and [dim][V_STRIDE] tiles written from registers
-    static constexpr int KS = 16, KMT = 32 * K_STRIDE, VI = 32 * V_STRIDE, VKK = 16;
-};
+// (dim tile i, key step kk) at vrow + i * VI + kk * VKK (the ring layout
+// below).
 
 // `mid` runs once the score products are issued (the full launch issues a
 // later block's loads there, while the matrix cores work on this one).
@@ -551,7 +502,8 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
 // each row meets its own chain's blocks in chain order, anchored as in the
 // full launch, and its output has the same bits as that token's row of the
 // full launch, whatever its group.  Grouping only fills the tile's rows: one
-// pass over a shared trunk serves up to 16 questions.
+// pass over a shared trunk serves up to 16 questions.  Blocks are staged in
+// the full launch's ring, so operands and arithmetic are the same.
 constexpr int RO_CAND = FK_TILE_TOKENS * FK_MAX_DEPTH;   // (slot, depth) candidates
 
 template <int RULE>
@@ -565,8 +517,7 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
                     const int32_t *__restrict__ seg_anc, const int32_t *__restrict__ seg_fork,
                     const int32_t *__restrict__ page_off, const int32_t *__restrict__ pages)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][K_LDS];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][V_LDS];
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[RING * STAGE];
     __shared__ int c_seg[RO_CAND], c_lim[RO_CAND], c_lo[RO_CAND];   // per (slot, depth)
     __shared__ int c_rep[RO_CAND], c_cnt[RO_CAND], c_key0[RO_CAND];
     __shared__ int r_seg[RO_CAND], r_depth[RO_CAND], r_count[RO_CAND], r_key0[RO_CAND];
@@ -576,20 +527,12 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int half = lane >> 5, n = lane & 31;
 
-    // this lane's row: entry of slot w*4 + n/8, q head g*G + n%8; its query
-    // loads are issued first and land while the walk is planned
+    // this lane's row: entry of slot w*4 + n/8, q head g*G + n%8
     const int slot = w * 4 + n / 8, e = grp * group + slot;
     const int t = (slot < group && e < n_rows) ? sel_rows[e] : -1;
     const bool row_valid = t >= 0 && t < T && tok_seg[t] >= 0;   // not unused, not padding
     const int h = g * G + (n % 8);
     const size_t qrow = (size_t)e * Hq + h;
-    bf16x8 qf[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (row_valid) u = *reinterpret_cast<const uint4 *>(q_rows + qrow * D + ks * 16 + half * 8);
-        qf[ks] = as_bf16x8(u);
-    }
 
     // candidate (slot ci / FK_MAX_DEPTH, depth ci % FK_MAX_DEPTH): the segment
     // that slot's entry meets at that depth, how many of its keys the entry
@@ -662,7 +605,15 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
     const int nr = uni(n_ranges);
     if (nr == 0) return;   // no used entry in this group
 
-    const bool wave_has_rows = __any(row_valid);
+    // wave-uniform (readfirstlane), so the walk branches on it with scalar branches
+    const bool wave_has_rows = __builtin_amdgcn_readfirstlane(__any(row_valid));
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (row_valid) u = *reinterpret_cast<const uint4 *>(q_rows + qrow * D + ks * 16 + half * 8);
+        qf[ks] = as_bf16x8(u);
+    }
 
     f32x16 o[D / 32];
 #pragma unroll
@@ -672,56 +623,91 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
 
     // the lane's visible keys [lo_r, lim_r) of range ri (none off its chain),
     // from the planning tables in LDS (no global load in the walk)
-    int lim_r = 0, lo_r = 0;
+    int lim_r = 0, lo_r = 0, lane_ri = 0;
     auto lane_range = [&](int ri) {
         const int a = uni(r_seg[ri]), dd = uni(r_depth[ri]);
         const int ci = slot * FK_MAX_DEPTH + dd;
         const bool on = row_valid && c_seg[ci] == a;
         lim_r = on ? c_lim[ci] : 0;
         lo_r = (RULE == WINDOW && on) ? c_lo[ci] : 0;
+        lane_ri = ri;
     };
-    // the walk position: range ri (its page list and key count held in
-    // registers), block key0; the next block's are looked up one block ahead
-    int ri = 0, key0 = uni(r_key0[0]), count = uni(r_count[0]);
-    const int32_t *plist = pages + uni(page_off[uni(r_seg[0])]);
+    // Blocks are staged as in the full launch (three-stage ring, direct
+    // loads two blocks ahead, every wave four loads per block), so each row's
+    // operands and arithmetic are the full launch's.  Walk position: range
+    // ri, block key0 (ranges are never empty).
+    struct RCursor {
+        int ri, key0, count;
+        const int32_t *plist;
+    };
+    auto r_range = [&](RCursor &c, int ri) {
+        c.ri = ri;
+        c.key0 = uni(r_key0[ri]);
+        c.count = uni(r_count[ri]);
+        c.plist = pages + ldc(page_off, uni(r_seg[ri]));
+    };
+    auto r_next = [&](RCursor &c) {
+        c.key0 += BN;
+        if (c.key0 < c.count) return true;
+        if (c.ri + 1 >= nr) return false;
+        r_range(c, c.ri + 1);
+        return true;
+    };
+    const uint32_t koff = ring_k_off(w, lane), voff = ring_v_off(w, lane);
+    const uint32_t ring_bytes =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)ring + w * 1024);
+    const uint16_t *kg = uniform_ptr(kp + (size_t)g * (FK_TILE_TOKENS * D));
+    const uint16_t *vg = uniform_ptr(vp + (size_t)g * (FK_TILE_TOKENS * D));
+    const uint32_t pstride = (uint32_t)Hkv * (FK_TILE_TOKENS * D);
+    const uint16_t *krow0 = ring + (n >> 4) * 2048 + half * 128 + (prow & 15) * 8;
+    const uint16_t *vrow0 = ring + 4096 + half * 256 + n * 8;
+
+    RCursor cur;
+    r_range(cur, 0);
     lane_range(0);
-    {
-        BlockRegs R;
-        load_block(R, kp, vp, plist, key0, count, g, Hkv);
-        store_block(k_lds[0], v_lds[0], R);
-    }
-    __syncthreads();
-    for (int buf = 0;; buf ^= 1) {
-        int nri = ri, nkey0 = key0 + BN, ncount = count;
-        const int32_t *nplist = plist;
-        bool more = true;
-        if (nkey0 >= count) {
-            nri = ri + 1;
-            more = nri < nr;
-            if (more) {
-                nkey0 = uni(r_key0[nri]);
-                ncount = uni(r_count[nri]);
-                nplist = pages + uni(page_off[uni(r_seg[nri])]);
-            }
-        }
-        BlockRegs R;
-        if (more) load_block(R, kp, vp, nplist, nkey0, ncount, g, Hkv);
+    ring_issue(ring_bytes, kg, vg, ring_pages(cur.plist, cur.key0, cur.count), pstride, koff, voff);
+    RCursor nxt = cur;
+    bool more = r_next(nxt);
+    if (more) ring_issue(ring_bytes + STAGE * 2, kg, vg, ring_pages(nxt.plist, nxt.key0, nxt.count), pstride, koff, voff);
+    RCursor nxt2 = nxt;
+    bool more2 = more && r_next(nxt2);
+    BlockPages pg2 = more2 ? ring_pages(nxt2.plist, nxt2.key0, nxt2.count) : BlockPages{0, 0};
+    // the query loads (and the first two blocks) complete here, so the
+    // compiler's own wait for them is not repeated inside the walk
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    for (int st = 0;;) {
+        // block j landed in every wave, and every wave is done with block j-1,
+        // whose stage block j+2 now takes
+        if (more)
+            ring_wait_barrier<4>();
+        else
+            ring_wait_barrier<0>();
+        const uint32_t st2_bytes = ring_bytes + (st == 0 ? 2 : st - 1) * (STAGE * 2);
+        if (cur.ri != lane_ri) lane_range(cur.ri);
         if (wave_has_rows) {   // wave-uniform
+            const int key0 = cur.key0;
             const bool lane_full = !row_valid || (key0 + BN <= lim_r && (RULE != WINDOW || key0 >= lo_r));
             const bool full = __all(lane_full);
             const int hi = lim_r - 1 - key0 - half * 8;
             const int lo = (RULE == WINDOW ? lo_r - key0 : 0) - half * 8;
-            block_compute<RULE, PaddedTiles>(k_lds[buf] + prow * K_STRIDE + half * 8, v_lds[buf] + n * V_STRIDE + half * 8,
-                                             qf, o, m, l, full, hi, lo, scale_log2e);
+            // block j+2's loads go out once this block's score products are
+            block_compute<RULE, RingTiles>(krow0 + st * STAGE, vrow0 + st * STAGE, qf, o, m, l, full, hi, lo,
+                                           scale_log2e, [&]() {
+                                               if (more2) ring_issue(st2_bytes, kg, vg, pg2, pstride, koff, voff);
+                                           });
+        } else if (more2) {
+            ring_issue(st2_bytes, kg, vg, pg2, pstride, koff, voff);
         }
         if (!more) break;
-        store_block(k_lds[buf ^ 1], v_lds[buf ^ 1], R);
-        if (nri != ri) lane_range(nri);
-        ri = nri;
-        key0 = nkey0;
-        count = ncount;
-        plist = nplist;
-        __syncthreads();   // next block staged; this buffer free for reuse
+        RCursor nxt3 = nxt2;
+        const bool more3 = more2 && r_next(nxt3);
+        if (more3) pg2 = ring_pages(nxt3.plist, nxt3.key0, nxt3.count);
+        cur = nxt;
+        nxt = nxt2;
+        nxt2 = nxt3;
+        more = more2;
+        more2 = more3;
+        st = st == 2 ? 0 : st + 1;
     }
     store_rows(o, l, row_valid, out_rows + qrow * D, half);
 }
