@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "fk_common.h"
 
@@ -447,7 +448,10 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     // compiler's own wait for them is not repeated inside the walk, where a
     // full wait would also drain the block loads in flight
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    for (int st = 0;;) {
+    // one block in stage ST; returns false after the last block.  The walk is
+    // unrolled over the three stages so that every LDS offset is an immediate.
+    auto step = [&](auto STC) {
+        constexpr int ST = decltype(STC)::value, ST2 = (ST + 2) % RING;
         // block j landed in every wave, and every wave is done with block j-1,
         // whose stage block j+2 now takes
         if (more)
@@ -456,9 +460,8 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             ring_wait_barrier<0>();
         // block j+2's loads are issued once this block's score products are
         // (their issue can stall on the memory pipeline while those run)
-        const uint32_t st2_bytes = ring_bytes + (st == 0 ? 2 : st - 1) * (STAGE * 2);
         auto issue_next = [&]() {
-            if (more2) ring_issue(st2_bytes, kg, vg, pg2, pstride, koff, voff);
+            if (more2) ring_issue(ring_bytes + ST2 * (STAGE * 2), kg, vg, pg2, pstride, koff, voff);
         };
         {
             const int key0 = cur.key0, count = cur.count, pdiff = cur.pdiff;
@@ -473,12 +476,12 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             // a wave whose four tokens all lie past the segment's end (in the
             // segment's last tile) only helps stage the blocks
             if (wave_live)
-                block_compute<RULE, RingTiles>(krow0 + st * STAGE, vrow0 + st * STAGE, qf, o, m, l, full, hi, lo,
+                block_compute<RULE, RingTiles>(krow0 + ST * STAGE, vrow0 + ST * STAGE, qf, o, m, l, full, hi, lo,
                                                scale_log2e, issue_next);
             else
                 issue_next();
         }
-        if (!more) break;
+        if (!more) return false;
         BlockCursor nxt3 = nxt2;
         const bool more3 = more2 && cursor_next<RULE>(nxt3, tc);
         if (more3) pg2 = ring_pages(nxt3.plist, nxt3.key0, nxt3.count);
@@ -487,7 +490,11 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
         nxt2 = nxt3;
         more = more2;
         more2 = more3;
-        st = st == 2 ? 0 : st + 1;
+        return true;
+    };
+    static_assert(RING == 3, "the walk is unrolled over three stages");
+    while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>()) &&
+           step(std::integral_constant<int, 2>())) {
     }
     store_rows(o, l, row_valid, out + qrow * D, half);
 }
@@ -675,14 +682,17 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
     // the query loads (and the first two blocks) complete here, so the
     // compiler's own wait for them is not repeated inside the walk
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    for (int st = 0;;) {
+    // one block in stage ST; returns false after the last block (the walk is
+    // unrolled over the three stages, as in the full launch)
+    auto step = [&](auto STC) {
+        constexpr int ST = decltype(STC)::value, ST2 = (ST + 2) % RING;
         // block j landed in every wave, and every wave is done with block j-1,
         // whose stage block j+2 now takes
         if (more)
             ring_wait_barrier<4>();
         else
             ring_wait_barrier<0>();
-        const uint32_t st2_bytes = ring_bytes + (st == 0 ? 2 : st - 1) * (STAGE * 2);
+        const uint32_t st2_bytes = ring_bytes + ST2 * (STAGE * 2);
         if (cur.ri != lane_ri) lane_range(cur.ri);
         if (wave_has_rows) {   // wave-uniform
             const int key0 = cur.key0;
@@ -691,14 +701,14 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
             const int hi = lim_r - 1 - key0 - half * 8;
             const int lo = (RULE == WINDOW ? lo_r - key0 : 0) - half * 8;
             // block j+2's loads go out once this block's score products are
-            block_compute<RULE, RingTiles>(krow0 + st * STAGE, vrow0 + st * STAGE, qf, o, m, l, full, hi, lo,
+            block_compute<RULE, RingTiles>(krow0 + ST * STAGE, vrow0 + ST * STAGE, qf, o, m, l, full, hi, lo,
                                            scale_log2e, [&]() {
                                                if (more2) ring_issue(st2_bytes, kg, vg, pg2, pstride, koff, voff);
                                            });
         } else if (more2) {
             ring_issue(st2_bytes, kg, vg, pg2, pstride, koff, voff);
         }
-        if (!more) break;
+        if (!more) return false;
         RCursor nxt3 = nxt2;
         const bool more3 = more2 && r_next(nxt3);
         if (more3) pg2 = ring_pages(nxt3.plist, nxt3.key0, nxt3.count);
@@ -707,7 +717,10 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
         nxt2 = nxt3;
         more = more2;
         more2 = more3;
-        st = st == 2 ? 0 : st + 1;
+        return true;
+    };
+    while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>()) &&
+           step(std::integral_constant<int, 2>())) {
     }
     store_rows(o, l, row_valid, out_rows + qrow * D, half);
 }
