@@ -31,6 +31,8 @@
 // that run together share their x and w tiles in that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "fk_common.h"
 
 namespace fk {
@@ -155,15 +157,17 @@ __global__ void __launch_bounds__((Shape<NF, WM>::NT), (Shape<NF, WM>::OCC)) k_p
     issue(0, 0);
     issue(1, 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the index reads and the first stages
-    for (int kt = 0, s = 0; kt < nk; ++kt) {
+    // k-step kt in stage S (= kt mod 3); the loop is unrolled over the three
+    // stages so that every LDS offset is an immediate
+    auto kstep = [&](auto SC, int kt) {
+        constexpr int S = decltype(SC)::value, S2 = (S + 2) % RING;
         // step kt landed in every wave; every wave is done with step kt-1,
         // whose stage step kt+2 now takes (the loads complete in order)
         if (kt + 1 < nk)
             wait_barrier<WF + 2>();
         else
             wait_barrier<0>();
-        const uint16_t *lw = ring + s * SH::STAGE, *lx = lw + SH::WT;
-        const int s2 = s == 0 ? 2 : s - 1;   // (s + 2) % 3
+        const uint16_t *lw = ring + S * SH::STAGE, *lx = lw + SH::WT;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int unit = ks * 2 + half;
@@ -182,10 +186,18 @@ __global__ void __launch_bounds__((Shape<NF, WM>::NT), (Shape<NF, WM>::OCC)) k_p
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
             // step kt+2's loads go out once the first products are issued
-            if (ks == 0 && kt + 2 < nk) issue(kt + 2, s2);
+            if (ks == 0 && kt + 2 < nk) issue(kt + 2, S2);
         }
-        s = s == 2 ? 0 : s + 1;
+    };
+    static_assert(RING == 3, "the k loop is unrolled over three stages");
+    int kt = 0;
+    for (; kt + RING <= nk; kt += RING) {
+        kstep(std::integral_constant<int, 0>(), kt);
+        kstep(std::integral_constant<int, 1>(), kt + 1);
+        kstep(std::integral_constant<int, 2>(), kt + 2);
     }
+    if (kt < nk) kstep(std::integral_constant<int, 0>(), kt);
+    if (kt + 1 < nk) kstep(std::integral_constant<int, 1>(), kt + 1);
     // y^T tile: lane holds row m = .. + c32 and features 8 (r / 4) + 4 half + r % 4
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
