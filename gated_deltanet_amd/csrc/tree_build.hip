@@ -205,19 +205,17 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
         const int koff = kid_base + block_scan(kc, lds, &tot);
         kid_base += tot;
         if (in) A.kid_off[s] = koff;
+        // level lists: a rank per live segment from its level's LDS counter
+        // (order within a level is whatever the atomics give: k_post sorts
+        // each level, and every segment computes the same way in any order)
         const int depth = in ? A.seg_depth[s] : -1;
-        for (int dd = 0; dd < m.max_depth; ++dd) {
-            const int pos = block_scan(live && depth == dd, lds, &tot);
-            if (live && depth == dd) {
-                const int rank = lvl_lds[dd] + pos;
-                if (rank < m.level_cap) A.lvl_seg[dd * m.level_cap + rank] = s;
-                else build_error(A.header, &flag, FK_E_CAPACITY);
-            }
-            __syncthreads();
-            if (threadIdx.x == 0) lvl_lds[dd] += tot;
-            __syncthreads();
+        if (live && depth >= 0 && depth < m.max_depth) {
+            const int rank = atomicAdd(&lvl_lds[depth], 1);
+            if (rank < m.level_cap) A.lvl_seg[depth * m.level_cap + rank] = s;
+            else build_error(A.header, &flag, FK_E_CAPACITY);
         }
     }
+    __syncthreads();
     if (threadIdx.x == 0) {
         A.kid_off[S] = kid_base;
         A.header[H_NTILES] = tile_base;
