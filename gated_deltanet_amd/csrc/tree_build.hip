@@ -4,10 +4,11 @@
 // table is built on the GPU; section 3.3.2: launch sizes come from host-known
 // capacities, so the host never reads the tree).
 //
-// Kernels (two launches):
-//   k_build    one block     clears the status and counters, token runs of
-//                            every segment (start, end, run count),
-//                            validation, lengths, first positions, ancestor
+// Kernels (four launches):
+//   k_clear    grid          clears the status and the per-segment counters
+//   k_tokens   grid          token runs of every segment (start, end, run
+//                            count), padding and segment-id checks
+//   k_build    one block     validation, lengths, first positions, ancestor
 //                            chains, tile / chunk / level offsets, fork points
 //   k_post     grid          tile order (heaviest first, by root within a
 //                            band of work) and each level's
@@ -91,6 +92,56 @@ __device__ bool block_failed(int *flag)
     return *flag != FK_OK;
 }
 
+// Phase 0, over the whole grid: k_clear zeroes the status and the
+// per-segment counters; then k_tokens checks every token's segment id, and the
+// first token of every run records the run start, the last its end, and
+// counts the run (an integer atomic: order-independent).
+__global__ void __launch_bounds__(BUILD_THREADS) k_clear(BuildArgs A)
+{
+    const int i = blockIdx.x * BUILD_THREADS + threadIdx.x;
+    if (i < H_WORDS) A.header[i] = 0;
+    if (i < A.m.S) {
+        A.seg_nrun[i] = 0;
+        A.kid_cnt[i] = 0;
+        A.kid_fill[i] = 0;
+    }
+}
+
+constexpr int TOKENS_PER_THREAD = 8;   // their loads in flight together
+__global__ void __launch_bounds__(BUILD_THREADS) k_tokens(BuildArgs A)
+{
+    const fk_tree_meta &m = A.m;
+    const int S = m.S, T = m.T;
+    constexpr int TB = TOKENS_PER_THREAD;
+    const int base = blockIdx.x * TB * BUILD_THREADS;
+    int sv[TB], pv[TB], nv[TB];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+        const int t = base + u * BUILD_THREADS + threadIdx.x;
+        sv[u] = t < T ? m.tok_seg[t] : 0;
+        pv[u] = t < T && t > 0 ? m.tok_seg[t - 1] : -1;
+        nv[u] = t + 1 < T ? m.tok_seg[t + 1] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+        const int t = base + u * BUILD_THREADS + threadIdx.x, s = sv[u];
+        if (t >= T) continue;
+        if (s == FK_PAD_TOKEN) {   // padding: only more padding may follow
+            if (t + 1 < T && nv[u] != FK_PAD_TOKEN) set_error(A.header, FK_E_SEG_RANGE);
+            continue;
+        }
+        if (s < 0 || s >= S) {
+            set_error(A.header, FK_E_SEG_RANGE);
+            continue;
+        }
+        if (t == 0 || pv[u] != s) {
+            atomicAdd(A.seg_nrun + s, 1);
+            A.seg_start[s] = t;   // meaningful only when the run count is 1
+        }
+        if (t == T - 1 || nv[u] != s) A.seg_end[s] = t + 1;
+    }
+}
+
 __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
 {
     __shared__ int lds[32];
@@ -98,48 +149,8 @@ __global__ void __launch_bounds__(BUILD_THREADS) k_build(BuildArgs A)
     __shared__ int flag;
     const fk_tree_meta &m = A.m;
     const int S = m.S;
-    // phase 0: clear the status and the per-segment counters; then each
-    // token checks its segment id, and the first token of every run records
-    // the run start, the last its end, and counts the run
-    for (int i = threadIdx.x; i < H_WORDS; i += blockDim.x) A.header[i] = 0;
-    for (int s = threadIdx.x; s < S; s += blockDim.x) {
-        A.seg_nrun[s] = 0;
-        A.kid_cnt[s] = 0;
-        A.kid_fill[s] = 0;
-    }
-    if (threadIdx.x == 0) flag = FK_OK;
-    __threadfence_block();
-    __syncthreads();
-    const int T = m.T;
-    constexpr int TB = 8;   // tokens per thread per round, their loads in flight together
-    for (int base = 0; base < T; base += TB * BUILD_THREADS) {
-        int sv[TB], pv[TB], nv[TB];
-#pragma unroll
-        for (int u = 0; u < TB; ++u) {
-            const int t = base + u * BUILD_THREADS + threadIdx.x;
-            sv[u] = t < T ? m.tok_seg[t] : 0;
-            pv[u] = t < T && t > 0 ? m.tok_seg[t - 1] : -1;
-            nv[u] = t + 1 < T ? m.tok_seg[t + 1] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < TB; ++u) {
-            const int t = base + u * BUILD_THREADS + threadIdx.x, s = sv[u];
-            if (t >= T) continue;
-            if (s == FK_PAD_TOKEN) {   // padding: only more padding may follow
-                if (t + 1 < T && nv[u] != FK_PAD_TOKEN) build_error(A.header, &flag, FK_E_SEG_RANGE);
-                continue;
-            }
-            if (s < 0 || s >= S) {
-                build_error(A.header, &flag, FK_E_SEG_RANGE);
-                continue;
-            }
-            if (t == 0 || pv[u] != s) {
-                atomicAdd(A.seg_nrun + s, 1);   // an integer count: order-independent
-                A.seg_start[s] = t;             // meaningful only when the run count is 1
-            }
-            if (t == T - 1 || nv[u] != s) A.seg_end[s] = t + 1;
-        }
-    }
+    // phase 0 ran in k_clear and k_tokens; their errors are in the status
+    if (threadIdx.x == 0) flag = A.header[H_STATUS];
     if (block_failed(&flag)) return;
 
     // phase 1: lengths
@@ -511,6 +522,12 @@ extern "C" int fk_tree_build(const fk_tree_meta *meta, void *ws, size_t ws_bytes
     A.seg_tile0 = ws_at<int32_t>(ws, L.seg_tile0);
     A.seg_coff = ws_at<int32_t>(ws, L.seg_coff);
     const int S = meta->S, T = meta->T;
+    {
+        const int nc = ((S > H_WORDS ? S : H_WORDS) + BUILD_THREADS - 1) / BUILD_THREADS;
+        const int per = TOKENS_PER_THREAD * BUILD_THREADS, nt = T > 0 ? (T + per - 1) / per : 1;
+        k_clear<<<(unsigned)nc, BUILD_THREADS, 0, st>>>(A);
+        k_tokens<<<(unsigned)nt, BUILD_THREADS, 0, st>>>(A);
+    }
     k_build<<<1, BUILD_THREADS, 0, st>>>(A);
     if ((rc = launch_status())) return rc;
     {
