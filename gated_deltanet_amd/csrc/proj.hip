@@ -13,18 +13,20 @@
 // on M), so its bits depend only on its own row of x and column of w.
 //
 // Tiles: waves compute 32-row x 32-feature products of y^T = w x^T with
-// v_mfma_f32_32x32x16_bf16 (A = rows of w, B = rows of x), k in steps of 32
-// through a ring of three LDS stages (the w and x tiles of one step) filled
-// by direct global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes
-// land at M0 + 16 * lane) two steps ahead, so no register holds a tile in
+// v_mfma_f32_32x32x16_bf16 (A = rows of w, B = rows of x), k in steps
+// through a ring of LDS stages (the w and x tiles of one step) filled by
+// direct global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes
+// land at M0 + 16 * lane) ahead of use, so no register holds a tile in
 // flight.  When N is a multiple of 256 a work-group of eight waves computes a
 // 256-feature x 256-row block (a wave 128 x 64: four w and two x fragments
-// per k-step for eight products; 96 KB, one work-group a CU); otherwise four
-// waves compute 128 x 128 (a wave 64 x 64; 48 KB, three a CU).  LDS rows are
-// 64 bytes, their four 16-byte units XOR-swizzled by bits 2-3 of the row, so
-// the operand reads (16 lanes: 16 rows, one unit) are free of bank
-// conflicts; the lane that fills unit u of row r loads the unit that belongs
-// there.  A lane's accumulator holds 4 consecutive output features of one
+// per 16-wide k-slice for eight products), k in steps of 64 through two
+// 64 KB stages (one step ahead; one work-group a CU); otherwise four waves
+// compute 128 x 128 (a wave 64 x 64), k in steps of 32 through three 16 KB
+// stages (two steps ahead; three work-groups a CU).  LDS rows hold one
+// step's k (64 or 128 bytes), their 16-byte units XOR-swizzled by bits 2-3
+// (or 1-3) of the row, so the operand reads (16 lanes: 16 rows, one unit)
+// are free of bank conflicts; the lane that fills unit u of row r loads the
+// unit that belongs there.  A lane's accumulator holds 4 consecutive output features of one
 // row: 8-byte stores.
 // Tiles are dealt to the eight XCDs in contiguous ranges of row blocks, and
 // within an XCD in groups of GM row blocks (row block fastest), so blocks
@@ -41,27 +43,34 @@ namespace proj {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int BM = 128, BN = 128;
 constexpr int K_MULT = 64;      // K must be a multiple of this (the documented contract)
 constexpr int WIDE_WM = 4;      // waves along the rows of the 256-feature blocks
-constexpr int RING = 3;         // stages
 constexpr int GM = 8;           // row blocks per group within an XCD
 constexpr int XCDS = 8;
 // NF: 32-feature fragments per wave (2: 128 x 128 blocks, three work-groups a
 // CU; 4: 256 features x 128 rows, two work-groups a CU and half the LDS
 // operand bytes per product, used when N is a multiple of 256)
-template <int NF, int WM>   // WM: waves along the rows (64 rows each)
+template <int NF, int WM, int BK_ = 32>   // WM: waves along the rows (64 rows each)
 struct Shape {
+    static constexpr int BK = BK_;                 // k per step
+    static constexpr int RN = BK == 32 ? 3 : 2;    // ring stages (loads RN - 1 steps ahead)
+    static constexpr int UNITS = BK / 8;           // 16-byte units per LDS row
+    static constexpr int RPL = 64 / UNITS;         // rows per 1 KB load
     static constexpr int BNW = 64 * NF;            // features per work-group
     static constexpr int BMW = 64 * WM;            // rows per work-group
     static constexpr int NT = 128 * WM;            // threads (2 x WM waves)
     static constexpr int WT = BNW * BK, XT = BMW * BK;   // bf16 elements of the w / x tiles
     static constexpr int STAGE = WT + XT;
     static constexpr int OCC = NF == 2 ? 3 : (WM == 2 ? 2 : 1);   // work-groups a CU
+    // rows of UNITS 16-byte units, XOR-swizzled so that a 16-lane read of
+    // one unit in 16 consecutive rows meets 16 distinct bank groups
+    static __device__ __forceinline__ int swz_unit(int row, int unit)
+    {
+        return BK == 32 ? unit ^ ((row >> 2) & 3) : unit ^ ((row >> 1) & 7);
+    }
+    static __device__ __forceinline__ int swz(int row, int unit) { return row * BK + (swz_unit(row, unit) << 3); }
 };
-
-__device__ __forceinline__ int swz_unit(int row, int unit) { return unit ^ ((row >> 2) & 3); }
-__device__ __forceinline__ int swz(int row, int unit) { return row * BK + (swz_unit(row, unit) << 3); }
 
 // one 16-byte direct global->LDS load per lane: global address g (per lane),
 // LDS address m0 + 16 * lane
@@ -103,29 +112,31 @@ __device__ __forceinline__ bool tile_of(const Args &A, int b, int &mb, int &nb)
     return true;
 }
 
-template <int NF, int WM>
-__global__ void __launch_bounds__((Shape<NF, WM>::NT), (Shape<NF, WM>::OCC)) k_proj_bf16(Args A)
+template <int NF, int WM, int BK_>
+__global__ void __launch_bounds__((Shape<NF, WM, BK_>::NT), (Shape<NF, WM, BK_>::OCC)) k_proj_bf16(Args A)
 {
-    using SH = Shape<NF, WM>;
-    __shared__ __attribute__((aligned(1024))) uint16_t ring[RING * SH::STAGE];
+    using SH = Shape<NF, WM, BK_>;
+    constexpr int BK = SH::BK, RNG = SH::RN, RPL = SH::RPL, UNITS = SH::UNITS;
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[RNG * SH::STAGE];
     int mb, nb;
     if (!tile_of(A, blockIdx.x, mb, nb)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wn = w & 1, wm = w >> 1, half = lane >> 5, c32 = lane & 31;
     const int m0 = mb * SH::BMW, n0 = nb * SH::BNW;
-    constexpr int WF = NF * 2 / WM;   // w loads a wave: 16-row pieces of the w tile
+    constexpr int WF = SH::BNW / RPL / (2 * WM);   // w loads a wave (RPL rows each)
+    constexpr int XL = 32 / RPL;                   // x loads a wave (32 rows)
 
     // loads, 16 rows (1 KB) an instruction, lane l: row r0 + l / 4, LDS unit
     // l % 4.  Wave w fills w rows 16 WF w .. +16 WF and x rows 32 w .. +32.
-    const uint16_t *wsrc[WF], *xsrc[2];
+    const uint16_t *wsrc[WF], *xsrc[XL];
 #pragma unroll
     for (int i = 0; i < WF; ++i) {
-        const int r = 16 * WF * w + 16 * i + (lane >> 2), u = swz_unit(r, lane & 3);
+        const int r = RPL * WF * w + RPL * i + lane / UNITS, u = SH::swz_unit(r, lane % UNITS);
         wsrc[i] = A.w + (size_t)(n0 + r) * A.K + u * 8;
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = 32 * w + 16 * i + (lane >> 2), u = swz_unit(r, lane & 3);
+    for (int i = 0; i < XL; ++i) {
+        const int r = 32 * w + RPL * i + lane / UNITS, u = SH::swz_unit(r, lane % UNITS);
         // a row past M, or an unused index entry, reads row 0 of x: that
         // output row is never stored, and no other row uses it
         const int m = m0 + r;
@@ -135,7 +146,7 @@ __global__ void __launch_bounds__((Shape<NF, WM>::NT), (Shape<NF, WM>::OCC)) k_p
         xsrc[i] = A.x + (size_t)src * A.K + u * 8;
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)ring;
-    const uint32_t wq = __builtin_amdgcn_readfirstlane(lds0 + w * 16 * WF * BK * 2);
+    const uint32_t wq = __builtin_amdgcn_readfirstlane(lds0 + w * RPL * WF * BK * 2);
     const uint32_t xq = __builtin_amdgcn_readfirstlane(lds0 + SH::WT * 2 + w * 32 * BK * 2);
     // stage s of k-step kt: w tile, then x tile (WF + 2 loads a wave)
     auto issue = [&](int kt, int s) {
@@ -144,7 +155,7 @@ __global__ void __launch_bounds__((Shape<NF, WM>::NT), (Shape<NF, WM>::OCC)) k_p
 #pragma unroll
         for (int i = 0; i < WF; ++i) lds_dma16(wsrc[i] + k0, wq + so + i * 1024);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + k0, xq + so + i * 1024);
+        for (int i = 0; i < XL; ++i) lds_dma16(xsrc[i] + k0, xq + so + i * 1024);
     };
 
     f32x16 acc[NF][2];
@@ -153,18 +164,19 @@ __global__ void __launch_bounds__((Shape<NF, WM>::NT), (Shape<NF, WM>::OCC)) k_p
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    const int nk = A.K / BK;   // >= 2
-    issue(0, 0);
-    issue(1, 1);
+    const int nk = A.K / BK;   // >= 1
+#pragma unroll
+    for (int p = 0; p < RNG - 1; ++p)
+        if (p < nk) issue(p, p);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the index reads and the first stages
-    // k-step kt in stage S (= kt mod 3); the loop is unrolled over the three
+    // k-step kt in stage S (= kt mod RN); the loop is unrolled over the
     // stages so that every LDS offset is an immediate
     auto kstep = [&](auto SC, int kt) {
-        constexpr int S = decltype(SC)::value, S2 = (S + 2) % RING;
+        constexpr int S = decltype(SC)::value, SN = (S + RNG - 1) % RNG;
         // step kt landed in every wave; every wave is done with step kt-1,
-        // whose stage step kt+2 now takes (the loads complete in order)
-        if (kt + 1 < nk)
-            wait_barrier<WF + 2>();
+        // whose stage step kt+RN-1 now takes (the loads complete in order)
+        if (RNG == 3 && kt + 1 < nk)
+            wait_barrier<WF + XL>();
         else
             wait_barrier<0>();
         const uint16_t *lw = ring + S * SH::STAGE, *lx = lw + SH::WT;
@@ -175,29 +187,36 @@ __global__ void __launch_bounds__((Shape<NF, WM>::NT), (Shape<NF, WM>::OCC)) k_p
 #pragma unroll
             for (int i = 0; i < NF; ++i)
                 a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                                                      &lw[swz(wn * 32 * NF + i * 32 + c32, unit)]));
+                                                      &lw[SH::swz(wn * 32 * NF + i * 32 + c32, unit)]));
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                                                      &lx[swz(wm * 64 + j * 32 + c32, unit)]));
+                                                      &lx[SH::swz(wm * 64 + j * 32 + c32, unit)]));
 #pragma unroll
             for (int i = 0; i < NF; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-            // step kt+2's loads go out once the first products are issued
-            if (ks == 0 && kt + 2 < nk) issue(kt + 2, S2);
+            // step kt+RN-1's loads go out once the first products are issued
+            if (ks == 0 && kt + RNG - 1 < nk) issue(kt + RNG - 1, SN);
         }
     };
-    static_assert(RING == 3, "the k loop is unrolled over three stages");
     int kt = 0;
-    for (; kt + RING <= nk; kt += RING) {
-        kstep(std::integral_constant<int, 0>(), kt);
-        kstep(std::integral_constant<int, 1>(), kt + 1);
-        kstep(std::integral_constant<int, 2>(), kt + 2);
+    if constexpr (RNG == 3) {
+        for (; kt + 3 <= nk; kt += 3) {
+            kstep(std::integral_constant<int, 0>(), kt);
+            kstep(std::integral_constant<int, 1>(), kt + 1);
+            kstep(std::integral_constant<int, 2>(), kt + 2);
+        }
+        if (kt < nk) kstep(std::integral_constant<int, 0>(), kt);
+        if (kt + 1 < nk) kstep(std::integral_constant<int, 1>(), kt + 1);
+    } else {
+        for (; kt + 2 <= nk; kt += 2) {
+            kstep(std::integral_constant<int, 0>(), kt);
+            kstep(std::integral_constant<int, 1>(), kt + 1);
+        }
+        if (kt < nk) kstep(std::integral_constant<int, 0>(), kt);
     }
-    if (kt < nk) kstep(std::integral_constant<int, 0>(), kt);
-    if (kt + 1 < nk) kstep(std::integral_constant<int, 1>(), kt + 1);
     // y^T tile: lane holds row m = .. + c32 and features 8 (r / 4) + 4 half + r % 4
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -244,16 +263,16 @@ extern "C" int fk_proj_gemm(const void *x, int32_t Mx, const int32_t *rows, int3
     A.K = K;
     A.N = N;
     const bool wide = N % 256 == 0;
-    using S2 = proj::Shape<2, 2>;
-    using S4 = proj::Shape<4, proj::WIDE_WM>;
+    using S2 = proj::Shape<2, 2, 32>;
+    using S4 = proj::Shape<4, proj::WIDE_WM, 64>;
     A.mt = (M + (wide ? S4::BMW : S2::BMW) - 1) / (wide ? S4::BMW : S2::BMW);
     A.nt = N / (wide ? S4::BNW : S2::BNW);
     const int m_per = (A.mt + proj::XCDS - 1) / proj::XCDS;
     const int64_t blocks = (int64_t)proj::XCDS * m_per * A.nt;
     if (blocks > INT32_MAX) return FK_E_UNSUPPORTED;
     if (wide)
-        proj::k_proj_bf16<4, proj::WIDE_WM><<<dim3((unsigned)blocks), S4::NT, 0, (hipStream_t)stream>>>(A);
+        proj::k_proj_bf16<4, proj::WIDE_WM, 64><<<dim3((unsigned)blocks), S4::NT, 0, (hipStream_t)stream>>>(A);
     else
-        proj::k_proj_bf16<2, 2><<<dim3((unsigned)blocks), S2::NT, 0, (hipStream_t)stream>>>(A);
+        proj::k_proj_bf16<2, 2, 32><<<dim3((unsigned)blocks), S2::NT, 0, (hipStream_t)stream>>>(A);
     return launch_status();
 }
