@@ -892,7 +892,7 @@ def measure(index: int, args, next_rows: bool):
                                "bytes_if_each_child_copied_its_state":
                                    nbytes + (children - n_forks) * sh.Hv * sh.dv * sh.dk * 4}
     else:
-        out["incomplete"] = "gdn_fork_forward unsupported for this dtype in this build: step lacks GDN"
+        out["incomplete"] = "gdn_fork_forward does not support this dtype: the step lacks GDN"
     if next_rows:
         out["next_rows"] = {"conv": measure_conv(wl, args.steps),
                             "window_attention": measure_rule(wl, args.steps, 1, 1024),
@@ -908,7 +908,7 @@ def measure(index: int, args, next_rows: bool):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "bench.py runs on one GPU; runs on several GPUs are not supported",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.calibrate_copy:

@@ -11,7 +11,7 @@ from tests.harness import GpuRound, oracle_attention, oracle_gdn, to_f64
 from tests.malformed import CASES, arrays
 from workloads import make_config, random_tree
 from workloads.tensors import Shapes, draw_inputs
-from workloads.configs import CONFIGS
+from workloads.configs import WORKLOADS
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4

@@ -17,13 +17,13 @@ import gated_deltanet_amd as fk
 import oracle
 from tests.harness import GpuRound, state_slots, stratified_rows, to_f64
 from workloads import build_tree, subtree_path
-from workloads.configs import CONFIGS, config_requests
+from workloads.configs import WORKLOADS, config_requests
 from workloads.tensors import draw_inputs
 
 pytestmark = pytest.mark.gpu
 MAX_ABS, MEAN_ABS = 2e-2, 2e-3
 SAMPLED = (0, 37)
-CFG = CONFIGS[4]
+CFG = WORKLOADS[4]
 SH = CFG.shapes
 G_HEADS = 4   # v heads the GDN oracle runs (the first ones)
 

@@ -8,4 +8,4 @@ consume the same inputs without sharing any code of the method.
 """
 from .trees import Seg, Tree, build_tree, subtree_path, random_tree  # noqa: F401
 from .tensors import draw_inputs, draw_conv, to_bf16, Inputs, ConvInputs  # noqa: F401
-from .configs import CONFIGS, make_config  # noqa: F401
+from .configs import WORKLOADS, make_config  # noqa: F401

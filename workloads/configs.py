@@ -40,7 +40,7 @@ class Config:
     page_size: int = 16
 
 
-CONFIGS = {
+WORKLOADS = {
     0: Config(0, "tiny decision request", 1000, "f32", Shapes(4, 1, 64, 2, 2, 32, 32), 3.0),
     1: Config(1, "decision-request mixture", 1001, "bf16", Shapes(16, 2, 128, 16, 16, 128, 128), 3.0),
     2: Config(2, "agent fan-out depth 3", 1002, "bf16", Shapes(32, 4, 128, 16, 32, 128, 128), 3.0),
@@ -55,7 +55,7 @@ def _structure_rng(seed: int) -> np.random.Generator:
 
 def config_requests(i: int, n_requests: Optional[int] = None):
     """Per-request node lists ``(parent_local, fork, length[, cached])``."""
-    cfg = CONFIGS[i]
+    cfg = WORKLOADS[i]
     rng = _structure_rng(cfg.seed)
     reqs = []
     if i == 0:
@@ -106,4 +106,4 @@ def config_requests(i: int, n_requests: Optional[int] = None):
 def make_config(i: int, n_requests: Optional[int] = None) -> tuple[Config, Tree]:
     """The config's round as a flattened tree (Eq. 2 level order)."""
     tree = build_tree(config_requests(i, n_requests)).flatten()
-    return CONFIGS[i], tree
+    return WORKLOADS[i], tree
