@@ -20,9 +20,11 @@
 // flight.  When N is a multiple of 256 a work-group of eight waves computes a
 // 256-feature x 256-row block (a wave 128 x 64: four w and two x fragments
 // per 16-wide k-slice for eight products), k in steps of 64 through two
-// 64 KB stages (one step ahead; one work-group a CU); otherwise four waves
-// compute 128 x 128 (a wave 64 x 64), k in steps of 32 through three 16 KB
-// stages (two steps ahead; three work-groups a CU).  LDS rows hold one
+// 64 KB stages (one step ahead; one work-group a CU), its two groups of four
+// waves taking turns: one multiplies while the other reads its next operands
+// (k_proj_pp); otherwise four waves compute 128 x 128 (a wave 64 x 64), k in
+// steps of 32 through three 16 KB stages (two steps ahead; three work-groups
+// a CU).  LDS rows hold one
 // step's k (64 or 128 bytes), their 16-byte units XOR-swizzled by bits 2-3
 // (or 1-3) of the row, so the operand reads (16 lanes: 16 rows, one unit)
 // are free of bank conflicts; the lane that fills unit u of row r loads the
@@ -48,9 +50,10 @@ constexpr int K_MULT = 64;      // K must be a multiple of this (the documented 
 constexpr int WIDE_WM = 4;      // waves along the rows of the 256-feature blocks
 constexpr int GM = 8;           // row blocks per group within an XCD
 constexpr int XCDS = 8;
-// NF: 32-feature fragments per wave (2: 128 x 128 blocks, three work-groups a
-// CU; 4: 256 features x 128 rows, two work-groups a CU and half the LDS
-// operand bytes per product, used when N is a multiple of 256)
+// NF: 32-feature fragments per wave (2: 128 x 128 blocks on four waves, three
+// work-groups a CU; 4 with WM = 4: 256 x 256 blocks on eight waves, one
+// work-group a CU and half the LDS operand bytes per product, used when N is
+// a multiple of 256)
 template <int NF, int WM, int BK_ = 32>   // WM: waves along the rows (64 rows each)
 struct Shape {
     static constexpr int BK = BK_;                 // k per step
@@ -239,6 +242,193 @@ __global__ void __launch_bounds__((Shape<NF, WM, BK_>::NT), (Shape<NF, WM, BK_>:
     }
 }
 
+// Wide blocks in two wave groups that take turns (group 0: waves 0-3, group
+// 1: waves 4-7, one wave of each on every SIMD).  A phase covers half a
+// k-step (two 16-wide k-slices): group 0 reads half j's operands from LDS
+// into registers in phase 2j and runs its 16 products in phase 2j+1; group 1
+// does the same one phase later; a barrier ends every phase.  Each element
+// still sums its 16-wide k-slices in ascending order in one wave.  Stage
+// (s mod 2) holds step s (halves 2s and 2s+1), read last in phase 4s+3.  In
+// phase 4t both groups issue step t+1's loads into the stage step t-1 left
+// (group 0 while reading half 2t, group 1 while multiplying half 2t-1), and
+// each wave waits for its loads before the barrier that ends phase 4t+3
+// (group 0 after multiplying half 2t+1, group 1 after reading it), so step
+// t+1 is in LDS when group 0 reads it in phase 4t+4.  Every wave meets the
+// same number of barriers: group 1's extra one at the start is matched by
+// group 0's after its stores.
+__global__ void __launch_bounds__((Shape<4, WIDE_WM, 64>::NT), 1) k_proj_pp(Args A)
+{
+    using SH = Shape<4, WIDE_WM, 64>;
+    static_assert(SH::NT == 512, "two groups of four waves");
+    constexpr int BK = SH::BK, RPL = SH::RPL, UNITS = SH::UNITS;
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * SH::STAGE];
+    int mb, nb;
+    if (!tile_of(A, blockIdx.x, mb, nb)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wn = w & 1, wm = w >> 1, half = lane >> 5, c32 = lane & 31;
+    const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
+    const int m0 = mb * SH::BMW, n0 = nb * SH::BNW;
+    constexpr int WF = SH::BNW / RPL / 8;   // w loads a wave (RPL rows each)
+    constexpr int XL = 32 / RPL;            // x loads a wave (32 rows)
+    const uint16_t *wsrc[WF], *xsrc[XL];
+#pragma unroll
+    for (int i = 0; i < WF; ++i) {
+        const int r = RPL * WF * w + RPL * i + lane / UNITS, u = SH::swz_unit(r, lane % UNITS);
+        wsrc[i] = A.w + (size_t)(n0 + r) * A.K + u * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+        const int r = 32 * w + RPL * i + lane / UNITS, u = SH::swz_unit(r, lane % UNITS);
+        const int m = m0 + r;
+        int src = -1;
+        if (m < A.M) src = A.rows ? A.rows[m] : m;
+        if (src < 0 || src >= A.Mx) src = 0;
+        xsrc[i] = A.x + (size_t)src * A.K + u * 8;
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)ring;
+    const uint32_t wq = __builtin_amdgcn_readfirstlane(lds0 + w * RPL * WF * BK * 2);
+    const uint32_t xq = __builtin_amdgcn_readfirstlane(lds0 + SH::WT * 2 + w * 32 * BK * 2);
+    auto issue = [&](int kt, int s) {
+        const int k0 = kt * BK;
+        const uint32_t so = s * (SH::STAGE * 2);
+#pragma unroll
+        for (int i = 0; i < WF; ++i) lds_dma16(wsrc[i] + k0, wq + so + i * 1024);
+#pragma unroll
+        for (int i = 0; i < XL; ++i) lds_dma16(xsrc[i] + k0, xq + so + i * 1024);
+    };
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    const int nk = A.K / BK;   // >= 1
+    issue(0, 0);
+    if (nk > 1) {
+        issue(1, 1);
+        wait_barrier<WF + XL>();
+    } else {
+        wait_barrier<0>();
+    }
+    if (grp) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // a phase covers half a step (two 16-wide k-slices): 48 operand registers
+    bf16x8 a[2][4], b[2][2];
+    auto read_ops = [&](auto SC, auto HC) {
+        constexpr int S = decltype(SC)::value, H = decltype(HC)::value;
+        const uint16_t *lw = ring + S * SH::STAGE, *lx = lw + SH::WT;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int unit = (2 * H + kk) * 2 + half;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[kk][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
+                                                          &lw[SH::swz(wn * 128 + i * 32 + c32, unit)]));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[kk][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
+                                                          &lx[SH::swz(wm * 64 + j * 32 + c32, unit)]));
+        }
+    };
+    // the products of one phase; `mid` runs after the first k-slice's
+    auto products = [&](auto mid) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][i], b[kk][j], acc[i][j], 0, 0, 0);
+            if (kk == 0) mid();
+        }
+    };
+    auto nothing = []() {};
+#define FK_PP_BAR(text)                           \
+    do {                                          \
+        __builtin_amdgcn_sched_barrier(0);        \
+        asm volatile(text ::: "memory");          \
+        __builtin_amdgcn_sched_barrier(0);        \
+    } while (0)
+    // group 0, half H of step s (stage S): read it (the first half also
+    // issues step s+1's loads), then multiply; step s+1 is waited for at the
+    // end of the second half
+    auto half0 = [&](auto SC, auto HC, int s) {
+        constexpr int S = decltype(SC)::value, H = decltype(HC)::value;
+        read_ops(SC, HC);
+        if (H == 0 && s >= 1 && s + 1 < nk) issue(s + 1, 1 - S);
+        FK_PP_BAR("s_waitcnt lgkmcnt(0)\n\ts_barrier");
+        products(nothing);
+        if (H == 1)
+            FK_PP_BAR("s_waitcnt vmcnt(0)\n\ts_barrier");
+        else
+            FK_PP_BAR("s_barrier");
+    };
+    // group 1, half H of step s (stage S): read it (step s+1's loads, issued
+    // in the previous phase, are waited for at the end of the second half),
+    // then multiply; the second half issues step s+2's loads into stage S
+    auto half1 = [&](auto SC, auto HC, int s) {
+        constexpr int S = decltype(SC)::value, H = decltype(HC)::value;
+        read_ops(SC, HC);
+        if (H == 1)
+            FK_PP_BAR("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier");
+        else
+            FK_PP_BAR("s_waitcnt lgkmcnt(0)\n\ts_barrier");
+        products([&]() {
+            if (H == 1 && s + 2 < nk) issue(s + 2, S);
+        });
+        FK_PP_BAR("s_barrier");
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    int kt = 0;
+    if (grp == 0) {
+        for (; kt + 2 <= nk; kt += 2) {
+            half0(I0(), I0(), kt);
+            half0(I0(), I1(), kt);
+            half0(I1(), I0(), kt + 1);
+            half0(I1(), I1(), kt + 1);
+        }
+        if (kt < nk) {
+            half0(I0(), I0(), kt);
+            half0(I0(), I1(), kt);
+        }
+    } else {
+        for (; kt + 2 <= nk; kt += 2) {
+            half1(I0(), I0(), kt);
+            half1(I0(), I1(), kt);
+            half1(I1(), I0(), kt + 1);
+            half1(I1(), I1(), kt + 1);
+        }
+        if (kt < nk) {
+            half1(I0(), I0(), kt);
+            half1(I0(), I1(), kt);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = m0 + wm * 64 + j * 32 + c32;
+        if (m >= A.M) continue;
+        if (A.rows) {
+            const int src = A.rows[m];
+            if (src < 0 || src >= A.Mx) continue;
+        }
+        uint16_t *yrow = A.y + (size_t)m * A.N + n0 + wn * 128;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint2 p;
+                p.x = (uint32_t)f32_to_bf16(acc[i][j][4 * g]) | ((uint32_t)f32_to_bf16(acc[i][j][4 * g + 1]) << 16);
+                p.y = (uint32_t)f32_to_bf16(acc[i][j][4 * g + 2]) | ((uint32_t)f32_to_bf16(acc[i][j][4 * g + 3]) << 16);
+                *reinterpret_cast<uint2 *>(yrow + i * 32 + 8 * g + 4 * half) = p;
+            }
+    }
+    if (grp == 0) FK_PP_BAR("s_barrier");
+#undef FK_PP_BAR
+}
+
 }  // namespace proj
 }  // namespace fk
 
@@ -271,7 +461,7 @@ extern "C" int fk_proj_gemm(const void *x, int32_t Mx, const int32_t *rows, int3
     const int64_t blocks = (int64_t)proj::XCDS * m_per * A.nt;
     if (blocks > INT32_MAX) return FK_E_UNSUPPORTED;
     if (wide)
-        proj::k_proj_bf16<4, proj::WIDE_WM, 64><<<dim3((unsigned)blocks), S4::NT, 0, (hipStream_t)stream>>>(A);
+        proj::k_proj_pp<<<dim3((unsigned)blocks), S4::NT, 0, (hipStream_t)stream>>>(A);
     else
         proj::k_proj_bf16<2, 2, 32><<<dim3((unsigned)blocks), S2::NT, 0, (hipStream_t)stream>>>(A);
     return launch_status();

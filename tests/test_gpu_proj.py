@@ -35,7 +35,8 @@ def _err(o, ref):
     return d.max(), d.mean()
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 64, 128), (300, 256, 384), (129, 1024, 256), (1000, 4096, 128)])
+@pytest.mark.parametrize("M,K,N", [(1, 64, 128), (300, 256, 384), (129, 1024, 256), (1000, 4096, 128),
+                                   (1, 64, 256), (257, 192, 512), (600, 320, 768)])
 def test_proj_matches_oracle(M, K, N):
     x, w, xt, wt = _draw(M + K + N, M, K, N)
     print(f"[proj] M={M} K={K} N={N}", flush=True)
