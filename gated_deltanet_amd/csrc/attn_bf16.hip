@@ -10,7 +10,7 @@
 // segment causally), in 32-key blocks anchored at every range start; a row's
 // reduction order therefore depends only on its own chain (Flide 3.5).
 // Blocks are staged in a ring of three 16 KB LDS stages by direct global->LDS
-// loads two blocks ahead (48 KB), and the kernels take at most 147 VGPRs, so
+// loads two blocks ahead (48 KB), and the kernels take at most 154 VGPRs, so
 // three work-groups (12 waves) share a compute unit.
 //
 // Per block and wave, with v_mfma_f32_32x32x16_bf16 (fp32 accumulate):
@@ -173,9 +173,9 @@ __device__ __forceinline__ void store_rows(const f32x16 (&o)[D / 32], float l, b
 // first visible key offset of the lane's row within the block, minus
 // 8 * half), online softmax with the per-row lazy rescale, O^T += V^T . P^T.
 // Where a lane's operands sit in a staged block (bf16 elements): K fragment
-// (key tile mt, k-step ks) at krow + mt * KMT + ks * KS, value fragment
-// (dim tile i, key step kk) at vrow + i * VI + kk * VKK (the ring layout
-// below).
+// (key tile mt, k-step ks) at krow + mt * KMT + (ks ^ kd) * KS, value
+// fragment (dim tile i, key step kk) at vrow + i * VI + kk * VKK (the ring
+// layout below; kd is the lane's swizzle of the k-step).
 
 // `mid` runs once the score products are issued (the full launch issues a
 // later block's loads there, while the matrix cores work on this one).
@@ -186,7 +186,7 @@ struct NoMid {
 template <int RULE, class LAY, class MID = NoMid>
 __device__ __forceinline__ void block_compute(const uint16_t *krow, const uint16_t *vrow, const bf16x8 (&qf)[D / 16],
                                               f32x16 (&o)[D / 32], float &m, float &l, bool full, int hi, int lo,
-                                              float scale_log2e, const MID &mid = MID())
+                                              int kd, float scale_log2e, const MID &mid = MID())
 {
     // S^T = K . Q^T
     f32x16 sacc[MT];
@@ -197,7 +197,7 @@ __device__ __forceinline__ void block_compute(const uint16_t *krow, const uint16
         for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + mt * LAY::KMT + ks * LAY::KS));
+                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + mt * LAY::KMT + (ks ^ kd) * LAY::KS));
                 sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
             }
         // keep LOOKAHEAD operand reads in flight ahead of the MFMAs
@@ -288,14 +288,18 @@ __device__ __forceinline__ void block_compute(const uint16_t *krow, const uint16
 // direct global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land
 // at M0 + 16 * lane), two blocks ahead of the one computed, so no register
 // holds a block in flight.  Stage layout (bf16 elements): K of the block's two
-// pages at [page][k-step 8][half 2][slot 16][8], V^T at 4096 + [page][dim tile
-// 4][half 2][dim 32][8].  A 16-lane read group then meets 16 distinct 16-byte
-// bank groups (keys: 16 slots; values: 16 dims), and each read of a lane is
-// its base plus an immediate offset.  The lane that fills 16-byte unit c of a
-// page region loads the unit of the page that belongs there (ring_k_off,
-// ring_v_off).
+// pages row by row, [page][slot 16][unit 16][8], the 16-byte unit u of a key
+// row at position u ^ slot; V^T at 4096 + [page][dim tile 4][half 2][dim 32]
+// [8].  A 16-lane read group then meets 16 distinct 16-byte bank groups
+// (keys: 16 slots, so 16 distinct positions of one unit; values: 16 dims).
+// A value read is its lane's base plus an immediate offset; a key read adds
+// (ks ^ kd) * 32 bytes, kd = slot / 2, since unit 2 ks + half of slot s sits at
+// 2 (ks ^ (s / 2)) + (half ^ (s % 2)).  Each wave loads four whole key rows and
+// 32 whole value rows of a page (1 KB, eight 128-byte lines an instruction);
+// the lane that fills 16-byte unit c of a page region loads the unit of the
+// page that belongs there (ring_k_off, ring_v_off).
 struct RingTiles {
-    static constexpr int KS = 256, KMT = 0, VI = 512, VKK = 2048;
+    static constexpr int KS = 16, KMT = 0, VI = 512, VKK = 2048;
 };
 constexpr int RING = 3;                 // stages
 constexpr int STAGE = 2 * BN * D;       // bf16 elements per stage: K and V^T of one block
@@ -303,7 +307,11 @@ static_assert(MT == 1 && BN == 2 * FK_TILE_TOKENS, "the ring layout holds two 16
 
 // byte offsets inside a 4 KB K / V page of the 16 bytes lane `lane` of wave
 // `w` loads (see the stage layout above)
-__device__ __forceinline__ uint32_t ring_k_off(int w, int lane) { return (lane & 15) * 256 + (4 * w + (lane >> 4)) * 16; }
+__device__ __forceinline__ uint32_t ring_k_off(int w, int lane)
+{
+    const int row = 4 * w + (lane >> 4);
+    return row * 256 + (((lane & 15) ^ (row & 15)) * 16);
+}
 __device__ __forceinline__ uint32_t ring_v_off(int w, int lane) { return (32 * w + (lane & 31)) * 32 + (lane >> 5) * 16; }
 
 __device__ __forceinline__ const uint16_t *uniform_ptr(const uint16_t *p)
@@ -415,7 +423,8 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     const uint16_t *kg = uniform_ptr(kp + (size_t)g * (FK_TILE_TOKENS * D));
     const uint16_t *vg = uniform_ptr(vp + (size_t)g * (FK_TILE_TOKENS * D));
     const uint32_t pstride = (uint32_t)Hkv * (FK_TILE_TOKENS * D);
-    const uint16_t *krow0 = ring + (n >> 4) * 2048 + half * 128 + (prow & 15) * 8;
+    const uint16_t *krow0 = ring + (n >> 4) * 2048 + (prow & 15) * 128 + (half ^ (prow & 1)) * 8;
+    const int kd = (prow & 15) >> 1;
     const uint16_t *vrow0 = ring + 4096 + half * 256 + n * 8;
 
     TileCtx tc;
@@ -477,7 +486,7 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
             // segment's last tile) only helps stage the blocks
             if (wave_live)
                 block_compute<RULE, RingTiles>(krow0 + ST * STAGE, vrow0 + ST * STAGE, qf, o, m, l, full, hi, lo,
-                                               scale_log2e, issue_next);
+                                               kd, scale_log2e, issue_next);
             else
                 issue_next();
         }
@@ -666,7 +675,8 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
     const uint16_t *kg = uniform_ptr(kp + (size_t)g * (FK_TILE_TOKENS * D));
     const uint16_t *vg = uniform_ptr(vp + (size_t)g * (FK_TILE_TOKENS * D));
     const uint32_t pstride = (uint32_t)Hkv * (FK_TILE_TOKENS * D);
-    const uint16_t *krow0 = ring + (n >> 4) * 2048 + half * 128 + (prow & 15) * 8;
+    const uint16_t *krow0 = ring + (n >> 4) * 2048 + (prow & 15) * 128 + (half ^ (prow & 1)) * 8;
+    const int kd = (prow & 15) >> 1;
     const uint16_t *vrow0 = ring + 4096 + half * 256 + n * 8;
 
     RCursor cur;
@@ -702,7 +712,7 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
             const int lo = (RULE == WINDOW ? lo_r - key0 : 0) - half * 8;
             // block j+2's loads go out once this block's score products are
             block_compute<RULE, RingTiles>(krow0 + ST * STAGE, vrow0 + ST * STAGE, qf, o, m, l, full, hi, lo,
-                                           scale_log2e, [&]() {
+                                           kd, scale_log2e, [&]() {
                                                if (more2) ring_issue(st2_bytes, kg, vg, pg2, pstride, koff, voff);
                                            });
         } else if (more2) {
