@@ -10,7 +10,7 @@
 // segment causally), in 32-key blocks anchored at every range start; a row's
 // reduction order therefore depends only on its own chain (Flide 3.5).
 // Blocks are staged in a ring of three 16 KB LDS stages by direct global->LDS
-// loads two blocks ahead (48 KB), and the kernels take at most 154 VGPRs, so
+// loads two blocks ahead (48 KB), and the kernels take at most 158 VGPRs, so
 // three work-groups (12 waves) share a compute unit.
 //
 // Per block and wave, with v_mfma_f32_32x32x16_bf16 (fp32 accumulate):
@@ -145,15 +145,22 @@ __device__ __forceinline__ bool cursor_next(BlockCursor &c, const TileCtx &t)
     return true;
 }
 
-// Epilogue: the row's sum is split over the two halves of the wave; a valid
-// row stores O / l as bf16 (registers 4*rq .. 4*rq+3 of tile i hold dims
-// 32*i + 8*rq + 4*half + [0, 4)).
-__device__ __forceinline__ void store_rows(const f32x16 (&o)[D / 32], float l, bool row_valid, uint16_t *orow,
-                                           int half)
+// Epilogue through LDS: the row's sum is split over the two halves of the
+// wave; every row's O / l is written as bf16 into this wave's 8 KB quarter of
+// the ring (idle once every wave has passed the barrier below), row-major with
+// the 16-byte units XORed by the row (registers 4*rq .. 4*rq+3 of tile i hold
+// dims 32*i + 8*rq + 4*half + [0, 4)), then read back and stored by whole
+// rows: instruction j stores rows 4j .. 4j+3 of the wave (heads 4(j%2) .. +3
+// of its token j/2: 1 KB, eight full lines), for a token whose rows are valid.
+// Row r of the wave (token r/8, head r%8) goes to orow0 + (r/8) tstride +
+// (r%8) D.
+__device__ __forceinline__ void store_rows(const f32x16 (&o)[D / 32], float l, bool row_valid, uint16_t *stage,
+                                           uint16_t *orow0, size_t tstride, int n, int half, int lane)
 {
-    const float lsum = pair_sum(l);
-    if (!row_valid) return;
-    const float inv = 1.f / lsum;
+    const float inv = 1.f / pair_sum(l);
+    // tokens 0-3 of the wave: lanes 0, 8, 16, 24 (a token's rows are all valid or not)
+    const uint64_t tok_valid = __ballot(row_valid);
+    __syncthreads();   // every wave is done with the ring
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
@@ -164,8 +171,15 @@ __device__ __forceinline__ void store_rows(const f32x16 (&o)[D / 32], float l, b
             for (int e = 0; e < 4; ++e) b4[e] = (__bf16)(o[i][rq * 4 + e] * inv);
             packed.x = (uint32_t)__builtin_bit_cast(uint16_t, b4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, b4[1]) << 16);
             packed.y = (uint32_t)__builtin_bit_cast(uint16_t, b4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, b4[3]) << 16);
-            *reinterpret_cast<uint2 *>(orow + i * 32 + rq * 8 + half * 4) = packed;
+            *reinterpret_cast<uint2 *>(stage + n * D + (((4 * i + rq) ^ (n & 15)) * 8) + half * 4) = packed;
         }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = 4 * j + (lane >> 4), up = lane & 15;
+        const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * D + up * 8);
+        if ((tok_valid >> ((j >> 1) * 8)) & 1)
+            *reinterpret_cast<uint4 *>(orow0 + (size_t)(j >> 1) * tstride + (r & 7) * D + ((up ^ (r & 15)) * 8)) = v;
+    }
 }
 
 // One key block for one wave's 32 rows: S^T = K . Q^T on MFMA, masking (only
@@ -505,7 +519,8 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
     while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>()) &&
            step(std::integral_constant<int, 2>())) {
     }
-    store_rows(o, l, row_valid, out + qrow * D, half);
+    store_rows(o, l, row_valid, ring + w * (32 * D), out + ((size_t)seg_start[s] + row0 + 4 * w) * Hq * D + (size_t)g * G * D,
+               (size_t)Hq * D, n, half, lane);
 }
 
 // Selective readout (Flide section 3.3.3): work item = (group of up to 16
@@ -732,7 +747,8 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
     while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>()) &&
            step(std::integral_constant<int, 2>())) {
     }
-    store_rows(o, l, row_valid, out_rows + qrow * D, half);
+    store_rows(o, l, row_valid, ring + w * (32 * D), out_rows + ((size_t)grp * group + 4 * w) * Hq * D + (size_t)g * G * D,
+               (size_t)Hq * D, n, half, lane);
 }
 
 }  // namespace attn
