@@ -550,7 +550,10 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
 {
     __shared__ __attribute__((aligned(1024))) uint16_t ring[RING * STAGE];
     __shared__ int c_seg[RO_CAND], c_lim[RO_CAND], c_lo[RO_CAND];   // per (slot, depth)
-    __shared__ int c_rep[RO_CAND], c_cnt[RO_CAND], c_key0[RO_CAND];
+    // planning only: these three live in the ring, which no block occupies
+    // before the walk (the barrier after the range table is built precedes
+    // the first block load), so three work-groups still fit a CU's LDS
+    int *const c_rep = reinterpret_cast<int *>(ring), *const c_cnt = c_rep + RO_CAND, *const c_key0 = c_cnt + RO_CAND;
     __shared__ int r_seg[RO_CAND], r_depth[RO_CAND], r_count[RO_CAND], r_key0[RO_CAND];
     __shared__ int n_ranges;
     if (header[H_STATUS] != FK_OK) return;
