@@ -524,7 +524,8 @@ k_attn_bf16(const uint16_t *__restrict__ q, int Hq, int Hkv, float scale_log2e, 
 }
 
 // Selective readout (Flide section 3.3.3): work item = (group of up to 16
-// entries of the row buffer, kv head).  The group's entries take the 16 token
+// entries of the row buffer, part, kv head), a part being the group's leading
+// entries of one request or the rest (below).  The group's entries take the 16 token
 // slots of a tile (wave w: slots 4w .. 4w+3, 8 q heads each), and the key walk
 // covers the union of their chains: depth by depth, every distinct segment
 // met at that depth, up to the largest count any entry sees of it.  A row
@@ -554,16 +555,42 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
     // before the walk (the barrier after the range table is built precedes
     // the first block load), so three work-groups still fit a CU's LDS
     int *const c_rep = reinterpret_cast<int *>(ring), *const c_cnt = c_rep + RO_CAND, *const c_key0 = c_cnt + RO_CAND;
+    int *const c_root = c_key0 + RO_CAND;   // per slot
     __shared__ int r_seg[RO_CAND], r_depth[RO_CAND], r_count[RO_CAND], r_key0[RO_CAND];
     __shared__ int n_ranges;
     if (header[H_STATUS] != FK_OK) return;
-    const int grp = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+    const int grp = blockIdx.x / Hkv / 2, part = blockIdx.x / Hkv % 2, g = blockIdx.x % Hkv;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int half = lane >> 5, n = lane & 31;
 
+    // The group's entries split in two parts, each walked by its own work-group:
+    // part 0 is the slots before the first used entry whose root segment differs
+    // from that of the group's first used entry, part 1 the rest (usually none,
+    // and that work-group ends here).  So a group that straddles two requests
+    // does not walk both histories in one work-group.
+    if (threadIdx.x < FK_TILE_TOKENS) {
+        const int ce = grp * group + (int)threadIdx.x;
+        const int ct = ((int)threadIdx.x < group && ce < n_rows) ? sel_rows[ce] : -1;
+        const int cs = (ct >= 0 && ct < T) ? tok_seg[ct] : -1;
+        c_root[threadIdx.x] = cs >= 0 ? seg_anc[(size_t)cs * FK_MAX_DEPTH] : -1;
+    }
+    __syncthreads();
+    int split = group, root0 = -1;
+    for (int i = 0; i < group; ++i) {
+        const int r = c_root[i];
+        if (r < 0) continue;
+        if (root0 < 0) root0 = r;
+        else if (r != root0) {
+            split = i;
+            break;
+        }
+    }
+    if (part == 1 && split == group) return;   // the whole work-group
+    auto in_part = [&](int sl) { return part == 0 ? sl < split : sl >= split; };
+
     // this lane's row: entry of slot w*4 + n/8, q head g*G + n%8
     const int slot = w * 4 + n / 8, e = grp * group + slot;
-    const int t = (slot < group && e < n_rows) ? sel_rows[e] : -1;
+    const int t = (slot < group && e < n_rows && in_part(slot)) ? sel_rows[e] : -1;
     const bool row_valid = t >= 0 && t < T && tok_seg[t] >= 0;   // not unused, not padding
     const int h = g * G + (n % 8);
     const size_t qrow = (size_t)e * Hq + h;
@@ -575,7 +602,7 @@ k_attn_readout_bf16(const uint16_t *__restrict__ q_rows, const int32_t *__restri
         const int ci = threadIdx.x, cslot = ci / FK_MAX_DEPTH, cd = ci % FK_MAX_DEPTH;
         const int ce = grp * group + cslot;
         int cseg = -1, clim = 0, clo = 0;
-        const int ct = (cslot < group && ce < n_rows) ? sel_rows[ce] : -1;
+        const int ct = (cslot < group && ce < n_rows && in_part(cslot)) ? sel_rows[ce] : -1;
         const int cs = (ct >= 0 && ct < T) ? tok_seg[ct] : -1;
         if (cs >= 0) {
             const int cdep = seg_depth[cs];
@@ -767,7 +794,7 @@ static void launch_rule(const fk_tree_meta *meta, const WsLayout &L, const void 
     const float sl = scale * 1.4426950408889634f;
     if (rows) {
         const int64_t groups = (n_rows + group - 1) / group;
-        attn::k_attn_readout_bf16<RULE><<<dim3((unsigned)(groups * Hkv)), attn::THREADS, 0, st>>>(
+        attn::k_attn_readout_bf16<RULE><<<dim3((unsigned)(groups * 2 * Hkv)), attn::THREADS, 0, st>>>(
             (const uint16_t *)q, rows, n_rows, group, Hq, Hkv, sl, window, meta->tok_seg, meta->T,
             ws_at<int32_t>(ws, L.seg_pos0), (const uint16_t *)k_pool, (const uint16_t *)v_pool, (uint16_t *)out,
             ws_at<int32_t>(ws, L.header), ws_at<int32_t>(ws, L.seg_start), ws_at<int32_t>(ws, L.seg_len),
@@ -786,6 +813,8 @@ static void launch_rule(const fk_tree_meta *meta, const WsLayout &L, const void 
 // rows == NULL: the full launch over the round's tiles; otherwise readout of
 // the n_rows entries of `rows` (q and out then hold one row per entry),
 // grouped so that the launch fills about three work-groups per compute unit
+// (two work-groups per group: one for each part of a group split at a request
+// boundary; the second usually ends at once)
 int fk_launch_attn_bf16(const fk_tree_meta *meta, const void *q, int Hq, int Hkv, float scale, int rule, int window,
                         const int32_t *rows, int n_rows, const void *k_pool, const void *v_pool, void *out,
                         const void *ws, hipStream_t st)
