@@ -113,3 +113,26 @@ def test_readout_grouped_mixed_entries(rule, W):
     used = rows >= 0
     assert np.isnan(o[~used]).all()
     assert np.array_equal(o[used], full[rows[used]])
+
+
+def test_readout_grouped_in_stream_order():
+    """Entries in stream order, repeated, so that groups of 16 hold runs of one
+    request and some straddle a request boundary (such a group's two parts are
+    walked by two work-groups, one request's chains each): every entry equals
+    its row of the full launch bit for bit, unused entries stay untouched."""
+    rng = np.random.default_rng(6401)
+    t = random_tree(rng, n_requests=6, p_cached_root=0.4, p_internal_fork=0.4, max_len=100, max_depth=4).flatten()
+    inp = draw_inputs(t, SH["bf16"], 78, "bf16")
+    r = GpuRound(inp).build()
+    full = to_f64(r.attention())
+    rows = np.concatenate([np.arange(t.T) for _ in range(8)]).astype(np.int32)
+    rows[rng.integers(0, len(rows), 20)] = -1
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    group = min(16, len(rows) * SH["bf16"].Hkv // (3 * n_cu))
+    print(f"[readout stream order] T={t.T} entries={len(rows)} group={group}", flush=True)
+    assert group >= 8
+    o = _readout(r, rows, FK_RULE_CAUSAL, 0)
+    assert r.status() == 0
+    used = rows >= 0
+    assert np.isnan(o[~used]).all()
+    assert np.array_equal(o[used], full[rows[used]])
